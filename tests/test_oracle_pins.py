@@ -1,0 +1,381 @@
+"""Pins of the CPU oracle against things other than itself: closed forms,
+invariants, brute-force enumeration, library routines, and numbers the pages print.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import workloads as W
+from oracle import e4m3
+from oracle import moe as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_numbers.txt")
+
+
+def _golden():
+    out = {}
+    for line in open(GOLDEN):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, val, unit, src = [p.strip() for p in line.split("|")]
+        out[key] = (val, unit, src)
+    return out
+
+
+def _printed(val: str) -> float:
+    mult = {"M": 1e6, "B": 1e9}
+    return float(val[:-1]) * mult[val[-1]] if val[-1] in mult else float(val)
+
+
+# ----------------------------------------------------------------------------- top-k
+
+def test_topk_weights_sum_to_one():
+    rng = np.random.default_rng(1)
+    z = rng.normal(size=(50, 16))
+    for K in (1, 2, 5, 16):
+        _, w = O.topk_softmax(z, K, norm_topk=True)
+        assert np.allclose(w.sum(axis=1), 1.0, atol=1e-12)
+
+
+def test_topk_bruteforce_tiny():
+    rng = np.random.default_rng(2)
+    for trial in range(40):
+        E = int(rng.integers(2, 9))
+        K = int(rng.integers(1, min(E, 3) + 1))
+        T = int(rng.integers(1, 6))
+        # distinct integer-spaced logits
+        z = np.stack([rng.permutation(E).astype(np.float64) * 0.75 - 2.0 for _ in range(T)])
+        ids, w = O.topk_softmax(z, K, norm_topk=True)
+        ids0, w0 = O.topk_softmax(z, K, norm_topk=False)
+        assert np.array_equal(ids, ids0)
+        for t in range(T):
+            best = max(itertools.combinations(range(E), K), key=lambda c: sum(z[t, list(c)]))
+            assert set(ids[t].tolist()) == set(best)
+            assert all(z[t, ids[t, i]] > z[t, ids[t, i + 1]] for i in range(K - 1))
+            assert np.allclose(w[t], scipy.special.softmax(z[t, ids[t]]), rtol=0, atol=1e-14)
+            assert np.allclose(w0[t], scipy.special.softmax(z[t])[ids[t]], rtol=0, atol=1e-14)
+
+
+def test_topk_ties_go_to_lower_id():
+    z = np.array([[1.0, 3.0, 3.0, 0.0, 3.0]])
+    ids, w = O.topk_softmax(z, 2)
+    assert ids.tolist() == [[1, 2]]
+    assert np.allclose(w, 0.5)
+
+
+def test_topk_per_token_shift_invariance():
+    rng = np.random.default_rng(3)
+    z = rng.integers(-20, 20, size=(30, 12)).astype(np.float64) / 4.0
+    shift = rng.integers(-8, 8, size=(30, 1)).astype(np.float64)  # exact in binary
+    a = O.topk_softmax(z, 3)
+    b = O.topk_softmax(z + shift, 3)
+    assert np.array_equal(a[0], b[0])
+    assert np.allclose(a[1], b[1], atol=1e-15)
+
+
+# ----------------------------------------------------------------------------- budget
+
+def _random_routing(rng, T, E, K):
+    z = rng.normal(size=(T, E))
+    return z, *O.topk_softmax(z, K)
+
+
+def test_budget_noop_when_off_or_at_or_above_union():
+    rng = np.random.default_rng(4)
+    _, ids, w = _random_routing(rng, 40, 16, 3)
+    nu = len(set(ids.ravel().tolist()))
+    for B in (0, nu, nu + 1, 10 * nu):
+        i2, w2, st = O.expert_budget(ids, w, B)
+        assert np.array_equal(i2, ids) and np.array_equal(w2, w)
+        assert st.tolist() == [nu, nu, 0, 0]
+
+
+def test_budget_bruteforce_tiny():
+    rng = np.random.default_rng(5)
+    for trial in range(25):
+        T, E, K = int(rng.integers(2, 6)), int(rng.integers(4, 9)), 2
+        z, ids, w = _random_routing(rng, T, E, K)
+        U = sorted(set(ids.ravel().tolist()))
+        if len(U) < 2:
+            continue
+        B = int(rng.integers(1, len(U)))
+        i2, w2, st = O.expert_budget(ids, w, B)
+        agg = {e: w[ids == e].sum() for e in U}
+        best = max(itertools.combinations(U, B), key=lambda c: sum(agg[e] for e in c))
+        kept = set(i2.ravel().tolist()) - {-1}
+        assert kept == set(best)
+        assert st[0] == len(U) and st[1] == B
+        for t in range(T):
+            kt = [e for e in ids[t].tolist() if e in kept]
+            assert i2[t, :len(kt)].tolist() == kt            # original order, compacted
+            assert (i2[t, len(kt):] == -1).all() and (w2[t, len(kt):] == 0).all()
+            if kt:  # renormalised kept weights = softmax over the token's kept logits
+                assert np.allclose(w2[t, :len(kt)], scipy.special.softmax(z[t, kt]), atol=1e-13)
+        assert st[2] == (ids >= 0).sum() - (i2 >= 0).sum()
+        assert st[3] == int(((i2 >= 0).sum(axis=1) == 0).sum())
+
+
+def test_budget_token_loses_every_expert():
+    ids = np.array([[0, 1], [0, 1], [2, 3]], dtype=np.int32)
+    w = np.array([[0.6, 0.4], [0.7, 0.3], [0.55, 0.45]])
+    i2, w2, st = O.expert_budget(ids, w, 2)
+    assert i2.tolist() == [[0, 1], [0, 1], [-1, -1]]
+    assert w2[2].tolist() == [0.0, 0.0]
+    assert st.tolist() == [4, 2, 2, 1]
+
+
+def test_budget_without_norm_topk_keeps_raw_weights():
+    ids = np.array([[0, 1], [2, 1]], dtype=np.int32)
+    w = np.array([[0.5, 0.2], [0.1, 0.3]])
+    i2, w2, st = O.expert_budget(ids, w, 2, norm_topk=False)
+    assert i2.tolist() == [[0, 1], [1, -1]]
+    assert w2.tolist() == [[0.5, 0.2], [0.3, 0.0]]
+
+
+# ----------------------------------------------------------------------------- routing statistics from the pages
+
+def test_union_of_16_experts_top2_block7_is_at_most_14():
+    g = _golden()
+    assert int(g["max_experts_touched_16_top2_block7"][0]) == 14
+    shape = W.DRAFTER
+    sizes = []
+    for seed in range(6):
+        inp = W.layer_inputs(shape, 224, 777 + seed)
+        z = O.router_logits(inp.x, inp.w_router, inp.logit_bias)
+        ids, _ = O.topk_softmax(z, shape.num_experts_per_tok)
+        for b in range(0, 224, 7):
+            sizes.append(len(set(ids[b:b + 7].ravel().tolist())))
+    assert max(sizes) <= 14 and min(sizes) >= 2
+    assert max(sizes) >= 11 and min(sizes) <= 4   # the block bias spreads the union over 2..14
+
+
+def test_uniform_routing_512_top10_block7_union():
+    g = _golden()
+    printed = float(g["experts_touched_512_top10_block7"][0])
+    E, K, T = 512, 10, 7
+    closed = E * (1 - (1 - K / E) ** T)                # 65.96 for independent uniform picks
+    rng = np.random.default_rng(6)
+    sizes = []
+    for _ in range(300):
+        ids, _ = O.topk_softmax(rng.normal(size=(T, E)), K)
+        sizes.append(len(set(ids.ravel().tolist())))
+    mean = float(np.mean(sizes))
+    assert abs(mean - closed) < 1.0
+    assert abs(mean - printed) < 2.5
+    # ~1 GB of expert weights per step vs 0.53 GB dense (bf16, H = 5120)
+    per_expert = 3 * 5120 * 512 * 2
+    assert abs(printed * per_expert / 1e9 - float(g["expert_bytes_512x512_top10_block7"][0])) < 0.1
+    assert abs(267_386_880 * 2 / 1e9 - float(g["dense_ffn_bytes"][0])) < 0.01
+
+
+def _ffn_params(H, I, E, S):
+    return 3 * H * I * E + 3 * H * S
+
+
+@pytest.mark.parametrize("key,H,I,E,K,S,which", [
+    ("ffn_params_16x1024_top2_shared2048", 5120, 1024, 16, 2, 2048, "all"),
+    ("active_params_16x1024_top2_shared2048", 5120, 1024, 16, 2, 2048, "active"),
+    ("ffn_params_16x2048_top2_shared2048", 5120, 2048, 16, 2, 2048, "all"),
+    ("active_params_16x2048_top2_shared2048", 5120, 2048, 16, 2, 2048, "active"),
+    ("active_params_16x2048_top4_shared2048", 5120, 2048, 16, 4, 2048, "active"),
+    ("ffn_params_512x512_top10_shared2048", 5120, 512, 512, 10, 2048, "all"),
+    ("active_params_512x512_top10_shared2048", 5120, 512, 512, 10, 2048, "active"),
+    ("dense_ffn_params_17408", 5120, 17408, 1, 1, 0, "all"),
+])
+def test_parameter_counts_match_the_pages(key, H, I, E, K, S, which):
+    """SwiGLU with three bias-free matrices per expert reproduces every printed count."""
+    val, _, _ = _golden()[key]
+    n = _ffn_params(H, I, E, S) if which == "all" else _ffn_params(H, I, K, S)
+    digits = len(val.rstrip("MB").split(".")[-1]) if "." in val else 0
+    scale = 1e9 if val.endswith("B") else 1e6
+    assert round(n / scale, digits) == _printed(val) / scale
+
+
+def test_workload_shapes_have_the_drafter_parameter_count():
+    shape = W.DRAFTER
+    w0 = W.expert_weights(shape, 1, 0)
+    sh = W.shared_expert_weights(shape, 1)
+    n = shape.n_routed_experts * sum(w0[k].numel() for k in ("gate", "up", "down"))
+    n += sum(sh[k].numel() for k in ("gate", "up", "down"))
+    assert n == 283_115_520
+    active = shape.num_experts_per_tok * sum(w0[k].numel() for k in ("gate", "up", "down")) \
+        + sum(sh[k].numel() for k in ("gate", "up", "down"))
+    assert active == 62_914_560
+
+
+# ----------------------------------------------------------------------------- dispatch
+
+def test_dispatch_matches_library_sort():
+    rng = np.random.default_rng(7)
+    for T, E, K in ((1, 1, 1), (13, 8, 3), (200, 64, 6), (64, 512, 10)):
+        z = rng.normal(size=(T, E))
+        ids, w = O.topk_softmax(z, K)
+        if T > 10:  # drop some slots the way the budget does
+            ids, w, _ = O.expert_budget(ids, w, max(1, E // 3))
+        counts, offsets, perm = O.dispatch(ids, E)
+        kept = np.nonzero(ids.ravel() >= 0)[0]
+        e = ids.ravel()[kept].astype(np.int64)
+        t = kept // K
+        expect = kept[np.argsort(e * T + t, kind="stable")]
+        assert np.array_equal(perm, expect)
+        assert np.array_equal(counts, np.bincount(e, minlength=E))
+        assert np.array_equal(offsets, np.concatenate([[0], np.cumsum(np.bincount(e, minlength=E))]))
+
+
+# ----------------------------------------------------------------------------- expert math
+
+def _torch_swiglu(x, wd):
+    x = torch.as_tensor(x, dtype=torch.float64)
+    g = torch.as_tensor(O.as_f64(wd["gate"]))
+    u = torch.as_tensor(O.as_f64(wd["up"]))
+    d = torch.as_tensor(O.as_f64(wd["down"]))
+    return torch.nn.functional.linear(torch.nn.functional.silu(torch.nn.functional.linear(x, g))
+                                      * torch.nn.functional.linear(x, u), d).numpy()
+
+
+def _tiny_layer(E=6, H=32, I=24, S=0, seed=8):
+    rng = np.random.default_rng(seed)
+    experts = [{k: rng.normal(scale=0.2, size=s) for k, s in
+                (("gate", (I, H)), ("up", (I, H)), ("down", (H, I)))} for _ in range(E)]
+    shared = None if S == 0 else {k: rng.normal(scale=0.2, size=s) for k, s in
+                                  (("gate", (S, H)), ("up", (S, H)), ("down", (H, S)))}
+    return rng, experts, shared
+
+
+def test_identical_experts_reduce_to_one_dense_ffn():
+    rng, experts, shared = _tiny_layer(E=5, S=16)
+    same = experts[0]
+    T, H = 9, 32
+    x = rng.normal(size=(T, H))
+    wr = rng.normal(size=(5, H))
+    wgate = rng.normal(size=H)
+    r = O.moe_layer(x, wr, wgate, None, 2, 5, lambda e: same, shared, "f32")
+    sg = 1 / (1 + np.exp(-(x @ wgate)))
+    expect = _torch_swiglu(x, same) + sg[:, None] * _torch_swiglu(x, shared)
+    assert np.allclose(r["y"], expect, rtol=1e-12, atol=1e-12)
+
+
+def test_single_expert_top1_is_the_ffn():
+    rng, experts, _ = _tiny_layer(E=1)
+    x = rng.normal(size=(7, 32))
+    r = O.moe_layer(x, rng.normal(size=(1, 32)), None, None, 1, 1, lambda e: experts[e], None, "f32")
+    assert np.allclose(r["y"], _torch_swiglu(x, experts[0]), rtol=1e-12, atol=1e-12)
+    assert r["w"].ravel().tolist() == [1.0] * 7
+
+
+def test_layer_equals_dense_masked_mixture():
+    """y = sum_e gate[t,e] * FFN_e(x_t) with the gate matrix built by torch.topk + softmax."""
+    rng, experts, shared = _tiny_layer(E=6, S=8, seed=9)
+    T, H, K = 11, 32, 3
+    x = rng.normal(size=(T, H))
+    wr = rng.normal(size=(6, H))
+    wgate = rng.normal(size=H)
+    r = O.moe_layer(x, wr, wgate, None, K, 6, lambda e: experts[e], shared, "f32")
+    z = torch.as_tensor(x @ wr.T)
+    top = torch.topk(z, K, dim=1)
+    gate = torch.zeros_like(z).scatter(1, top.indices, torch.softmax(top.values, dim=1)).numpy()
+    expect = sum(gate[:, e:e + 1] * _torch_swiglu(x, experts[e]) for e in range(6))
+    expect = expect + torch.sigmoid(torch.as_tensor(x @ wgate)).numpy()[:, None] * _torch_swiglu(x, shared)
+    assert np.allclose(r["y"], expect, rtol=1e-11, atol=1e-12)
+    # subset evaluation equals the full evaluation row by row
+    sub = [10, 0, 5]
+    r2 = O.moe_combine(x, r["ids"], r["w"], r["shared_gate"], lambda e: experts[e], shared, "f32", sub)
+    assert np.allclose(r2, r["y"][sub], rtol=1e-13, atol=1e-14)
+
+
+def test_token_with_no_kept_expert_and_no_shared_is_exactly_zero():
+    rng, experts, _ = _tiny_layer(E=4, seed=10)
+    x = rng.normal(size=(3, 32))
+    ids = np.array([[0, 1], [-1, -1], [2, -1]], dtype=np.int32)
+    w = np.array([[0.5, 0.5], [0.0, 0.0], [1.0, 0.0]])
+    y = O.moe_combine(x, ids, w, None, lambda e: experts[e], None, "f32")
+    assert (y[1] == 0).all() and (y[0] != 0).all()
+
+
+# ----------------------------------------------------------------------------- e4m3 codec (OCP spec)
+
+def test_e4m3_decode_all_codes_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    mine = e4m3.decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+    assert np.array_equal(mine[~nan], ref[~nan])
+    assert mine[0x7E] == 448.0 and mine[0x01] == 2.0 ** -9 and mine[0x08] == 2.0 ** -6
+
+
+def test_e4m3_encode_matches_torch_on_dense_sweep():
+    rng = np.random.default_rng(11)
+    v = np.concatenate([
+        rng.uniform(-448, 448, 200_000),
+        rng.normal(scale=0.01, size=100_000),
+        np.exp2(rng.uniform(-12, 8.8, 100_000)) * rng.choice([-1, 1], 100_000),
+        e4m3.decode(np.arange(256, dtype=np.uint8)[[c for c in range(256) if c not in (0x7F, 0xFF)]]),
+    ]).astype(np.float32)
+    # exact midpoints between neighbouring codes exercise ties-to-even
+    fin = np.sort(np.unique(e4m3.decode(np.arange(0, 0x7F, dtype=np.uint8))))
+    mids = ((fin[1:] + fin[:-1]) / 2).astype(np.float32)
+    v = np.clip(np.concatenate([v, mids, -mids]), -448, 448).astype(np.float32)
+    mine = e4m3.encode_rne(v)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    same = (mine == ref) | ((mine & 0x7F) == 0) & ((ref & 0x7F) == 0)
+    assert same.all(), v[~same][:10]
+
+
+def test_e4m3_round_trip_every_finite_code():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    for s in (1.0, 2.0 ** -7, 2.0 ** 5):
+        back = e4m3.encode_rne(e4m3.decode(codes) * s / s)
+        assert np.array_equal(back, codes)
+
+
+def test_quantise_group128_bounds_and_special_cases():
+    rng = np.random.default_rng(12)
+    v = rng.normal(size=(5, 384)).astype(np.float32)
+    v[2, 128:256] = 0.0
+    q, s = e4m3.quantise_group128(v)
+    assert s.shape == (5, 3) and s[2, 1] == 1.0 and (q[2, 128:256] & 0x7F == 0).all()
+    d = e4m3.dequantise_group128(q, s)
+    # at most half an e4m3 step of the scaled value (3 mantissa bits; 2^-9 in the subnormal range),
+    # plus the float32 rounding of v / s
+    sr = np.repeat(s, 128, axis=1).astype(np.float64)
+    a = np.abs(v / sr)
+    step = np.maximum(np.exp2(np.floor(np.log2(np.maximum(a, 1e-30))) - 3), 2.0 ** -9)
+    assert (np.abs(d - v) <= sr * (step / 2 + a * 2.0 ** -23)).all()
+    # the amax element of each non-zero group lands on +-448 (or its neighbour under fp32 rounding of s)
+    amax_codes = np.abs(e4m3.decode(q)).reshape(5, 3, 128).max(axis=2)
+    assert ((amax_codes[s != 1.0] >= 416) & (amax_codes[s != 1.0] <= 448)).all()
+
+
+def test_fp8_swiglu_matches_torch_float8_pipeline():
+    """The fp8 expert path vs the same pipeline built from torch's float8_e4m3fn casts."""
+    shape = W.LARGE_FP8.with_(hidden_size=256, moe_intermediate_size=256)
+    wd = W.expert_weights(shape, 3, 0)
+    x = torch.randn(6, 256, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    mine = O.swiglu_ffn(O.as_f64(x), wd, "fp8_e4m3_g128")
+
+    def tq(v):  # torch: fp32 amax/448, fp32 divide, clamp, float8 cast, dequantise in float64
+        v = v.to(torch.float32).reshape(v.shape[0], -1, 128)
+        amax = v.abs().amax(dim=2, keepdim=True)
+        s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+        q = (v / s).clamp(-448, 448).to(torch.float8_e4m3fn)
+        return (q.to(torch.float64) * s.to(torch.float64)).reshape(v.shape[0], -1)
+
+    def tw(name):
+        q = wd[name].view(torch.float8_e4m3fn).to(torch.float64)
+        s = wd[name + "_s"].to(torch.float64)
+        return (q.reshape(q.shape[0], -1, 128) * s[:, :, None]).reshape(q.shape)
+
+    xa = tq(x)
+    a = xa @ tw("gate").T
+    b = xa @ tw("up").T
+    h = torch.nn.functional.silu(a) * b
+    ref = tq(h.to(torch.float32)) @ tw("down").T
+    assert np.allclose(mine, ref.numpy(), rtol=1e-12, atol=1e-12)

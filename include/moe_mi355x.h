@@ -1,0 +1,179 @@
+/*
+ * moe_mi355x.h -- C ABI of the routed Mixture-of-Experts FFN forward for AMD
+ * MI355X (gfx950).
+ *
+ * The layer (one call sequence per batch of T tokens):
+ *   moe_route     router logits, softmax top-k with renormalisation, optional
+ *                 cross-token expert budget, sigmoid shared-expert gate;
+ *   moe_dispatch  per-expert counts, exclusive offsets, and the slot
+ *                 permutation sorted by (expert, token);
+ *   moe_forward   routed SwiGLU experts (grouped gate/up with fused SwiGLU, then
+ *                 down with the gate-weighted combine) plus the shared expert.
+ *
+ * The problem statement is the pages' config keys: hidden size,
+ * n_routed_experts, moe_intermediate_size, num_experts_per_tok, a shared
+ * expert width [SpecForge PR #943, "Modifications"], the weight dtype, and an
+ * expert budget [colibri issue_budget.md, "TL;DR" and "How it works"].
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers marked (device) are device pointers; (host) are host pointers.
+ *     The caller owns every buffer.  The library allocates nothing, keeps no
+ *     mutable global state and caches nothing between calls.
+ *   - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     default stream).  Nothing synchronises with the host and nothing is copied
+ *     device-to-host, so the calls may be captured into a HIP graph.
+ *   - Row-major layouts; "[A, B]" means A rows of B contiguous elements.
+ *   - Every argument is validated on the host before anything is launched.  The
+ *     return value is MOE_OK (0) or a negative moe_status; on error nothing has
+ *     been enqueued and no output has been touched.  No exception or abort
+ *     crosses this boundary.  MOE_ERR_LAUNCH_FAILED reports a HIP launch error
+ *     (earlier launches of the same call may already be enqueued).
+ *   - T = 0 is valid and enqueues nothing.
+ *   - Supported dtype combinations (weight_dtype / act_dtype):
+ *       F32 / F32, BF16 / BF16, FP8_E4M3_G128 / BF16.
+ *     With BF16 or FP8 weights, hidden_size, moe_intermediate_size and
+ *     shared_expert_intermediate_size must be multiples of 128
+ *     (MOE_ERR_UNSUPPORTED otherwise).  1 <= n_routed_experts <= 512,
+ *     1 <= num_experts_per_tok <= min(n_routed_experts, 16).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_NULL_PTR = -1,            /* a required pointer is NULL                  */
+  MOE_ERR_BAD_SHAPE = -2,           /* a size is out of range                      */
+  MOE_ERR_BAD_DTYPE = -3,           /* unknown dtype or unsupported combination    */
+  MOE_ERR_UNSUPPORTED = -4,         /* valid but not implemented (alignment, E>512) */
+  MOE_ERR_WORKSPACE_TOO_SMALL = -5, /* ws_bytes < moe_workspace_size(...)          */
+  MOE_ERR_LAUNCH_FAILED = -6        /* a HIP launch reported an error              */
+} moe_status;
+
+typedef enum moe_dtype {
+  MOE_DTYPE_F32 = 0,
+  MOE_DTYPE_BF16 = 1,
+  /* OCP FP8 E4M3 ("e4m3fn": bias 7, max 448, no inf) codes, one byte each, with a
+   * float32 scale per output row and per group of 128 consecutive elements of the
+   * contraction dimension: w = decode(q) * s.  Activations that meet these
+   * weights in a contraction are quantised the same way inside the kernels,
+   * per token row and 128-group: s = amax/448 (s = 1 if amax = 0),
+   * q = RNE(clamp(v/s, +-448)).  Group-128 scaling follows [colibri
+   * issue_budget.md, header notes on issue_grouped_quant.md]; the fp8 x fp8
+   * expert contraction follows the W8A8 MoE path that [DeepGEMM fork PR #5,
+   * "Performance"] compares against. */
+  MOE_DTYPE_FP8_E4M3_G128 = 2
+} moe_dtype;
+
+typedef struct moe_config {
+  int32_t hidden_size;                     /* H                                             */
+  int32_t n_routed_experts;                /* E, 1..512                                     */
+  int32_t moe_intermediate_size;           /* I, width of each routed expert                */
+  int32_t num_experts_per_tok;             /* K, 1..min(E,16)                               */
+  int32_t shared_expert_intermediate_size; /* S, 0 = no shared expert                        */
+  int32_t weight_dtype;                    /* moe_dtype of routed and shared expert weights  */
+  int32_t act_dtype;                       /* moe_dtype of x, w_router, w_shared_gate        */
+  int32_t norm_topk_prob;                  /* 1: renormalise the kept top-k weights to sum 1 */
+  int32_t expert_budget;                   /* B >= 0, 0 = off: cap on distinct routed experts
+                                              over the whole batch [colibri issue_budget.md] */
+} moe_config;
+
+/* Expert weights, all (device).  The contraction dimension is contiguous.
+ *   w_gate, w_up   [E, I, H]      w_down [E, H, I]
+ *   s_gate, s_up   [E, I, H/128]  s_down [E, H, I/128]   (FP8 only, else NULL)
+ *   ws_gate, ws_up [S, H]         ws_down [H, S]         (S > 0 only, else NULL)
+ *   ss_gate, ss_up [S, H/128]     ss_down [H, S/128]     (FP8 and S > 0 only)
+ * Element type is weight_dtype (one byte per element for FP8). */
+typedef struct moe_expert_weights {
+  const void *w_gate, *w_up, *w_down;
+  const float *s_gate, *s_up, *s_down;
+  const void *ws_gate, *ws_up, *ws_down;
+  const float *ss_gate, *ss_up, *ss_down;
+} moe_expert_weights;
+
+/* Bytes of device workspace needed by moe_route / moe_dispatch / moe_forward for
+ * any T <= max_tokens.  One workspace may be reused by consecutive calls on one
+ * stream; moe_forward_gate_up and moe_forward_down must see the same workspace
+ * (the intermediate activations live there).  bytes: (host) out. */
+int moe_workspace_size(const moe_config* cfg, int32_t max_tokens, size_t* bytes);
+
+/* Router: logits z[t,e] = x_t . w_router[e] (+ logit_bias[t,e]) accumulated in
+ * float32; softmax over the E experts, keep the K largest (ties: lower expert
+ * id), renormalise them to sum 1 if norm_topk_prob [SpecForge PR #943,
+ * "Modifications": softmax, renormalised top-k]; then, if expert_budget > 0 and
+ * the batch uses more than B distinct experts, keep the B experts with the
+ * largest summed weight (ties: lower id), drop the other slots and renormalise
+ * each token's kept weights [colibri issue_budget.md, "How it works" steps 1-5].
+ *   x            (device) [T, H] act_dtype
+ *   w_router     (device) [E, H] act_dtype
+ *   w_shared_gate(device) [H] act_dtype; required iff S > 0, else ignored
+ *   logit_bias   (device) [T, E] float32 or NULL (added to the logits)
+ *   topk_ids     (device) out [T, K] int32, by descending weight; dropped slots
+ *                are moved to the end of their row as id -1
+ *   topk_weights (device) out [T, K] float32; 0 for dropped slots
+ *   shared_gate  (device) out [T] float32 sigmoid(x_t . w_shared_gate); required
+ *                iff S > 0, else ignored
+ *   route_stats  (device) out int32[4] or NULL: {distinct experts before the
+ *                budget, after, dropped slots, tokens left with no expert}
+ * A token that loses every expert to the budget keeps ids -1 / weights 0. */
+int moe_route(const moe_config* cfg, int32_t num_tokens, const void* x, const void* w_router,
+              const void* w_shared_gate, const float* logit_bias, int32_t* topk_ids,
+              float* topk_weights, float* shared_gate, int32_t* route_stats, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/* Dispatch: expert_counts[e] = number of slots with id e (ids < 0 are skipped);
+ * expert_offsets = exclusive prefix sum of counts (E+1 entries, last = kept
+ * slots); perm[offsets[e] + j] = t*K + k for the j-th token (ascending t) routed
+ * to e.  Entries of perm past offsets[E] are left untouched.
+ *   topk_ids (device) [T, K] int32 in [-1, E)
+ *   expert_counts (device) out [E], expert_offsets (device) out [E+1],
+ *   perm (device) out [T*K] int32 */
+int moe_dispatch(const moe_config* cfg, int32_t num_tokens, const int32_t* topk_ids,
+                 int32_t* expert_counts, int32_t* expert_offsets, int32_t* perm, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/* Experts and combine:
+ *   y[t,:] = sum_k topk_weights[t,k] * down_e(silu(gate_e x_t) * up_e x_t)
+ *          + shared_gate[t] * down_s(silu(gate_s x_t) * up_s x_t)
+ * with e = topk_ids[t,k], taken through the dispatch outputs.  y (device) out
+ * [T, H] float32, overwritten.  The intermediate activations are stored in the
+ * workspace as bf16 (BF16 weights), float32 (F32) or e4m3 + group-128 scales
+ * (FP8).  Accumulation is float32; the combine uses float32 atomics, so the
+ * bits of y may vary between runs in the last place. */
+int moe_forward(const moe_config* cfg, int32_t num_tokens, const void* x,
+                const float* topk_weights, const float* shared_gate,
+                const int32_t* expert_counts, const int32_t* expert_offsets, const int32_t* perm,
+                const moe_expert_weights* weights /* (host) struct of (device) pointers */,
+                float* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two halves of moe_forward, same arguments, for callers that time or
+ * overlap them: gate_up zero-fills y and writes the intermediate activations to
+ * the workspace; down reads them and accumulates into y.  Calling gate_up then
+ * down on one stream with one workspace equals moe_forward. */
+int moe_forward_gate_up(const moe_config* cfg, int32_t num_tokens, const void* x,
+                        const float* topk_weights, const float* shared_gate,
+                        const int32_t* expert_counts, const int32_t* expert_offsets,
+                        const int32_t* perm, const moe_expert_weights* weights, float* y,
+                        void* workspace, size_t workspace_bytes, void* stream);
+int moe_forward_down(const moe_config* cfg, int32_t num_tokens, const void* x,
+                     const float* topk_weights, const float* shared_gate,
+                     const int32_t* expert_counts, const int32_t* expert_offsets,
+                     const int32_t* perm, const moe_expert_weights* weights, float* y,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* moe_status_string(int status);
+
+/* Library version, e.g. 0x000100 = 0.1.0. */
+int moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

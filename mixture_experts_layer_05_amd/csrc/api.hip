@@ -1,0 +1,273 @@
+// C ABI: argument validation, workspace layout, and the launches of each call.
+// Everything is enqueued on the caller's stream; nothing is allocated, nothing is
+// read back to the host.
+#include <algorithm>
+
+#include "../../include/moe_mi355x.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+bool valid_dtype(int d) { return d == MOE_DTYPE_F32 || d == MOE_DTYPE_BF16 || d == MOE_DTYPE_FP8_E4M3_G128; }
+
+// Shape and dtype checks shared by every entry point.
+int check_config(const moe_config* c) {
+  if (!c) return MOE_ERR_NULL_PTR;
+  if (!valid_dtype(c->weight_dtype) || !valid_dtype(c->act_dtype)) return MOE_ERR_BAD_DTYPE;
+  const bool combo = (c->weight_dtype == MOE_DTYPE_F32 && c->act_dtype == MOE_DTYPE_F32) ||
+                     (c->weight_dtype == MOE_DTYPE_BF16 && c->act_dtype == MOE_DTYPE_BF16) ||
+                     (c->weight_dtype == MOE_DTYPE_FP8_E4M3_G128 && c->act_dtype == MOE_DTYPE_BF16);
+  if (!combo) return MOE_ERR_BAD_DTYPE;
+  if (c->hidden_size <= 0 || c->moe_intermediate_size <= 0 || c->n_routed_experts <= 0 ||
+      c->num_experts_per_tok <= 0 || c->shared_expert_intermediate_size < 0 || c->expert_budget < 0 ||
+      (c->norm_topk_prob != 0 && c->norm_topk_prob != 1))
+    return MOE_ERR_BAD_SHAPE;
+  if (c->num_experts_per_tok > c->n_routed_experts) return MOE_ERR_BAD_SHAPE;
+  if (c->n_routed_experts > kMaxExperts || c->num_experts_per_tok > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  if (c->weight_dtype != MOE_DTYPE_F32) {
+    if (c->hidden_size % 128 || c->moe_intermediate_size % 128 ||
+        c->shared_expert_intermediate_size % 128)
+      return MOE_ERR_UNSUPPORTED;
+  }
+  // Index arithmetic is 32-bit inside the kernels for rows and slots.
+  if (static_cast<int64_t>(c->hidden_size) * c->moe_intermediate_size > (1LL << 31))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_tokens(const moe_config* c, int32_t T) {
+  if (T < 0) return MOE_ERR_BAD_SHAPE;
+  if (static_cast<int64_t>(T) * c->num_experts_per_tok >= (1LL << 31) / 2) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+struct Layout {
+  size_t z, h, xq, xs, hq, hs, total;
+  int ldz;
+  size_t h_shared;  // element offset of the shared expert's rows in h
+};
+
+Layout layout(const moe_config& c, int64_t T) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    const size_t o = off;
+    off = align_up(off + n, kAlign);
+    return o;
+  };
+  const int E = c.n_routed_experts;
+  L.ldz = static_cast<int>(align_up(E + 1, 16));
+  L.z = take(static_cast<size_t>(T) * L.ldz * sizeof(float));
+  const size_t routed = static_cast<size_t>(T) * c.num_experts_per_tok * c.moe_intermediate_size;
+  const size_t elems = routed + static_cast<size_t>(T) * c.shared_expert_intermediate_size;
+  L.h_shared = routed;
+  const size_t hsize = (c.weight_dtype == MOE_DTYPE_BF16) ? 2 : 4;
+  L.h = take(elems * hsize);
+  if (c.weight_dtype == MOE_DTYPE_FP8_E4M3_G128) {
+    L.xq = take(static_cast<size_t>(T) * c.hidden_size);
+    L.xs = take(static_cast<size_t>(T) * (c.hidden_size / kGroup) * sizeof(float));
+    L.hq = take(elems);
+    L.hs = take(elems / kGroup * sizeof(float));
+  }
+  L.total = std::max<size_t>(off, kAlign);
+  return L;
+}
+
+int check_workspace(const moe_config& c, int32_t T, const void* ws, size_t ws_bytes, Layout* L) {
+  *L = layout(c, T);
+  if (!ws) return MOE_ERR_NULL_PTR;
+  if (ws_bytes < L->total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return MOE_OK;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH_FAILED; }
+
+int check_forward(const moe_config* cfg, int32_t T, const void* x, const float* topk_w,
+                  const float* shared_gate, const int32_t* counts, const int32_t* offsets,
+                  const int32_t* perm, const moe_expert_weights* w, float* y) {
+  int st = check_config(cfg);
+  if (st) return st;
+  if ((st = check_tokens(cfg, T))) return st;
+  if (!x || !topk_w || !counts || !offsets || !perm || !w || !y) return MOE_ERR_NULL_PTR;
+  if (!w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_NULL_PTR;
+  const bool fp8 = cfg->weight_dtype == MOE_DTYPE_FP8_E4M3_G128;
+  if (fp8 && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_NULL_PTR;
+  if (cfg->shared_expert_intermediate_size > 0) {
+    if (!shared_gate || !w->ws_gate || !w->ws_up || !w->ws_down) return MOE_ERR_NULL_PTR;
+    if (fp8 && (!w->ss_gate || !w->ss_up || !w->ss_down)) return MOE_ERR_NULL_PTR;
+  }
+  if (reinterpret_cast<uintptr_t>(y) % 16) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+ExpertArgs expert_args(const moe_config& c, int32_t T, const void* x, const float* topk_w,
+                       const float* shared_gate, const int32_t* counts, const int32_t* offsets,
+                       const int32_t* perm, const moe_expert_weights& w, float* y, void* ws,
+                       const Layout& L) {
+  ExpertArgs a{};
+  a.x = x;
+  a.counts = counts;
+  a.offsets = offsets;
+  a.perm = perm;
+  a.topk_w = topk_w;
+  a.shared_gate = shared_gate;
+  a.w_gate = w.w_gate; a.w_up = w.w_up; a.w_down = w.w_down;
+  a.s_gate = w.s_gate; a.s_up = w.s_up; a.s_down = w.s_down;
+  a.ws_gate = w.ws_gate; a.ws_up = w.ws_up; a.ws_down = w.ws_down;
+  a.ss_gate = w.ss_gate; a.ss_up = w.ss_up; a.ss_down = w.ss_down;
+  a.h = at<void>(ws, L.h);
+  a.h_shared = L.h_shared;
+  if (c.weight_dtype == MOE_DTYPE_FP8_E4M3_G128) {
+    a.xq = at<uint8_t>(ws, L.xq);
+    a.xs = at<float>(ws, L.xs);
+    a.hq = at<uint8_t>(ws, L.hq);
+    a.hs = at<float>(ws, L.hs);
+  }
+  a.y = y;
+  a.T = T;
+  a.H = c.hidden_size;
+  a.I = c.moe_intermediate_size;
+  a.S = c.shared_expert_intermediate_size;
+  a.E = c.n_routed_experts;
+  a.K = c.num_experts_per_tok;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_version(void) { return 0x000100; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL_PTR: return "a required pointer is NULL";
+    case MOE_ERR_BAD_SHAPE: return "a size is out of range";
+    case MOE_ERR_BAD_DTYPE: return "unknown dtype or unsupported dtype combination";
+    case MOE_ERR_UNSUPPORTED: return "configuration not supported (alignment or limits)";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than moe_workspace_size()";
+    case MOE_ERR_LAUNCH_FAILED: return "a HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_workspace_size(const moe_config* cfg, int32_t max_tokens, size_t* bytes) {
+  int st = check_config(cfg);
+  if (st) return st;
+  if (!bytes) return MOE_ERR_NULL_PTR;
+  if ((st = check_tokens(cfg, max_tokens))) return st;
+  *bytes = layout(*cfg, max_tokens).total;
+  return MOE_OK;
+}
+
+int moe_route(const moe_config* cfg, int32_t T, const void* x, const void* w_router,
+              const void* w_shared_gate, const float* logit_bias, int32_t* topk_ids, float* topk_w,
+              float* shared_gate, int32_t* route_stats, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_config(cfg);
+  if (st) return st;
+  if ((st = check_tokens(cfg, T))) return st;
+  const bool has_shared = cfg->shared_expert_intermediate_size > 0;
+  if (!x || !w_router || !topk_ids || !topk_w) return MOE_ERR_NULL_PTR;
+  if (has_shared && (!w_shared_gate || !shared_gate)) return MOE_ERR_NULL_PTR;
+  Layout L;
+  if ((st = check_workspace(*cfg, T, ws, ws_bytes, &L))) return st;
+  if (T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int E = cfg->n_routed_experts, H = cfg->hidden_size, K = cfg->num_experts_per_tok;
+  const int ncols = E + (has_shared ? 1 : 0);
+  float* z = at<float>(ws, L.z);
+  if (cfg->act_dtype == MOE_DTYPE_BF16) {
+    dim3 grid(static_cast<unsigned>(ceil_div(T, 16)), static_cast<unsigned>(ceil_div(ncols, 16)));
+    router_logits_bf16_kernel<<<grid, 256, 0, s>>>(
+        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
+        static_cast<const uint16_t*>(has_shared ? w_shared_gate : w_router), T, H, E, ncols, z, L.ldz);
+  } else {
+    const int64_t items = static_cast<int64_t>(T) * ncols;
+    router_logits_f32_kernel<<<static_cast<unsigned>(ceil_div(items, 4)), 256, 0, s>>>(
+        static_cast<const float*>(x), static_cast<const float*>(w_router),
+        static_cast<const float*>(has_shared ? w_shared_gate : w_router), T, H, E, ncols, z, L.ldz);
+  }
+  if ((st = launched(hipGetLastError()))) return st;
+  topk_kernel<<<static_cast<unsigned>(ceil_div(T, 4)), 256, 0, s>>>(
+      z, L.ldz, logit_bias, T, E, K, cfg->norm_topk_prob, has_shared ? 1 : 0, topk_ids, topk_w,
+      shared_gate);
+  if ((st = launched(hipGetLastError()))) return st;
+  if (cfg->expert_budget > 0 || route_stats) {
+    budget_kernel<<<1, 1024, 0, s>>>(topk_ids, topk_w, T, E, K, cfg->expert_budget,
+                                     cfg->norm_topk_prob, route_stats);
+    if ((st = launched(hipGetLastError()))) return st;
+  }
+  return MOE_OK;
+}
+
+int moe_dispatch(const moe_config* cfg, int32_t T, const int32_t* topk_ids, int32_t* counts,
+                 int32_t* offsets, int32_t* perm, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_config(cfg);
+  if (st) return st;
+  if ((st = check_tokens(cfg, T))) return st;
+  if (!topk_ids || !counts || !offsets || !perm) return MOE_ERR_NULL_PTR;
+  Layout L;
+  if ((st = check_workspace(*cfg, T, ws, ws_bytes, &L))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  dispatch_kernel<<<1, 1024, 0, s>>>(topk_ids, T, cfg->n_routed_experts, cfg->num_experts_per_tok,
+                                     counts, offsets, perm);
+  return launched(hipGetLastError());
+}
+
+int moe_forward_gate_up(const moe_config* cfg, int32_t T, const void* x, const float* topk_w,
+                        const float* shared_gate, const int32_t* counts, const int32_t* offsets,
+                        const int32_t* perm, const moe_expert_weights* w, float* y, void* ws,
+                        size_t ws_bytes, void* stream) {
+  int st = check_forward(cfg, T, x, topk_w, shared_gate, counts, offsets, perm, w, y);
+  if (st) return st;
+  Layout L;
+  if ((st = check_workspace(*cfg, T, ws, ws_bytes, &L))) return st;
+  if (T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const ExpertArgs a = expert_args(*cfg, T, x, topk_w, shared_gate, counts, offsets, perm, *w, y, ws, L);
+  if (cfg->weight_dtype == MOE_DTYPE_FP8_E4M3_G128) {
+    if ((st = launched(launch_quant_x(a, at<uint8_t>(ws, L.xq), at<float>(ws, L.xs), s)))) return st;
+  }
+  if ((st = launched(launch_gate_up(a, cfg->weight_dtype, s)))) return st;
+  if (cfg->weight_dtype == MOE_DTYPE_FP8_E4M3_G128) {
+    if ((st = launched(launch_quant_h(a, at<uint8_t>(ws, L.hq), at<float>(ws, L.hs), s)))) return st;
+  }
+  return MOE_OK;
+}
+
+int moe_forward_down(const moe_config* cfg, int32_t T, const void* x, const float* topk_w,
+                     const float* shared_gate, const int32_t* counts, const int32_t* offsets,
+                     const int32_t* perm, const moe_expert_weights* w, float* y, void* ws,
+                     size_t ws_bytes, void* stream) {
+  int st = check_forward(cfg, T, x, topk_w, shared_gate, counts, offsets, perm, w, y);
+  if (st) return st;
+  Layout L;
+  if ((st = check_workspace(*cfg, T, ws, ws_bytes, &L))) return st;
+  if (T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const ExpertArgs a = expert_args(*cfg, T, x, topk_w, shared_gate, counts, offsets, perm, *w, y, ws, L);
+  return launched(launch_down(a, cfg->weight_dtype, s));
+}
+
+int moe_forward(const moe_config* cfg, int32_t T, const void* x, const float* topk_w,
+                const float* shared_gate, const int32_t* counts, const int32_t* offsets,
+                const int32_t* perm, const moe_expert_weights* w, float* y, void* ws, size_t ws_bytes,
+                void* stream) {
+  int st = moe_forward_gate_up(cfg, T, x, topk_w, shared_gate, counts, offsets, perm, w, y, ws,
+                               ws_bytes, stream);
+  if (st) return st;
+  return moe_forward_down(cfg, T, x, topk_w, shared_gate, counts, offsets, perm, w, y, ws, ws_bytes,
+                          stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Kernel declarations and the argument block shared by the expert kernels.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// Everything an expert kernel may need.  Unused fields are null / zero.
+//
+// Intermediate activations h: routed rows first, in dispatch (perm) order,
+// [T*K, I]; then the shared expert's rows [T, S] starting at element h_shared.
+// With fp8 weights h is kept in float32 and then quantised to hq / hs with the
+// same layout (hs has one float per 128 elements).
+struct ExpertArgs {
+  const void* x;                 // [T, H] act dtype
+  const int32_t* counts;         // [E]
+  const int32_t* offsets;        // [E+1]
+  const int32_t* perm;           // [T*K]
+  const float* topk_w;           // [T, K]
+  const float* shared_gate;      // [T]
+  const void *w_gate, *w_up, *w_down;
+  const float *s_gate, *s_up, *s_down;
+  const void *ws_gate, *ws_up, *ws_down;
+  const float *ss_gate, *ss_up, *ss_down;
+  void* h;
+  size_t h_shared;               // element offset of the shared rows in h / hq
+  const uint8_t* xq;             // fp8: quantised x [T, H]
+  const float* xs;               // fp8: scales [T, H/128]
+  const uint8_t* hq;             // fp8: quantised h
+  const float* hs;               // fp8: scales of h
+  float* y;                      // [T, H]
+  int T, H, I, S, E, K;
+};
+
+// route.hip
+__global__ void router_logits_bf16_kernel(const uint16_t*, const uint16_t*, const uint16_t*, int, int,
+                                          int, int, float*, int);
+__global__ void router_logits_f32_kernel(const float*, const float*, const float*, int, int, int, int,
+                                         float*, int);
+__global__ void topk_kernel(const float*, int, const float*, int, int, int, int, int, int32_t*, float*,
+                            float*);
+__global__ void budget_kernel(int32_t*, float*, int, int, int, int, int, int32_t*);
+
+// dispatch.hip
+__global__ void dispatch_kernel(const int32_t*, int, int, int, int32_t*, int32_t*, int32_t*);
+
+// experts.hip: host-side launchers (they pick tile shapes and grid sizes).
+hipError_t launch_gate_up(const ExpertArgs& a, int weight_dtype, hipStream_t stream);
+hipError_t launch_down(const ExpertArgs& a, int weight_dtype, hipStream_t stream);
+hipError_t launch_quant_x(const ExpertArgs& a, uint8_t* xq, float* xs, hipStream_t stream);
+hipError_t launch_quant_h(const ExpertArgs& a, uint8_t* hq, float* hs, hipStream_t stream);
+
+}  // namespace moe

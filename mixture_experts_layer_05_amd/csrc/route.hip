@@ -1,0 +1,245 @@
+// Router: logits GEMV, softmax top-k with renormalisation, expert budget.
+//
+// Logits z[t,e] = x_t . W_r[e] are accumulated in float32; the shared-expert gate
+// logit x_t . w_g rides along as one extra column.  Selection follows the
+// "softmax, renormalised top-k" preset of [SpecForge PR #943, "Modifications"];
+// the budget follows [colibri issue_budget.md, "How it works", steps 1-5].
+#include "kernels.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------ logits, bf16 (MFMA)
+//
+// One workgroup = 4 waves computes a 16-token x 16-column tile; the waves split
+// the hidden dimension into four contiguous ranges and their partial tiles are
+// summed through LDS.  Column c < E is W_r[c], column E (if present) is w_g, the
+// rest of the padded tile is skipped.  Every product of two bf16 values is exact
+// in float32 and the MFMA accumulates in float32.
+__global__ void __launch_bounds__(256) router_logits_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_router,
+    const uint16_t* __restrict__ w_gate_col, int T, int H, int E, int ncols,
+    float* __restrict__ z, int ldz) {
+  __shared__ f32x4 red[4][kWave];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int t0 = blockIdx.x * 16, c0 = blockIdx.y * 16;
+  const int t = min(t0 + r, T - 1);
+  const int c = min(c0 + r, ncols - 1);
+  const uint16_t* arow = x + static_cast<size_t>(t) * H;
+  const uint16_t* brow = (c < E) ? w_router + static_cast<size_t>(c) * H : w_gate_col;
+  const int nch = H / 128;
+  const int kb = (wave * nch) / 4, ke = ((wave + 1) * nch) / 4;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int kc = kb; kc < ke; ++kc) {
+    const int k = kc * 128 + 32 * g;
+    uint4 a[4], b[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      a[s] = *reinterpret_cast<const uint4*>(arow + k + 8 * s);
+      b[s] = *reinterpret_cast<const uint4*>(brow + k + 8 * s);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = mfma_bf16_16x16x32(a[s], b[s], acc);
+  }
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    f32x4 s = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      f32x4 o = red[w][lane];
+      s[0] += o[0]; s[1] += o[1]; s[2] += o[2]; s[3] += o[3];
+    }
+    const int col = c0 + mfma16_col(lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = t0 + mfma16_row(lane, i);
+      if (row < T && col < ncols) z[static_cast<size_t>(row) * ldz + col] = s[i];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ logits, f32 (FMA)
+//
+// One wave per (token, column): lanes stride the hidden dimension, then a wave sum.
+__global__ void __launch_bounds__(256) router_logits_f32_kernel(
+    const float* __restrict__ x, const float* __restrict__ w_router,
+    const float* __restrict__ w_gate_col, int T, int H, int E, int ncols,
+    float* __restrict__ z, int ldz) {
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= T * ncols) return;
+  const int t = item / ncols, c = item % ncols;
+  const float* a = x + static_cast<size_t>(t) * H;
+  const float* b = (c < E) ? w_router + static_cast<size_t>(c) * H : w_gate_col;
+  float s = 0.f;
+  for (int h = lane; h < H; h += kWave) s = fmaf(a[h], b[h], s);
+  s = wave_sum(s);
+  if (lane == 0) z[static_cast<size_t>(t) * ldz + c] = s;
+}
+
+// ------------------------------------------------------------------ top-k
+//
+// One wave per token.  Lane l holds experts l, l+64, ... (up to 8 each).  K rounds
+// of a wave-wide argmax on (logit desc, id asc) pick the ids in descending
+// order.  Weights: exp(z_k - z_max) over the K picks, divided by their sum
+// (renormalised top-k) or by the sum over all E experts (plain softmax).
+__global__ void __launch_bounds__(256) topk_kernel(
+    const float* __restrict__ z, int ldz, const float* __restrict__ bias, int T, int E, int K,
+    int norm_topk, int has_shared, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+    float* __restrict__ shared_gate) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* zr = z + static_cast<size_t>(t) * ldz;
+  float v[kMaxExperts / kWave];
+#pragma unroll
+  for (int j = 0; j < kMaxExperts / kWave; ++j) {
+    const int e = lane + kWave * j;
+    float val = -INFINITY;
+    if (e < E) {
+      val = zr[e];
+      if (bias) val += bias[static_cast<size_t>(t) * E + e];
+    }
+    v[j] = val;
+  }
+  // Plain-softmax denominator (only needed without renormalisation).
+  float zmax = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kMaxExperts / kWave; ++j) zmax = fmaxf(zmax, v[j]);
+  zmax = wave_max(zmax);
+  float denom_all = 0.f;
+  if (!norm_topk) {
+#pragma unroll
+    for (int j = 0; j < kMaxExperts / kWave; ++j)
+      if (lane + kWave * j < E) denom_all += expf(v[j] - zmax);
+    denom_all = wave_sum(denom_all);
+  }
+  int my_id = -1;
+  float my_z = 0.f;
+  for (int k = 0; k < K; ++k) {
+    // Lane-local best: largest value, lowest id on ties (ids grow with j).
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < kMaxExperts / kWave; ++j) {
+      const int e = lane + kWave * j;
+      if (e < E && (v[j] > bv || (v[j] == bv && e < be))) { bv = v[j]; be = e; }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, kWave);
+      const int oe = __shfl_xor(be, o, kWave);
+      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+    }
+    if ((be & 63) == lane) {
+#pragma unroll
+      for (int j = 0; j < kMaxExperts / kWave; ++j)
+        if (j == (be >> 6)) v[j] = -INFINITY;
+    }
+    if (lane == k) { my_id = be; my_z = bv; }
+  }
+  // The first pick is the maximum logit.
+  const float zmax_k = __shfl(my_z, 0, kWave);
+  float p = (lane < K) ? expf(my_z - zmax_k) : 0.f;
+  float denom = norm_topk ? wave_sum(p) : denom_all * expf(zmax - zmax_k);
+  if (lane < K) {
+    topk_ids[static_cast<size_t>(t) * K + lane] = my_id;
+    topk_w[static_cast<size_t>(t) * K + lane] = p / denom;
+  }
+  if (has_shared && lane == 0) shared_gate[t] = 1.0f / (1.0f + expf(-zr[E]));
+}
+
+// ------------------------------------------------------------------ expert budget
+//
+// One workgroup of 1024 threads over the whole batch.
+//  1. Aggregate gate weight per distinct expert (float64; per-wave LDS copies).
+//  2-3. Rank the experts of the union by (aggregate desc, id asc); keep rank < B.
+//  4. Per token: compact kept slots to the front in their original order, write
+//     -1 / 0 into the tail, renormalise kept weights if norm_topk (not when none
+//     is left).
+//  5. Statistics {union before, union after, dropped slots, empty tokens}.
+// With B = 0 or union <= B only the statistics are written.
+__global__ void __launch_bounds__(1024) budget_kernel(
+    int32_t* __restrict__ ids, float* __restrict__ w, int T, int E, int K, int budget,
+    int norm_topk, int32_t* __restrict__ stats) {
+  constexpr int kWaves = 16;
+  __shared__ double agg[kWaves][kMaxExperts];  // 64 KiB
+  __shared__ int present[kMaxExperts];
+  __shared__ int keep[kMaxExperts];
+  __shared__ int s_union, s_dropped, s_empty;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  for (int i = tid; i < kWaves * kMaxExperts; i += 1024) (&agg[0][0])[i] = 0.0;
+  for (int e = tid; e < kMaxExperts; e += 1024) present[e] = 0;
+  if (tid == 0) { s_union = 0; s_dropped = 0; s_empty = 0; }
+  __syncthreads();
+  const int nslots = T * K;
+  for (int s = tid; s < nslots; s += 1024) {
+    const int e = ids[s];
+    if (e >= 0) {
+      atomicAdd(&agg[wave][e], static_cast<double>(w[s]));
+      present[e] = 1;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024) {
+    double a = 0.0;
+#pragma unroll
+    for (int q = 0; q < kWaves; ++q) a += agg[q][e];
+    agg[0][e] = a;
+    if (present[e]) atomicAdd(&s_union, 1);
+  }
+  __syncthreads();
+  const int nu = s_union;
+  const bool active = budget > 0 && nu > budget;
+  if (active) {
+    for (int e = tid; e < E; e += 1024) {
+      int k = 0;
+      if (present[e]) {
+        const double a = agg[0][e];
+        int rank = 0;
+        for (int o = 0; o < E; ++o)
+          rank += (present[o] && (agg[0][o] > a || (agg[0][o] == a && o < e))) ? 1 : 0;
+        k = rank < budget;
+      }
+      keep[e] = k;
+    }
+    __syncthreads();
+    for (int t = tid; t < T; t += 1024) {
+      int32_t* ir = ids + static_cast<size_t>(t) * K;
+      float* wr = w + static_cast<size_t>(t) * K;
+      int nk = 0, nd = 0;
+      float sum = 0.f;
+      for (int k = 0; k < K; ++k) {
+        const int e = ir[k];
+        if (e < 0) continue;
+        if (keep[e]) { sum += wr[k]; ++nk; } else { ++nd; }
+      }
+      if (nd) {
+        // Compact in place: position j <= k has already been read when it is written.
+        int j = 0;
+        for (int k = 0; k < K; ++k) {
+          const int e = ir[k];
+          if (e >= 0 && keep[e]) {
+            const float v = wr[k];
+            ir[j] = e;
+            wr[j] = norm_topk ? v / sum : v;
+            ++j;
+          }
+        }
+        for (; j < K; ++j) { ir[j] = -1; wr[j] = 0.f; }
+      }
+      if (nd) atomicAdd(&s_dropped, nd);
+      if (nk == 0) atomicAdd(&s_empty, 1);
+    }
+    __syncthreads();
+  }
+  if (tid == 0 && stats) {
+    stats[0] = nu;
+    stats[1] = active ? budget : nu;
+    stats[2] = s_dropped;
+    stats[3] = s_empty;
+  }
+}
+
+}  // namespace moe

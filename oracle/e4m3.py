@@ -20,9 +20,7 @@ E4M3_MAX = 448.0
 GROUP = 128
 
 
-def decode(codes) -> np.ndarray:
-    """uint8 codes -> float64 values (NaN for S.1111.111)."""
-    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+def _decode_bits(c: np.ndarray) -> np.ndarray:
     sign = np.where(c & 0x80, -1.0, 1.0)
     exp = (c >> 3) & 0xF
     man = c & 0x7
@@ -30,6 +28,15 @@ def decode(codes) -> np.ndarray:
     nrm = (1.0 + man / 8.0) * np.exp2(exp.astype(np.float64) - 7.0)
     val = sign * np.where(exp == 0, sub, nrm)
     return np.where((exp == 15) & (man == 7), np.nan, val)
+
+
+# The 256 code points decoded once from the bit fields above.
+_TABLE = _decode_bits(np.arange(256, dtype=np.int64))
+
+
+def decode(codes) -> np.ndarray:
+    """uint8 codes -> float64 values (NaN for S.1111.111)."""
+    return _TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
 def _round_half_even(a: np.ndarray) -> np.ndarray:

@@ -1,0 +1,183 @@
+"""Test-side harness: seeded inputs, conditioned by the oracle so that every
+routing decision has a margin, run through the HIP library and compared with the
+CPU oracle.
+
+TEST INFRASTRUCTURE (imports the oracle).  Used by tests/ and the smoke check.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+import torch
+
+import workloads as W
+from oracle import moe as O
+
+# Top-k margin: the sorted logits of every token differ by more than this between
+# neighbours 1..K+1, so the float32 GPU logits pick the same ids in the same order.
+TOPK_MARGIN = 1e-3
+# Budget margin: the B-th and (B+1)-th aggregate weights differ by more than this.
+BUDGET_MARGIN = 1e-4
+
+TOL = {"f32": 1e-5, "bf16": 2e-3, "fp8_e4m3_g128": 1e-2}   # relative L2 of y
+W_TOL = 1e-6                                                   # routing weights, absolute
+
+
+@dataclasses.dataclass
+class Case:
+    shape: W.LayerShape
+    T: int
+    seed: int
+    alpha: Optional[float]
+    inp: W.LayerInputs
+    weights: Dict[str, torch.Tensor]            # stacked routed weights (device)
+    shared: Optional[Dict[str, torch.Tensor]]   # shared expert weights (device)
+    redrawn_rows: int = 0
+    bias_attempts: int = 0
+
+    def expert_cpu(self, e: int) -> Dict[str, torch.Tensor]:
+        return {k: v[e].cpu() for k, v in self.weights.items()}
+
+    def shared_cpu(self):
+        return None if self.shared is None else {k: v.cpu() for k, v in self.shared.items()}
+
+
+def _topk_gaps_ok(z: np.ndarray, K: int) -> np.ndarray:
+    """Per token: the K+1 largest logits are separated by more than TOPK_MARGIN."""
+    E = z.shape[1]
+    top = -np.sort(-z, axis=1)[:, :min(K + 1, E)]
+    gaps = top[:, :-1] - top[:, 1:]
+    return (gaps > TOPK_MARGIN).all(axis=1) if gaps.shape[1] else np.ones(z.shape[0], bool)
+
+
+def condition_topk(shape: W.LayerShape, inp: W.LayerInputs, max_attempts: int = 200) -> int:
+    """Re-draw rows of x (seeded by token and attempt) until every token's top-k has margins."""
+    redrawn = 0
+    for attempt in range(1, max_attempts + 1):
+        z = O.router_logits(inp.x, inp.w_router, inp.logit_bias)
+        bad = np.nonzero(~_topk_gaps_ok(z, shape.num_experts_per_tok))[0]
+        if len(bad) == 0:
+            return redrawn
+        for t in bad:
+            inp.x[t] = W.token_row(shape, inp.seed, int(t), attempt)
+        redrawn += len(bad)
+    raise RuntimeError("could not condition the top-k margins")
+
+
+def _budget_gap(shape: W.LayerShape, inp: W.LayerInputs) -> float:
+    r = O.route(inp.x, inp.w_router, inp.w_shared_gate, inp.logit_bias, shape.num_experts_per_tok,
+                bool(shape.norm_topk_prob), 0)
+    ids, w = r["ids"], r["w"]
+    agg = sorted((float(w[ids == e].sum()) for e in set(ids.ravel().tolist())), reverse=True)
+    B = shape.expert_budget
+    if B <= 0 or len(agg) <= B:
+        return float("inf")
+    return agg[B - 1] - agg[B]
+
+
+def make_case(shape: W.LayerShape, T: int, seed: int, alpha: Optional[float] = None,
+              device: str = "cuda", condition: bool = True) -> Case:
+    inp = W.layer_inputs(shape, T, seed, alpha)
+    redrawn = attempts = 0
+    if condition and T > 0:
+        redrawn = condition_topk(shape, inp)
+        while shape.expert_budget > 0 and _budget_gap(shape, inp) <= BUDGET_MARGIN:
+            attempts += 1
+            if attempts > 50:
+                raise RuntimeError("could not condition the budget margin")
+            if alpha:   # re-permute the Zipf ranks
+                inp.logit_bias = W.zipf_rank_bias(shape, seed, T, alpha, attempts)
+            else:       # re-draw the first token
+                inp.x[0] = W.token_row(shape, seed, 0, 10_000 + attempts)
+            redrawn += condition_topk(shape, inp)
+    weights = W.stacked_expert_weights(shape, seed, device)
+    shared = W.shared_expert_weights(shape, seed, device)
+    return Case(shape, T, seed, alpha, inp, weights, shared, redrawn, attempts)
+
+
+def config(shape: W.LayerShape):
+    import mixture_experts_layer_05_amd as moe
+    return moe.MoEConfig(shape.hidden_size, shape.n_routed_experts, shape.moe_intermediate_size,
+                         shape.num_experts_per_tok, shape.shared_expert_intermediate_size,
+                         shape.weight_dtype, shape.act_dtype, shape.norm_topk_prob, shape.expert_budget)
+
+
+def run_gpu(case: Case, layer=None) -> Dict[str, np.ndarray]:
+    """route -> dispatch -> forward through the C ABI; returns host copies of every output."""
+    import mixture_experts_layer_05_amd as moe
+    shape, T = case.shape, case.T
+    if layer is None:
+        layer = moe.MoELayer(config(shape), case.weights, case.inp.w_router.cuda(),
+                             None if case.inp.w_shared_gate is None else case.inp.w_shared_gate.cuda(),
+                             case.shared, max_tokens=max(T, 1))
+    x = case.inp.x.cuda()
+    bias = None if case.inp.logit_bias is None else case.inp.logit_bias.cuda()
+    layer.route_stats.fill_(-7)
+    y = layer(x, bias)
+    torch.cuda.synchronize()
+    v = layer.views(T)
+    nkept = int(layer.offsets[-1].item())
+    return {
+        "ids": v["topk_ids"].cpu().numpy(), "w": v["topk_weights"].cpu().numpy(),
+        "shared_gate": v["shared_gate"].cpu().numpy(), "stats": layer.route_stats.cpu().numpy(),
+        "counts": layer.counts.cpu().numpy(), "offsets": layer.offsets.cpu().numpy(),
+        "perm": v["perm"][:nkept].cpu().numpy(), "y": y.cpu().numpy().astype(np.float64),
+    }
+
+
+def run_oracle(case: Case, tokens: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+    shape = case.shape
+    return O.moe_layer(case.inp.x, case.inp.w_router, case.inp.w_shared_gate, case.inp.logit_bias,
+                       shape.num_experts_per_tok, shape.n_routed_experts, case.expert_cpu,
+                       case.shared_cpu(), shape.weight_dtype, bool(shape.norm_topk_prob),
+                       shape.expert_budget, tokens)
+
+
+def rel_l2(a: np.ndarray, b: np.ndarray) -> float:
+    den = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / den) if den > 0 else float(np.linalg.norm(a))
+
+
+def compare(case: Case, gpu: Dict, ora: Dict, tokens: Optional[Sequence[int]] = None) -> Dict[str, float]:
+    """Assert parity; return the measured errors."""
+    shape = case.shape
+    K = shape.num_experts_per_tok
+    assert np.array_equal(gpu["ids"], ora["ids"]), "expert ids differ"
+    werr = float(np.abs(gpu["w"] - ora["w"]).max()) if gpu["w"].size else 0.0
+    assert werr <= W_TOL, f"routing weights differ by {werr}"
+    if shape.expert_budget > 0:
+        assert np.array_equal(gpu["stats"], ora["stats"]), (gpu["stats"], ora["stats"])
+    else:
+        nu = len(set(ora["ids"].ravel().tolist()) - {-1})
+        assert gpu["stats"].tolist() == [nu, nu, 0, 0]
+    assert np.array_equal(gpu["counts"], ora["counts"]), "expert counts differ"
+    assert np.array_equal(gpu["offsets"], ora["offsets"]), "expert offsets differ"
+    assert np.array_equal(gpu["perm"], ora["perm"]), "dispatch permutation differs"
+    # Dispatch as a pure function of the GPU's own ids, too.
+    c2, o2, p2 = O.dispatch(gpu["ids"], shape.n_routed_experts)
+    assert np.array_equal(gpu["perm"], p2) and np.array_equal(gpu["counts"], c2)
+    sg_err = 0.0
+    if shape.shared_expert_intermediate_size > 0:
+        sg_err = float(np.abs(gpu["shared_gate"] - ora["shared_gate"]).max())
+        assert sg_err <= 1e-5, f"shared gate differs by {sg_err}"
+    y_gpu = gpu["y"] if tokens is None else gpu["y"][np.asarray(tokens)]
+    err = rel_l2(y_gpu, ora["y"])
+    tol = TOL[shape.weight_dtype]
+    assert err <= tol, f"y relative L2 {err:.3e} > {tol:.0e}"
+    # Tokens with no kept expert and no shared expert must be exactly zero.
+    if shape.shared_expert_intermediate_size == 0:
+        toks = np.arange(case.T) if tokens is None else np.asarray(tokens)
+        empty = (ora["ids"][toks] < 0).all(axis=1)
+        assert (y_gpu[empty] == 0).all()
+    return {"y_rel_l2": err, "w_max_abs": werr, "shared_gate_max_abs": sg_err}
+
+
+def sample_tokens(T: int, n: int, seed: int = 0) -> np.ndarray:
+    """n tokens spread over [0, T): first, last and a seeded sample in between."""
+    if T <= n:
+        return np.arange(T)
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(1, T - 1), size=n - 2, replace=False)
+    return np.sort(np.concatenate([[0, T - 1], mid]))

@@ -1,0 +1,145 @@
+"""The C-ABI library: it loads, exports every declared entry point, and rejects
+invalid arguments with the documented status before launching anything.
+These calls never reach a kernel, so they run without a GPU."""
+import ctypes
+import re
+
+import pytest
+
+import mixture_experts_layer_05_amd as moe
+
+OK, NULL_PTR, BAD_SHAPE, BAD_DTYPE, UNSUPPORTED, WS_SMALL = 0, -1, -2, -3, -4, -5
+
+
+def _declared_functions():
+    text = open(moe.HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding_entry_points():
+    assert set(_declared_functions()) == set(moe.ENTRY_POINTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = moe.lib()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.moe_version() == 0x000100
+    for st in (0, -1, -2, -3, -4, -5, -6, 99):
+        assert moe.status_string(st)
+
+
+def _cfg(**kw):
+    base = dict(hidden_size=5120, n_routed_experts=16, moe_intermediate_size=1024, num_experts_per_tok=2,
+                shared_expert_intermediate_size=2048, weight_dtype="bf16", act_dtype="bf16",
+                norm_topk_prob=1, expert_budget=0)
+    base.update(kw)
+    return moe.MoEConfig(**base)
+
+
+def _ws(cfg, T=4):
+    n = ctypes.c_size_t(0)
+    st = moe.lib().moe_workspace_size(ctypes.byref(cfg.c()), T, ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, OK),
+    (dict(num_experts_per_tok=17, n_routed_experts=32), UNSUPPORTED),
+    (dict(num_experts_per_tok=3, n_routed_experts=2), BAD_SHAPE),
+    (dict(n_routed_experts=513), UNSUPPORTED),
+    (dict(n_routed_experts=0), BAD_SHAPE),
+    (dict(hidden_size=0), BAD_SHAPE),
+    (dict(hidden_size=5000), UNSUPPORTED),
+    (dict(weight_dtype="fp8_e4m3_g128", moe_intermediate_size=1000), UNSUPPORTED),
+    (dict(shared_expert_intermediate_size=100), UNSUPPORTED),
+    (dict(weight_dtype="f32"), BAD_DTYPE),
+    (dict(act_dtype="f32", weight_dtype="fp8_e4m3_g128"), BAD_DTYPE),
+    (dict(act_dtype="fp8_e4m3_g128", weight_dtype="fp8_e4m3_g128"), BAD_DTYPE),
+    (dict(expert_budget=-1), BAD_SHAPE),
+    (dict(norm_topk_prob=2), BAD_SHAPE),
+    (dict(shared_expert_intermediate_size=-128), BAD_SHAPE),
+    (dict(weight_dtype="f32", act_dtype="f32", hidden_size=100, moe_intermediate_size=30), OK),
+])
+def test_workspace_size_validation(kw, status):
+    assert _ws(_cfg(**kw))[0] == status
+
+
+def test_workspace_size_null_arguments_and_tokens():
+    lib = moe.lib()
+    n = ctypes.c_size_t(0)
+    assert lib.moe_workspace_size(None, 4, ctypes.byref(n)) == NULL_PTR
+    assert lib.moe_workspace_size(ctypes.byref(_cfg().c()), 4, None) == NULL_PTR
+    assert lib.moe_workspace_size(ctypes.byref(_cfg().c()), -1, ctypes.byref(n)) == BAD_SHAPE
+    a, b = _ws(_cfg(), 7)[1], _ws(_cfg(), 224)[1]
+    assert 0 < a < b
+
+
+FAKE = 0x1000  # never dereferenced: every call below returns before any launch
+
+
+def _route(cfg, T=4, ws_bytes=None, **ptrs):
+    p = dict(x=FAKE, w_router=FAKE, w_shared_gate=FAKE, logit_bias=None, ids=FAKE, w=FAKE, sg=FAKE,
+             stats=None, ws=FAKE)
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = _ws(cfg, max(T, 0))[1]
+    return moe.lib().moe_route(ctypes.byref(cfg.c()), T, p["x"], p["w_router"], p["w_shared_gate"],
+                               p["logit_bias"], p["ids"], p["w"], p["sg"], p["stats"], p["ws"], ws_bytes,
+                               None)
+
+
+def test_route_validation():
+    cfg = _cfg()
+    assert _route(cfg, x=None) == NULL_PTR
+    assert _route(cfg, w_router=None) == NULL_PTR
+    assert _route(cfg, ids=None) == NULL_PTR
+    assert _route(cfg, w_shared_gate=None) == NULL_PTR     # S > 0 needs the gate vector
+    assert _route(cfg, sg=None) == NULL_PTR
+    assert _route(cfg, ws=None) == NULL_PTR
+    assert _route(cfg, T=4, ws_bytes=16) == WS_SMALL
+    assert _route(cfg, T=-2) == BAD_SHAPE
+    assert _route(cfg, T=0) == OK                           # nothing to do, nothing launched
+    assert _route(_cfg(shared_expert_intermediate_size=0), T=0, w_shared_gate=None, sg=None) == OK
+
+
+def _forward(cfg, T=4, name="moe_forward", y=FAKE, **ptrs):
+    w = moe._Weights(FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, FAKE, None, None, None)
+    for k, v in ptrs.items():
+        if hasattr(w, k):
+            setattr(w, k, v)
+    g = lambda k: ptrs.get(k, FAKE)  # noqa: E731
+    return getattr(moe.lib(), name)(ctypes.byref(cfg.c()), T, g("x"), g("topk_w"), g("shared_gate"),
+                                    g("counts"), g("offsets"), g("perm"), ctypes.byref(w), y, g("ws"),
+                                    _ws(cfg, max(T, 0))[1], None)
+
+
+def test_forward_validation():
+    cfg = _cfg()
+    for name in ("moe_forward", "moe_forward_gate_up", "moe_forward_down"):
+        assert _forward(cfg, name=name, x=None) == NULL_PTR
+        assert _forward(cfg, name=name, counts=None) == NULL_PTR
+        assert _forward(cfg, name=name, ws_down=None) == NULL_PTR
+        assert _forward(cfg, name=name, shared_gate=None) == NULL_PTR
+        assert _forward(cfg, name=name, y=FAKE + 4) == UNSUPPORTED       # y must be 16-byte aligned
+        assert _forward(cfg, name=name, T=0) == OK
+    fp8 = _cfg(weight_dtype="fp8_e4m3_g128")
+    assert _forward(fp8) == NULL_PTR                                      # scales missing
+    assert _forward(_cfg(shared_expert_intermediate_size=0), T=0, ws_gate=None, ws_up=None,
+                    ws_down=None, shared_gate=None) == OK
+
+
+def test_dispatch_validation():
+    lib = moe.lib()
+    cfg = _cfg()
+    ws = _ws(cfg)[1]
+    assert lib.moe_dispatch(ctypes.byref(cfg.c()), 4, None, FAKE, FAKE, FAKE, FAKE, ws, None) == NULL_PTR
+    assert lib.moe_dispatch(ctypes.byref(cfg.c()), 4, FAKE, FAKE, FAKE, FAKE, FAKE, 8, None) == WS_SMALL
+    assert lib.moe_dispatch(ctypes.byref(cfg.c()), -1, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == BAD_SHAPE
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(moe, "_lib", None)
+    with pytest.raises(ImportError):
+        moe.lib()

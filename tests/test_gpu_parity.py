@@ -1,0 +1,147 @@
+"""GPU parity: the HIP library through its C ABI vs the CPU oracle.
+
+Ids, counts, offsets, the permutation and the budget statistics must match
+bit-exactly; routing weights within 1e-6; y within the relative-L2 bar of its
+weight dtype (fp32 1e-5, bf16 2e-3, fp8 1e-2).  Sizes the oracle finishes in
+seconds are compared on every token; the full-size workloads on sampled tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from tests import harness as Hn
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(shape, T, seed, alpha=None, tokens=None, condition=True, mutate=None):
+    print(f"\n[case] {shape.name} T={T} seed={seed} alpha={alpha}", flush=True)
+    case = Hn.make_case(shape, T, seed, alpha, condition=condition)
+    if mutate:
+        mutate(case)
+    gpu = Hn.run_gpu(case)
+    ora = Hn.run_oracle(case, tokens)
+    errs = Hn.compare(case, gpu, ora, tokens)
+    print(f"[case] ok {errs} redrawn_rows={case.redrawn_rows}", flush=True)
+    return case, gpu, ora, errs
+
+
+def test_tiny_fp32_layer():
+    _run(W.TINY, 64, W.base_seed(0, 64))
+
+
+@pytest.mark.parametrize("T", [7, 56, 224])
+def test_drafter_layer(T):
+    _run(W.DRAFTER, T, W.base_seed(1, T))
+
+
+@pytest.mark.parametrize("T", [7, 56])
+def test_narrow_layer(T):
+    _run(W.NARROW, T, W.base_seed(2, T))
+
+
+def test_narrow_layer_224_sampled():
+    _run(W.NARROW, 224, W.base_seed(2, 224), tokens=Hn.sample_tokens(224, 48))
+
+
+@pytest.mark.parametrize("alpha", [0.0, 1.5])
+def test_large_layer_512(alpha):
+    _run(W.LARGE, 512, W.base_seed(3, 512), alpha, tokens=Hn.sample_tokens(512, 24))
+
+
+def test_large_layer_8192_skewed_sampled():
+    _run(W.LARGE, 8192, W.base_seed(3, 8192), 1.5, tokens=Hn.sample_tokens(8192, 16))
+
+
+def test_fp8_budget_layer_8192_sampled():
+    case, gpu, ora, errs = _run(W.LARGE_FP8, 8192, W.base_seed(4, 8192), 1.5,
+                                tokens=Hn.sample_tokens(8192, 16))
+    assert gpu["stats"][1] == 64 and gpu["stats"][0] > 64
+
+
+def test_fp8_small_budget_drops_experts():
+    shape = W.LARGE_FP8.with_(expert_budget=32)
+    case, gpu, ora, errs = _run(shape, 512, W.base_seed(4, 512), 1.5, tokens=Hn.sample_tokens(512, 24))
+    assert gpu["stats"][0] > 32 and gpu["stats"][1] == 32 and gpu["stats"][2] > 0
+    # Same quantisation decisions on both sides: far below the fp8 bar.
+    assert errs["y_rel_l2"] < 1e-3
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+EDGE = W.LayerShape("edge_k_eq_e", 256, 4, 256, 4, 128, W.DT_BF16, W.DT_BF16)
+
+
+def test_k_equals_e_with_ragged_tokens():
+    _run(EDGE, 13, 5)
+
+
+def test_single_expert_top1():
+    _run(W.LayerShape("one_expert", 128, 1, 128, 1, 0, W.DT_BF16, W.DT_BF16), 5, 6)
+
+
+def test_single_token():
+    _run(W.DRAFTER, 1, 7)
+
+
+def test_budget_of_one_empties_tokens():
+    shape = W.LayerShape("budget1", 256, 8, 128, 2, 0, W.DT_BF16, W.DT_BF16, expert_budget=1)
+    case, gpu, ora, _ = _run(shape, 40, 8)
+    assert gpu["stats"][1] == 1 and gpu["stats"][3] > 0   # some tokens lose every expert
+
+
+def test_budget_at_union_is_a_noop():
+    shape = W.LayerShape("budget16", 256, 16, 128, 2, 0, W.DT_BF16, W.DT_BF16, expert_budget=16)
+    case, gpu, ora, _ = _run(shape, 64, 9)
+    assert gpu["stats"].tolist()[1:] == [gpu["stats"][0], 0, 0]
+
+
+def test_plain_softmax_without_renormalisation():
+    shape = W.LayerShape("no_norm", 256, 8, 128, 3, 128, W.DT_BF16, W.DT_BF16, norm_topk_prob=0)
+    case, gpu, ora, _ = _run(shape, 33, 10)
+    assert (gpu["w"].sum(axis=1) < 1.0).all()
+
+
+def test_fp8_zero_activation_row():
+    shape = W.LayerShape("fp8_zero_row", 256, 8, 256, 2, 128, W.DT_FP8, W.DT_BF16)
+
+    def zero_row(case):
+        case.inp.x[3] = 0   # logits exactly 0: ids 0..K-1 by the tie rule; fp8 group amax = 0
+    case, gpu, ora, _ = _run(shape, 20, 11, mutate=zero_row)
+    assert gpu["ids"][3].tolist() == [0, 1]
+
+
+def test_zero_tokens_is_a_noop():
+    import mixture_experts_layer_05_amd as moe
+    case = Hn.make_case(W.DRAFTER.with_(n_routed_experts=16), 0, 1)
+    layer = moe.MoELayer(Hn.config(case.shape), case.weights, case.inp.w_router.cuda(),
+                         case.inp.w_shared_gate.cuda(), case.shared, max_tokens=4)
+    x = torch.empty(0, case.shape.hidden_size, dtype=torch.bfloat16, device="cuda")
+    y = layer(x)
+    torch.cuda.synchronize()
+    assert y.shape == (0, case.shape.hidden_size)
+    assert int(layer.offsets[-1].item()) == 0 and int(layer.counts.sum().item()) == 0
+
+
+def test_routing_is_deterministic():
+    case = Hn.make_case(W.NARROW, 56, 12)
+    a = Hn.run_gpu(case)
+    b = Hn.run_gpu(case)
+    for k in ("ids", "w", "counts", "offsets", "perm", "stats"):
+        assert np.array_equal(a[k], b[k]), k
+    assert Hn.rel_l2(a["y"], b["y"]) < 1e-6
+
+
+def test_halves_equal_forward():
+    import mixture_experts_layer_05_amd as moe
+    case = Hn.make_case(W.DRAFTER, 56, 13)
+    layer = moe.MoELayer(Hn.config(case.shape), case.weights, case.inp.w_router.cuda(),
+                         case.inp.w_shared_gate.cuda(), case.shared, max_tokens=56)
+    x = case.inp.x.cuda()
+    bias = case.inp.logit_bias.cuda()
+    y1 = layer(x, bias).clone()
+    layer.forward(x, half="gate_up")
+    layer.forward(x, half="down")
+    torch.cuda.synchronize()
+    assert Hn.rel_l2(layer.views(56)["y"].cpu().numpy(), y1.cpu().numpy()) < 1e-6

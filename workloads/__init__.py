@@ -90,17 +90,17 @@ def base_seed(shape_index: int, T: int) -> int:
     return 1000 * shape_index + T
 
 
-def _gen(*key: int) -> torch.Generator:
-    # Fold an integer tuple into one 63-bit seed (splitmix-style mixing of the parts).
+def _gen(*key: int, device="cpu") -> torch.Generator:
+    # Fold an integer tuple into one 63-bit seed (hash-combine of the parts).
     h = 0x9E3779B97F4A7C15
     for k in key:
         h ^= (int(k) + 0x9E3779B97F4A7C15 + ((h << 6) & 0xFFFFFFFFFFFFFFFF) + (h >> 2)) & 0xFFFFFFFFFFFFFFFF
         h &= 0xFFFFFFFFFFFFFFFF
-    return torch.Generator().manual_seed(h & 0x7FFFFFFFFFFFFFFF)
+    return torch.Generator(device=device).manual_seed(h & 0x7FFFFFFFFFFFFFFF)
 
 
 def _normal(shape, std: float, g: torch.Generator) -> torch.Tensor:
-    return torch.randn(*shape, generator=g, dtype=torch.float32) * std
+    return torch.randn(*shape, generator=g, dtype=torch.float32, device=g.device) * std
 
 
 def act_torch_dtype(shape: LayerShape) -> torch.dtype:
@@ -182,30 +182,45 @@ def _quantise_rows_g128(w: torch.Tensor):
     return q.reshape(n, kc).view(torch.uint8), s.to(torch.float32).contiguous()
 
 
-def expert_weights(shape: LayerShape, seed: int, e: int) -> Dict[str, torch.Tensor]:
+def expert_weights(shape: LayerShape, seed: int, e: int, device="cpu") -> Dict[str, torch.Tensor]:
     """Weights of routed expert e.
 
     gate, up: [I, H]; down: [H, I] (contraction dim contiguous).  For fp8 also
-    the group-128 scales gate_s/up_s [I, H/128], down_s [H, I/128].
+    the group-128 scales gate_s/up_s [I, H/128], down_s [H, I/128].  The numbers
+    depend on the device's generator (CPU and GPU draws differ), never on anything else.
     """
     H, I = shape.hidden_size, shape.moe_intermediate_size
-    g = _gen(seed, _SUB_EXPERT, e)
+    g = _gen(seed, _SUB_EXPERT, e, device=device)
     wg = _normal((I, H), shape.weight_std, g)
     wu = _normal((I, H), shape.weight_std, g)
     wd = _normal((H, I), shape.weight_std, g)
     return _pack(shape, wg, wu, wd)
 
 
-def shared_expert_weights(shape: LayerShape, seed: int) -> Optional[Dict[str, torch.Tensor]]:
+def shared_expert_weights(shape: LayerShape, seed: int, device="cpu") -> Optional[Dict[str, torch.Tensor]]:
     """Shared expert: gate, up [S, H]; down [H, S] (+ scales for fp8)."""
     S, H = shape.shared_expert_intermediate_size, shape.hidden_size
     if S == 0:
         return None
-    g = _gen(seed, _SUB_SHARED)
+    g = _gen(seed, _SUB_SHARED, device=device)
     wg = _normal((S, H), shape.weight_std, g)
     wu = _normal((S, H), shape.weight_std, g)
     wd = _normal((H, S), shape.weight_std, g)
     return _pack(shape, wg, wu, wd)
+
+
+def stacked_expert_weights(shape: LayerShape, seed: int, device="cpu") -> Dict[str, torch.Tensor]:
+    """Routed weights stacked over experts ([E, I, H], [E, I, H], [E, H, I] (+ scales)),
+    filled expert by expert so that only one expert's float32 draw is live at a time."""
+    out = None
+    for e in range(shape.n_routed_experts):
+        w = expert_weights(shape, seed, e, device)
+        if out is None:
+            out = {k: torch.empty((shape.n_routed_experts, *v.shape), dtype=v.dtype, device=v.device)
+                   for k, v in w.items()}
+        for k, v in w.items():
+            out[k][e].copy_(v)
+    return out
 
 
 def _pack(shape: LayerShape, wg, wu, wd) -> Dict[str, torch.Tensor]:
@@ -246,7 +261,3 @@ def layer_inputs(shape: LayerShape, T: int, seed: int, alpha: Optional[float] = 
                        shared_gate_weight(shape, seed), bias, alpha)
 
 
-def all_expert_weights(shape: LayerShape, seed: int) -> Dict[str, torch.Tensor]:
-    """Stacked routed weights [E, ...] on the CPU (only for shapes that fit host memory)."""
-    per = [expert_weights(shape, seed, e) for e in range(shape.n_routed_experts)]
-    return {k: torch.stack([p[k] for p in per]).contiguous() for k in per[0]}

@@ -1,0 +1,221 @@
+"""Benchmark of the routed MoE FFN forward on one MI355X.
+
+One step = route -> dispatch -> forward (every kernel of the layer) over one
+batch of synthetic tokens, inputs already resident in HBM.  The default workload
+is the 16 x 1024 top-2 drafter layer with its 2048-wide sigmoid-gated shared
+expert at 32 concurrent 7-token blocks (T = 224), the decode-sized point of
+[SpecForge PR #943, "End-to-end serving speed"].  Several copies of the layer
+weights are cycled (one per step, like the layers of a model) so that no step
+finds its weights in the 256 MB last-level cache.
+
+Prints ONE JSON line (rank 0): tokens/s of the whole layer plus TFLOP/s, weight
+GB/s, the roofline of the dominant kernel (timed with HIP events on the stream
+the kernel runs on) and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8_e4m3_g128": 5000.0, "f32": 157.3}
+
+METRIC = "MoE layer tokens/s + TFLOP/s (prefill M) and weight HBM GB/s (decode M), 1 GPU"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="drafter",
+                   choices=["drafter", "narrow", "large", "large_fp8", "tiny"])
+    p.add_argument("--tokens", type=int, default=None, help="T (default: the workload's bench size)")
+    p.add_argument("--alpha", type=float, default=None, help="Zipf router skew for the large layers")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-tokens", type=int, default=None)
+    return p.parse_args()
+
+
+def workload(args):
+    import workloads as W
+    table = {
+        "drafter": (W.DRAFTER, 1, 224, None),
+        "narrow": (W.NARROW, 2, 224, None),
+        "large": (W.LARGE, 3, 8192, 1.5),
+        "large_fp8": (W.LARGE_FP8, 4, 8192, 1.5),
+        "tiny": (W.TINY, 0, 64, None),
+    }
+    shape, idx, T, alpha = table[args.workload]
+    if args.tokens is not None:
+        T = args.tokens
+    if args.alpha is not None:
+        alpha = args.alpha
+    return shape, idx, T, alpha
+
+
+def weight_bytes_per_elem(shape) -> float:
+    return {"f32": 4.0, "bf16": 2.0, "fp8_e4m3_g128": 1.0 + 4.0 / 128}[shape.weight_dtype]
+
+
+def accounting(shape, T, counts):
+    """Algorithmic FLOPs and bytes of one step (from the realised routing)."""
+    H, I, S, E = shape.hidden_size, shape.moe_intermediate_size, shape.shared_expert_intermediate_size, \
+        shape.n_routed_experts
+    slots = int(counts.sum())
+    touched = int((counts > 0).sum())
+    bw = weight_bytes_per_elem(shape)
+    ba = 4.0 if shape.act_dtype == "f32" else 2.0
+    flops = 2.0 * T * H * (E + (1 if S else 0)) + 6.0 * H * I * slots + 6.0 * T * H * S
+    gate_up_w = touched * 2.0 * I * H * bw + 2.0 * S * H * bw
+    down_w = touched * 1.0 * H * I * bw + 1.0 * H * S * bw
+    router_w = (E + (1 if S else 0)) * H * ba
+    weights = gate_up_w + down_w + router_w
+    x_bytes = T * H * ba
+    y_bytes = T * H * 4.0
+    hbytes = 2.0 if shape.weight_dtype == "bf16" else 4.0
+    h_elems = slots * I + T * S
+    # Dominant kernel (gate/up + SwiGLU): its weights, x in, h out.
+    gate_up_bytes = gate_up_w + x_bytes + h_elems * hbytes
+    return dict(flops=flops, weight_bytes=weights, total_bytes=weights + x_bytes + y_bytes,
+                gate_up_bytes=gate_up_bytes, touched=touched, slots=slots,
+                gate_up_flops=4.0 * H * I * slots + 4.0 * T * H * S)
+
+
+def cpu_baseline(shape, case_inputs, expert_cpu, shared_cpu, T, sample_tokens):
+    """The CPU oracle as it stands, on a bounded sample: routing of every token plus
+    the expert math of `sample_tokens` tokens; reported per token of the sample."""
+    import numpy as np
+    import threadpoolctl
+    from oracle import moe as O
+    toks = np.arange(min(sample_tokens, T))
+    t0 = time.perf_counter()
+    O.moe_layer(case_inputs.x, case_inputs.w_router, case_inputs.w_shared_gate, case_inputs.logit_bias,
+                shape.num_experts_per_tok, shape.n_routed_experts, expert_cpu, shared_cpu,
+                shape.weight_dtype, bool(shape.norm_topk_prob), shape.expert_budget, toks)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    return {"value": len(toks) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(toks)} of {T} tokens: routing of all {T} tokens + expert math of the "
+                      f"first {len(toks)}, float64 numpy on the host, {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is not sharded "
+              f"across GPUs in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import workloads as W
+    import mixture_experts_layer_05_amd as moe
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    moe.lib()   # fail loudly if the HIP library is missing
+
+    shape, idx, T, alpha = workload(args)
+    seed = W.base_seed(idx, T)
+    cfg = moe.MoEConfig(shape.hidden_size, shape.n_routed_experts, shape.moe_intermediate_size,
+                        shape.num_experts_per_tok, shape.shared_expert_intermediate_size,
+                        shape.weight_dtype, shape.act_dtype, shape.norm_topk_prob, shape.expert_budget)
+
+    # Weight copies: enough that consecutive steps never share cached weights.
+    one = (shape.n_routed_experts * 3 * shape.hidden_size * shape.moe_intermediate_size
+           + 3 * shape.hidden_size * shape.shared_expert_intermediate_size) * weight_bytes_per_elem(shape)
+    n_copies = int(max(1, min(8, np.ceil(2.0e9 / one))))
+    inp = W.layer_inputs(shape, T, seed, alpha)
+    layers = []
+    for c in range(n_copies):
+        wts = W.stacked_expert_weights(shape, seed + 7919 * c, "cuda")
+        shw = W.shared_expert_weights(shape, seed + 7919 * c, "cuda")
+        wr = W.router_weight(shape, seed + 7919 * c).to(dev) if c else inp.w_router.to(dev)
+        wg = inp.w_shared_gate.to(dev) if inp.w_shared_gate is not None else None
+        layers.append(moe.MoELayer(cfg, wts, wr, wg, shw, max_tokens=T))
+    x = inp.x.to(dev)
+    bias = inp.logit_bias.to(dev) if inp.logit_bias is not None else None
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        L = layers[i % n_copies]
+        if ev is not None:
+            ev[0].record(stream)
+        L.route(x, bias)
+        L.dispatch(T)
+        if ev is not None:
+            ev[1].record(stream)
+        L.forward(x, half="gate_up")
+        if ev is not None:
+            ev[2].record(stream)
+        L.forward(x, half="down")
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    gate_up_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    down_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    route_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+
+    acc = [accounting(shape, T, L.counts.cpu().numpy()) for L in layers]
+    a = {k: float(np.mean([d[k] for d in acc])) for k in acc[0]}
+    tokens_per_s = T / (ms_per_step * 1e-3)
+    achieved = a["gate_up_bytes"] / (gate_up_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": shape.weight_dtype,
+        "data": "synthetic (seeded; random-init weights)",
+        "config": {"workload": f"{shape.name} T={T}" + (f" alpha={alpha}" if alpha is not None else ""),
+                   "tokens": T, "hidden": shape.hidden_size, "experts": shape.n_routed_experts,
+                   "intermediate": shape.moe_intermediate_size, "topk": shape.num_experts_per_tok,
+                   "shared": shape.shared_expert_intermediate_size, "budget": shape.expert_budget,
+                   "weight_copies": n_copies},
+        "tflops": round(a["flops"] / (ms_per_step * 1e-3) / 1e12, 3),
+        "weight_gbps": round(a["weight_bytes"] / (ms_per_step * 1e-3) / 1e9, 1),
+        "stage_ms": {"route_dispatch": round(route_ms, 5), "gate_up": round(gate_up_ms, 5),
+                     "down": round(down_ms, 5)},
+        "experts_touched": a["touched"],
+        "roofline": {"bound": "hbm", "kernel": "gate_up_mfma_kernel", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None},
+    }
+    if shape.weight_dtype != "f32" and a["gate_up_flops"] / (gate_up_ms * 1e-3) / 1e12 > 0:
+        line["gate_up_tflops"] = round(a["gate_up_flops"] / (gate_up_ms * 1e-3) / 1e12, 2)
+    if not args.no_cpu_baseline:
+        L0 = layers[0]
+        expert_cpu = lambda e: {k: v[e].cpu() for k, v in L0.weights_dict.items()}  # noqa: E731
+        shared_cpu = None if L0.shared_dict is None else {k: v.cpu() for k, v in L0.shared_dict.items()}
+        sample = args.cpu_sample_tokens or min(T, 224 if shape.hidden_size <= 5120 else 16)
+        line["cpu_baseline"] = cpu_baseline(shape, inp, expert_cpu, shared_cpu, T, sample)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -28,7 +28,9 @@
  *     been enqueued and no output has been touched.  No exception or abort
  *     crosses this boundary.  MOE_ERR_LAUNCH_FAILED reports a HIP launch error
  *     (earlier launches of the same call may already be enqueued).
- *   - T = 0 is valid and enqueues nothing.
+ *   - T = 0 is valid: moe_route and moe_forward* then return MOE_OK without
+ *     reading any pointer but cfg and enqueue nothing; moe_dispatch writes zero
+ *     counts and offsets (topk_ids and perm may be NULL).
  *   - Supported dtype combinations (weight_dtype / act_dtype):
  *       F32 / F32, BF16 / BF16, FP8_E4M3_G128 / BF16.
  *     With BF16 or FP8 weights, hidden_size, moe_intermediate_size and

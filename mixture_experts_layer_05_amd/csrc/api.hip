@@ -91,12 +91,14 @@ T* at(void* base, size_t off) {
 
 int launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH_FAILED; }
 
+// Returns MOE_OK for T = 0 without looking at any pointer (nothing is read or written).
 int check_forward(const moe_config* cfg, int32_t T, const void* x, const float* topk_w,
                   const float* shared_gate, const int32_t* counts, const int32_t* offsets,
                   const int32_t* perm, const moe_expert_weights* w, float* y) {
   int st = check_config(cfg);
   if (st) return st;
   if ((st = check_tokens(cfg, T))) return st;
+  if (T == 0) return MOE_OK;
   if (!x || !topk_w || !counts || !offsets || !perm || !w || !y) return MOE_ERR_NULL_PTR;
   if (!w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_NULL_PTR;
   const bool fp8 = cfg->weight_dtype == MOE_DTYPE_FP8_E4M3_G128;
@@ -177,11 +179,11 @@ int moe_route(const moe_config* cfg, int32_t T, const void* x, const void* w_rou
   if (st) return st;
   if ((st = check_tokens(cfg, T))) return st;
   const bool has_shared = cfg->shared_expert_intermediate_size > 0;
+  if (T == 0) return MOE_OK;  // nothing is read or written
   if (!x || !w_router || !topk_ids || !topk_w) return MOE_ERR_NULL_PTR;
   if (has_shared && (!w_shared_gate || !shared_gate)) return MOE_ERR_NULL_PTR;
   Layout L;
   if ((st = check_workspace(*cfg, T, ws, ws_bytes, &L))) return st;
-  if (T == 0) return MOE_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int E = cfg->n_routed_experts, H = cfg->hidden_size, K = cfg->num_experts_per_tok;
   const int ncols = E + (has_shared ? 1 : 0);
@@ -215,7 +217,8 @@ int moe_dispatch(const moe_config* cfg, int32_t T, const int32_t* topk_ids, int3
   int st = check_config(cfg);
   if (st) return st;
   if ((st = check_tokens(cfg, T))) return st;
-  if (!topk_ids || !counts || !offsets || !perm) return MOE_ERR_NULL_PTR;
+  if (!counts || !offsets) return MOE_ERR_NULL_PTR;
+  if (T > 0 && (!topk_ids || !perm)) return MOE_ERR_NULL_PTR;
   Layout L;
   if ((st = check_workspace(*cfg, T, ws, ws_bytes, &L))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -229,10 +232,9 @@ int moe_forward_gate_up(const moe_config* cfg, int32_t T, const void* x, const f
                         const int32_t* perm, const moe_expert_weights* w, float* y, void* ws,
                         size_t ws_bytes, void* stream) {
   int st = check_forward(cfg, T, x, topk_w, shared_gate, counts, offsets, perm, w, y);
-  if (st) return st;
+  if (st || T == 0) return st;
   Layout L;
   if ((st = check_workspace(*cfg, T, ws, ws_bytes, &L))) return st;
-  if (T == 0) return MOE_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const ExpertArgs a = expert_args(*cfg, T, x, topk_w, shared_gate, counts, offsets, perm, *w, y, ws, L);
   if (cfg->weight_dtype == MOE_DTYPE_FP8_E4M3_G128) {
@@ -250,10 +252,9 @@ int moe_forward_down(const moe_config* cfg, int32_t T, const void* x, const floa
                      const int32_t* perm, const moe_expert_weights* w, float* y, void* ws,
                      size_t ws_bytes, void* stream) {
   int st = check_forward(cfg, T, x, topk_w, shared_gate, counts, offsets, perm, w, y);
-  if (st) return st;
+  if (st || T == 0) return st;
   Layout L;
   if ((st = check_workspace(*cfg, T, ws, ws_bytes, &L))) return st;
-  if (T == 0) return MOE_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const ExpertArgs a = expert_args(*cfg, T, x, topk_w, shared_gate, counts, offsets, perm, *w, y, ws, L);
   return launched(launch_down(a, cfg->weight_dtype, s));

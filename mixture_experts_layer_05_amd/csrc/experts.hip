@@ -26,107 +26,35 @@
 #include <algorithm>
 
 #include "kernels.h"
+#include "schedule.h"
 
 namespace moe {
 
 namespace {
 
-constexpr int kDtypeF32 = 0, kDtypeBf16 = 1, kDtypeFp8 = 2;
-
-// ---------------------------------------------------------------- tile schedule
-
-// prefix[g+1] - prefix[g] = ceil(rows_g / BM) * ntiles_g for g in [0, G), where
-// group E (if has_shared) is the shared expert with T rows.  Wave 0 scans.
-__device__ int build_tile_prefix(int* prefix, const int32_t* counts, int E, int T, bool has_shared,
-                                 int BM, int nt_routed, int nt_shared) {
-  const int G = E + (has_shared ? 1 : 0);
-  if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x;
-    int carry = 0;
-    for (int base = 0; base < G; base += kWave) {
-      const int g = base + lane;
-      int v = 0;
-      if (g < G) {
-        const int rows = (g < E) ? counts[g] : T;
-        v = static_cast<int>(ceil_div(rows, BM)) * ((g < E) ? nt_routed : nt_shared);
-      }
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int n = __shfl_up(v, o, kWave);
-        if (lane >= o) v += n;
-      }
-      if (g < G) prefix[g + 1] = carry + v;
-      carry += __shfl(v, kWave - 1, kWave);
-    }
-    if (lane == 0) prefix[0] = 0;
-  }
-  __syncthreads();
-  return prefix[G];
-}
-
-struct TileInfo {
-  int group;   // expert id, or E for the shared expert
-  bool shared;
-  int rows;    // rows of the group
-  int rowbase; // first dispatch row of the group (routed) or 0 (shared)
-  int m0;      // first row of the tile inside the group
-  int nt;      // n-tile index
-};
-
-__device__ __forceinline__ TileInfo find_tile(const int* prefix, int G, int tile, const ExpertArgs& a,
-                                              int BM) {
-  int lo = 0, hi = G;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (prefix[mid] <= tile) lo = mid; else hi = mid;
-  }
-  TileInfo t;
-  t.group = lo;
-  t.shared = lo == a.E;
-  t.rows = t.shared ? a.T : a.counts[lo];
-  t.rowbase = t.shared ? 0 : a.offsets[lo];
-  const int mt = static_cast<int>(ceil_div(t.rows, BM));
-  const int local = tile - prefix[lo];
-  t.nt = local / mt;
-  t.m0 = (local % mt) * BM;
-  return t;
-}
-
-// Token behind row m of a tile (m clamped into the group by the caller).
-__device__ __forceinline__ int row_token(const ExpertArgs& a, const TileInfo& t, int m) {
-  return t.shared ? m : a.perm[t.rowbase + m] / a.K;
-}
-
-__device__ __forceinline__ void zero_output(const ExpertArgs& a) {
-  const size_t n = static_cast<size_t>(a.T) * a.H;
-  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
-  const size_t first = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  float4* y4 = reinterpret_cast<float4*>(a.y);
-  const float4 z = {0.f, 0.f, 0.f, 0.f};
-  for (size_t i = first; i < n / 4; i += stride) y4[i] = z;
-  for (size_t i = (n / 4) * 4 + first; i < n; i += stride) a.y[i] = 0.f;
-}
-
 // ---------------------------------------------------------------- wave-level MFMA streams
+//
+// Contraction chunks are 128 elements.  For bf16, chunk step s (0..3) covers
+// elements [32s, 32s+32); lane group g = lane/16 holds elements [32s+8g, +8) of its
+// row, so the four lanes of a row read 64 contiguous bytes per load instruction.
+// The next chunk's loads are issued before the current chunk's MFMAs (register
+// double buffering), so every wave keeps a full chunk of weight bytes in flight.
 
-// acc[i][j] += A(row block i) . B(column block j) over 128-element chunks [kb, ke).
-// arow[i] / brow[j] point at this lane's row (lane % 16) of each block.
 template <int RM, int CN>
-__device__ __forceinline__ void wave_mma_bf16(const uint16_t* const (&arow)[RM],
-                                              const uint16_t* const (&brow)[CN], int kb, int ke, int g,
-                                              f32x4 (&acc)[RM][CN]) {
-  for (int kc = kb; kc < ke; ++kc) {
-    const int k = kc * 128 + 32 * g;
-    uint4 a[RM][4], b[CN][4];
+struct Bf16Chunk {
+  uint4 a[RM][4], b[CN][4];
+  __device__ __forceinline__ void load(const uint16_t* const (&arow)[RM], const uint16_t* const (&brow)[CN],
+                                       int kc, int g) {
 #pragma unroll
-    for (int j = 0; j < CN; ++j)
+    for (int s = 0; s < 4; ++s) {
+      const int k = kc * 128 + 32 * s + 8 * g;
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        b[j][s] = ld16_stream(brow[j] + k + 8 * s);
+      for (int j = 0; j < CN; ++j) b[j][s] = ld16_stream(brow[j] + k);
 #pragma unroll
-    for (int i = 0; i < RM; ++i)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) a[i][s] = *reinterpret_cast<const uint4*>(arow[i] + k + 8 * s);
+      for (int i = 0; i < RM; ++i) a[i][s] = ld16(arow[i] + k);
+    }
+  }
+  __device__ __forceinline__ void mma(f32x4 (&acc)[RM][CN]) const {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -134,40 +62,56 @@ __device__ __forceinline__ void wave_mma_bf16(const uint16_t* const (&arow)[RM],
 #pragma unroll
         for (int j = 0; j < CN; ++j) acc[i][j] = mfma_bf16_16x16x32(a[i][s], b[j][s], acc[i][j]);
   }
+};
+
+// acc[i][j] += A(row block i) . B(column block j) over chunks [kb, ke).
+// arow[i] / brow[j] point at this lane's row (lane % 16) of each block.
+template <int RM, int CN>
+__device__ __forceinline__ void wave_mma_bf16(const uint16_t* const (&arow)[RM],
+                                              const uint16_t* const (&brow)[CN], int kb, int ke, int g,
+                                              f32x4 (&acc)[RM][CN]) {
+  if (kb >= ke) return;
+  Bf16Chunk<RM, CN> c0, c1;
+  c0.load(arow, brow, kb, g);
+  int kc = kb;
+  for (; kc + 1 < ke; kc += 2) {
+    c1.load(arow, brow, kc + 1, g);
+    c0.mma(acc);
+    if (kc + 2 < ke) c0.load(arow, brow, kc + 2, g);
+    c1.mma(acc);
+  }
+  if (kc < ke) c0.mma(acc);
 }
 
-// fp8: one MFMA per 128-element chunk = one scale group.  ascale[i][e] points at
-// the scale row of output row 4*(lane/16)+e of block i, bscale[j] at the scale row
-// of this lane's output column; partial products are rescaled in float32.
+// fp8: one MFMA per 128-element chunk = one scale group.  Lane group g holds bytes
+// [16g, 16g+16) and [64+16g, 64+16g+16) of its row's chunk (two 64-byte runs across
+// the four lanes of a row).  ascale[i][e] points at the scale row of output row
+// 4*(lane/16)+e of block i, bscale[j] at the scale row of this lane's output column;
+// partial products are rescaled in float32.
 template <int RM, int CN>
-__device__ __forceinline__ void wave_mma_fp8(const uint8_t* const (&arow)[RM],
-                                             const float* const (&ascale)[RM][4],
-                                             const uint8_t* const (&brow)[CN],
-                                             const float* const (&bscale)[CN], int kb, int ke, int g,
-                                             f32x4 (&acc)[RM][CN]) {
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  for (int kc = kb; kc < ke; ++kc) {
-    const int k = kc * 128 + 32 * g;
-    i32x8 a[RM], b[CN];
+struct Fp8Chunk {
+  i32x8 a[RM], b[CN];
+  float sa[RM][4], sb[CN];
+  __device__ __forceinline__ static i32x8 pack(uint4 lo, uint4 hi) {
+    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+  __device__ __forceinline__ void load(const uint8_t* const (&arow)[RM], const float* const (&ascale)[RM][4],
+                                       const uint8_t* const (&brow)[CN], const float* const (&bscale)[CN],
+                                       int kc, int g) {
+    const int k = kc * 128 + 16 * g;
 #pragma unroll
-    for (int j = 0; j < CN; ++j) {
-      const uint4 lo = ld16_stream(brow[j] + k);
-      const uint4 hi = ld16_stream(brow[j] + k + 16);
-      b[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
+    for (int j = 0; j < CN; ++j) b[j] = pack(ld16_stream(brow[j] + k), ld16_stream(brow[j] + k + 64));
 #pragma unroll
-    for (int i = 0; i < RM; ++i) {
-      const uint4 lo = *reinterpret_cast<const uint4*>(arow[i] + k);
-      const uint4 hi = *reinterpret_cast<const uint4*>(arow[i] + k + 16);
-      a[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-    float sb[CN], sa[RM][4];
+    for (int i = 0; i < RM; ++i) a[i] = pack(ld16(arow[i] + k), ld16(arow[i] + k + 64));
 #pragma unroll
     for (int j = 0; j < CN; ++j) sb[j] = bscale[j][kc];
 #pragma unroll
     for (int i = 0; i < RM; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) sa[i][e] = ascale[i][e][kc];
+  }
+  __device__ __forceinline__ void mma(f32x4 (&acc)[RM][CN]) const {
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < RM; ++i)
 #pragma unroll
@@ -177,6 +121,25 @@ __device__ __forceinline__ void wave_mma_fp8(const uint8_t* const (&arow)[RM],
         for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(p[e], sa[i][e] * sb[j], acc[i][j][e]);
       }
   }
+};
+
+template <int RM, int CN>
+__device__ __forceinline__ void wave_mma_fp8(const uint8_t* const (&arow)[RM],
+                                             const float* const (&ascale)[RM][4],
+                                             const uint8_t* const (&brow)[CN],
+                                             const float* const (&bscale)[CN], int kb, int ke, int g,
+                                             f32x4 (&acc)[RM][CN]) {
+  if (kb >= ke) return;
+  Fp8Chunk<RM, CN> c0, c1;
+  c0.load(arow, ascale, brow, bscale, kb, g);
+  int kc = kb;
+  for (; kc + 1 < ke; kc += 2) {
+    c1.load(arow, ascale, brow, bscale, kc + 1, g);
+    c0.mma(acc);
+    if (kc + 2 < ke) c0.load(arow, ascale, brow, bscale, kc + 2, g);
+    c1.mma(acc);
+  }
+  if (kc < ke) c0.mma(acc);
 }
 
 // ---------------------------------------------------------------- gate/up + SwiGLU (MFMA)
@@ -533,8 +496,14 @@ int tile_bound(const ExpertArgs& a, int BM, int nt_routed, int nt_shared) {
   return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(b, kMaxGrid)));
 }
 
-// Rows per expert decide the tile height: 16 rows while the average expert sees
-// at most 16 tokens (decode), 32 rows above that.
+// Rows per expert decide the kernel: the average expert sees rho = T*K/E rows
+// (the same load measure as the small-M / large-M family choice of
+// [DeepGEMM fork PR #5, "Dynamic family selection"]).  Up to 16 rows: 16-row
+// streaming tiles; up to kTiledRows: 32-row streaming tiles; above: LDS-tiled
+// MFMA kernels, 128-row tiles, and 256-row tiles from kTallRows.
+constexpr int64_t kTiledRows = 48, kTallRows = 160;
+
+int64_t rows_per_expert(const ExpertArgs& a) { return static_cast<int64_t>(a.T) * a.K / a.E; }
 bool tall_tiles(const ExpertArgs& a) { return static_cast<int64_t>(a.T) * a.K > 16LL * a.E; }
 
 }  // namespace
@@ -546,6 +515,8 @@ hipError_t launch_gate_up(const ExpertArgs& a, int weight_dtype, hipStream_t str
     return hipGetLastError();
   }
   const bool fp8 = weight_dtype == kDtypeFp8;
+  const int64_t rho = rows_per_expert(a);
+  if (rho >= kTiledRows) return launch_gate_up_tiled(a, fp8, rho >= kTallRows, stream);
   if (tall_tiles(a)) {
     const int grid = tile_bound(a, 32, a.I / 32, a.S / 32);
     if (fp8) gate_up_mfma_kernel<2, 2, 4, true><<<grid, 256, 0, stream>>>(a);
@@ -565,6 +536,8 @@ hipError_t launch_down(const ExpertArgs& a, int weight_dtype, hipStream_t stream
     return hipGetLastError();
   }
   const bool fp8 = weight_dtype == kDtypeFp8;
+  const int64_t rho = rows_per_expert(a);
+  if (rho >= kTiledRows && a.H % 256 == 0) return launch_down_tiled(a, fp8, rho >= kTallRows, stream);
   if (tall_tiles(a)) {
     const int grid = tile_bound(a, 32, a.H / 64, a.H / 64);
     if (fp8) down_mfma_kernel<2, 4, 4, true><<<grid, 256, 0, stream>>>(a);

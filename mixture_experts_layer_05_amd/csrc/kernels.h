@@ -47,6 +47,8 @@ __global__ void dispatch_kernel(const int32_t*, int, int, int, int32_t*, int32_t
 // experts.hip: host-side launchers (they pick tile shapes and grid sizes).
 hipError_t launch_gate_up(const ExpertArgs& a, int weight_dtype, hipStream_t stream);
 hipError_t launch_down(const ExpertArgs& a, int weight_dtype, hipStream_t stream);
+hipError_t launch_gate_up_tiled(const ExpertArgs& a, bool fp8, bool tall, hipStream_t stream);
+hipError_t launch_down_tiled(const ExpertArgs& a, bool fp8, bool tall, hipStream_t stream);
 hipError_t launch_quant_x(const ExpertArgs& a, uint8_t* xq, float* xs, hipStream_t stream);
 hipError_t launch_quant_h(const ExpertArgs& a, uint8_t* hq, float* hs, hipStream_t stream);
 

@@ -1,0 +1,89 @@
+// Tile schedule shared by the expert kernels (included by each kernel file).
+//
+// A "group" is a routed expert (rows = its dispatch segment) or the shared expert
+// (rows = every token).  Tiles are (group, m-tile of BM rows, n-tile); the
+// per-group tile counts come from expert_counts on the device, so no host round
+// trip is needed.
+#pragma once
+
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kDtypeF32 = 0, kDtypeBf16 = 1, kDtypeFp8 = 2;
+
+// prefix[g+1] - prefix[g] = ceil(rows_g / BM) * ntiles_g for g in [0, G), where
+// group E (if has_shared) is the shared expert with T rows.  Wave 0 scans.
+__device__ int build_tile_prefix(int* prefix, const int32_t* counts, int E, int T, bool has_shared,
+                                 int BM, int nt_routed, int nt_shared) {
+  const int G = E + (has_shared ? 1 : 0);
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    int carry = 0;
+    for (int base = 0; base < G; base += kWave) {
+      const int g = base + lane;
+      int v = 0;
+      if (g < G) {
+        const int rows = (g < E) ? counts[g] : T;
+        v = static_cast<int>(ceil_div(rows, BM)) * ((g < E) ? nt_routed : nt_shared);
+      }
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int n = __shfl_up(v, o, kWave);
+        if (lane >= o) v += n;
+      }
+      if (g < G) prefix[g + 1] = carry + v;
+      carry += __shfl(v, kWave - 1, kWave);
+    }
+    if (lane == 0) prefix[0] = 0;
+  }
+  __syncthreads();
+  return prefix[G];
+}
+
+struct TileInfo {
+  int group;   // expert id, or E for the shared expert
+  bool shared;
+  int rows;    // rows of the group
+  int rowbase; // first dispatch row of the group (routed) or 0 (shared)
+  int m0;      // first row of the tile inside the group
+  int nt;      // n-tile index
+};
+
+__device__ __forceinline__ TileInfo find_tile(const int* prefix, int G, int tile, const ExpertArgs& a,
+                                              int BM) {
+  int lo = 0, hi = G;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (prefix[mid] <= tile) lo = mid; else hi = mid;
+  }
+  TileInfo t;
+  t.group = lo;
+  t.shared = lo == a.E;
+  t.rows = t.shared ? a.T : a.counts[lo];
+  t.rowbase = t.shared ? 0 : a.offsets[lo];
+  const int mt = static_cast<int>(ceil_div(t.rows, BM));
+  const int local = tile - prefix[lo];
+  t.nt = local / mt;
+  t.m0 = (local % mt) * BM;
+  return t;
+}
+
+// Token behind row m of a tile (m clamped into the group by the caller).
+__device__ __forceinline__ int row_token(const ExpertArgs& a, const TileInfo& t, int m) {
+  return t.shared ? m : a.perm[t.rowbase + m] / a.K;
+}
+
+__device__ __forceinline__ void zero_output(const ExpertArgs& a) {
+  const size_t n = static_cast<size_t>(a.T) * a.H;
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  const size_t first = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  float4* y4 = reinterpret_cast<float4*>(a.y);
+  const float4 z = {0.f, 0.f, 0.f, 0.f};
+  for (size_t i = first; i < n / 4; i += stride) y4[i] = z;
+  for (size_t i = (n / 4) * 4 + first; i < n; i += stride) a.y[i] = 0.f;
+}
+
+}  // namespace
+}  // namespace moe

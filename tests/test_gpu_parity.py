@@ -50,6 +50,10 @@ def test_large_layer_512(alpha):
     _run(W.LARGE, 512, W.base_seed(3, 512), alpha, tokens=Hn.sample_tokens(512, 24))
 
 
+def test_large_layer_2048_uniform_sampled():
+    _run(W.LARGE, 2048, W.base_seed(3, 2048), 0.0, tokens=Hn.sample_tokens(2048, 16))
+
+
 def test_large_layer_8192_skewed_sampled():
     _run(W.LARGE, 8192, W.base_seed(3, 8192), 1.5, tokens=Hn.sample_tokens(8192, 16))
 
@@ -71,6 +75,20 @@ def test_fp8_small_budget_drops_experts():
 # ----------------------------------------------------------------------------- edge cases
 
 EDGE = W.LayerShape("edge_k_eq_e", 256, 4, 256, 4, 128, W.DT_BF16, W.DT_BF16)
+
+
+# Few experts, many rows each: the LDS-tiled kernels with partial 128- and 256-row tiles.
+TILED = W.LayerShape("tiled_rows", 512, 4, 256, 2, 256, W.DT_BF16, W.DT_BF16)
+
+
+@pytest.mark.parametrize("T", [300, 700])
+def test_tiled_kernels_with_partial_tiles(T):
+    _run(TILED, T, 20 + T)
+
+
+@pytest.mark.parametrize("T", [300, 700])
+def test_tiled_fp8_kernels_with_partial_tiles(T):
+    _run(TILED.with_(name="tiled_rows_fp8", weight_dtype=W.DT_FP8), T, 30 + T)
 
 
 def test_k_equals_e_with_ragged_tokens():

@@ -144,10 +144,12 @@ int moe_dispatch(const moe_config* cfg, int32_t num_tokens, const int32_t* topk_
  *   y[t,:] = sum_k topk_weights[t,k] * down_e(silu(gate_e x_t) * up_e x_t)
  *          + shared_gate[t] * down_s(silu(gate_s x_t) * up_s x_t)
  * with e = topk_ids[t,k], taken through the dispatch outputs.  y (device) out
- * [T, H] float32, overwritten.  The intermediate activations are stored in the
- * workspace as bf16 (BF16 weights), float32 (F32) or e4m3 + group-128 scales
- * (FP8).  Accumulation is float32; the combine uses float32 atomics, so the
- * bits of y may vary between runs in the last place. */
+ * [T, H] float32, 16-byte aligned, overwritten.  The intermediate activations
+ * are stored in the workspace as bf16 (BF16 weights), float32 (F32) or e4m3 +
+ * group-128 scales (FP8).  Accumulation is float32.  Each routed slot's
+ * down-projection row is kept in the workspace and the slots of a token are
+ * added to y in slot order after the shared term, so y is bit-reproducible
+ * (no atomics).  Slots with weight 0 (dropped by the budget) are skipped. */
 int moe_forward(const moe_config* cfg, int32_t num_tokens, const void* x,
                 const float* topk_weights, const float* shared_gate,
                 const int32_t* expert_counts, const int32_t* expert_offsets, const int32_t* perm,
@@ -155,9 +157,10 @@ int moe_forward(const moe_config* cfg, int32_t num_tokens, const void* x,
                 float* y, void* workspace, size_t workspace_bytes, void* stream);
 
 /* The two halves of moe_forward, same arguments, for callers that time or
- * overlap them: gate_up zero-fills y and writes the intermediate activations to
- * the workspace; down reads them and accumulates into y.  Calling gate_up then
- * down on one stream with one workspace equals moe_forward. */
+ * overlap them: gate_up writes the intermediate activations to the workspace
+ * (y is not touched); down reads them, writes the per-slot outputs to the
+ * workspace and then y.  Calling gate_up then down on one stream with one
+ * workspace equals moe_forward. */
 int moe_forward_gate_up(const moe_config* cfg, int32_t num_tokens, const void* x,
                         const float* topk_weights, const float* shared_gate,
                         const int32_t* expert_counts, const int32_t* expert_offsets,

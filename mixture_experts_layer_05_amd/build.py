@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_mi355x.so")
-SOURCES = ["api.hip", "route.hip", "dispatch.hip", "experts.hip", "tile_gemm.hip"]
+SOURCES = ["api.hip", "route.hip", "dispatch.hip", "experts.hip", "tile_gemm.hip", "stream_gemm.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

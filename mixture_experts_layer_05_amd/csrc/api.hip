@@ -46,7 +46,7 @@ int check_tokens(const moe_config* c, int32_t T) {
 }
 
 struct Layout {
-  size_t z, h, xq, xs, hq, hs, total;
+  size_t z, h, o, xq, xs, hq, hs, total;
   int ldz;
   size_t h_shared;  // element offset of the shared expert's rows in h
 };
@@ -67,6 +67,7 @@ Layout layout(const moe_config& c, int64_t T) {
   L.h_shared = routed;
   const size_t hsize = (c.weight_dtype == MOE_DTYPE_BF16) ? 2 : 4;
   L.h = take(elems * hsize);
+  L.o = take(static_cast<size_t>(T) * c.num_experts_per_tok * c.hidden_size * sizeof(float));
   if (c.weight_dtype == MOE_DTYPE_FP8_E4M3_G128) {
     L.xq = take(static_cast<size_t>(T) * c.hidden_size);
     L.xs = take(static_cast<size_t>(T) * (c.hidden_size / kGroup) * sizeof(float));
@@ -134,6 +135,7 @@ ExpertArgs expert_args(const moe_config& c, int32_t T, const void* x, const floa
     a.hq = at<uint8_t>(ws, L.hq);
     a.hs = at<float>(ws, L.hs);
   }
+  a.o = at<float>(ws, L.o);
   a.y = y;
   a.T = T;
   a.H = c.hidden_size;
@@ -257,7 +259,8 @@ int moe_forward_down(const moe_config* cfg, int32_t T, const void* x, const floa
   if ((st = check_workspace(*cfg, T, ws, ws_bytes, &L))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const ExpertArgs a = expert_args(*cfg, T, x, topk_w, shared_gate, counts, offsets, perm, *w, y, ws, L);
-  return launched(launch_down(a, cfg->weight_dtype, s));
+  if ((st = launched(launch_down(a, cfg->weight_dtype, s)))) return st;
+  return launched(launch_combine(a, s));
 }
 
 int moe_forward(const moe_config* cfg, int32_t T, const void* x, const float* topk_w,

@@ -7,6 +7,11 @@ namespace moe {
 
 // Everything an expert kernel may need.  Unused fields are null / zero.
 //
+// Down-projection outputs: a routed row (token t, slot k) is written, unweighted,
+// to row t*K+k of o; shared-expert rows go straight to y, weighted by
+// sigmoid(g_t).  A combine pass then adds the weighted slots of each token in
+// slot order, so y is bit-reproducible and no atomics are needed.
+//
 // Intermediate activations h: routed rows first, in dispatch (perm) order,
 // [T*K, I]; then the shared expert's rows [T, S] starting at element h_shared.
 // With fp8 weights h is kept in float32 and then quantised to hq / hs with the
@@ -28,6 +33,7 @@ struct ExpertArgs {
   const float* xs;               // fp8: scales [T, H/128]
   const uint8_t* hq;             // fp8: quantised h
   const float* hs;               // fp8: scales of h
+  float* o;                      // [T*K, H] unweighted routed outputs, row = slot t*K+k
   float* y;                      // [T, H]
   int T, H, I, S, E, K;
 };
@@ -49,6 +55,9 @@ hipError_t launch_gate_up(const ExpertArgs& a, int weight_dtype, hipStream_t str
 hipError_t launch_down(const ExpertArgs& a, int weight_dtype, hipStream_t stream);
 hipError_t launch_gate_up_tiled(const ExpertArgs& a, bool fp8, bool tall, hipStream_t stream);
 hipError_t launch_down_tiled(const ExpertArgs& a, bool fp8, bool tall, hipStream_t stream);
+hipError_t launch_gate_up_stream(const ExpertArgs& a, bool fp8, int64_t rho, hipStream_t stream);
+hipError_t launch_down_stream(const ExpertArgs& a, bool fp8, int64_t rho, hipStream_t stream);
+hipError_t launch_combine(const ExpertArgs& a, hipStream_t stream);
 hipError_t launch_quant_x(const ExpertArgs& a, uint8_t* xq, float* xs, hipStream_t stream);
 hipError_t launch_quant_h(const ExpertArgs& a, uint8_t* hq, float* hs, hipStream_t stream);
 

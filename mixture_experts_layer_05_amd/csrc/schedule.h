@@ -75,14 +75,16 @@ __device__ __forceinline__ int row_token(const ExpertArgs& a, const TileInfo& t,
   return t.shared ? m : a.perm[t.rowbase + m] / a.K;
 }
 
-__device__ __forceinline__ void zero_output(const ExpertArgs& a) {
-  const size_t n = static_cast<size_t>(a.T) * a.H;
-  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
-  const size_t first = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  float4* y4 = reinterpret_cast<float4*>(a.y);
-  const float4 z = {0.f, 0.f, 0.f, 0.f};
-  for (size_t i = first; i < n / 4; i += stride) y4[i] = z;
-  for (size_t i = (n / 4) * 4 + first; i < n; i += stride) a.y[i] = 0.f;
+// Destination of row m of a down-projection tile: routed rows go, unweighted, to
+// their slot's row of o; shared-expert rows go to y weighted by sigmoid(g).
+struct DownDst {
+  float* row;
+  float w;
+};
+
+__device__ __forceinline__ DownDst down_row(const ExpertArgs& a, const TileInfo& t, int m) {
+  if (t.shared) return {a.y + static_cast<size_t>(m) * a.H, a.shared_gate[m]};
+  return {a.o + static_cast<size_t>(a.perm[t.rowbase + m]) * a.H, 1.0f};
 }
 
 }  // namespace

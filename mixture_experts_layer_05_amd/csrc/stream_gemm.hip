@@ -1,0 +1,355 @@
+// Weight-streaming grouped expert GEMMs for decode-sized M (few rows per expert).
+//
+// At decode sizes every routed expert sees a handful of tokens, so the layer is
+// bound by reading each touched expert's weights once from HBM [SpecForge PR
+// #943, "Motivation": each draft step streams the touched experts' weights].
+// This kernel is organised for that stream:
+//
+//   * a workgroup (4 waves) owns a tile of BN weight rows of one group (routed
+//     expert or shared expert) and BM rows of tokens;
+//   * the contraction runs in stages of 256 bytes per row (128 bf16, or one fp8
+//     128-group of 128 bytes).  Global loads give each row 256 (bf16) or 128 (fp8)
+//     contiguous bytes per wave instruction, the pattern that measured ~7 TB/s on
+//     MI355X, whereas loading MFMA fragments straight from HBM (16 rows x 64 bytes
+//     per instruction) stays near 4-5 TB/s;
+//   * two stages are in flight in registers while the current one is consumed
+//     from LDS, so each workgroup keeps ~2 x (BN + BM) x 256 bytes of loads
+//     outstanding and a CU holds several workgroups;
+//   * each wave computes all BM rows against BN/4 weight rows with 16x16x32 bf16
+//     or 16x16x128 fp8 MFMAs (fp8 partial sums rescaled by the row and column
+//     group scales in float32);
+//   * gate/up tiles fuse SwiGLU and write h; down tiles stage the finished tile in
+//     LDS and store whole row segments (512 bytes) of each slot's output row.
+#include "kernels.h"
+#include "schedule.h"
+
+namespace moe {
+namespace {
+
+constexpr int kStreamThreads = 256;
+constexpr int kXcdCount = 8;
+
+enum class SMode { GateUp, Down };
+
+template <SMode MODE, int BM, int BN, bool FP8>
+struct StreamCfg {
+  static constexpr int kRowData = FP8 ? 128 : 256;            // bytes per row per stage
+  static constexpr int kRowStride = kRowData + 16;            // padded LDS row
+  static constexpr int kLanesPerRow = kRowData / 16;
+  static constexpr int kRowsPerPass = kStreamThreads / kLanesPerRow;
+  static constexpr int kAPasses = (BM + kRowsPerPass - 1) / kRowsPerPass;
+  static constexpr int kBPasses = BN / kRowsPerPass;
+  static constexpr int kRM = BM / 16;                          // row blocks
+  static constexpr int kCB = BN / 4 / 16;                      // column blocks per wave
+  static constexpr int kElems = FP8 ? 128 : 128;               // contraction elements per stage
+  static constexpr int kStage = (BM + BN) * kRowStride;
+  static constexpr int kOutBytes = MODE == SMode::Down ? BM * (BN + 4) * 4 : 0;
+  static constexpr int kSmem = kStage > kOutBytes ? kStage : kOutBytes;
+  static_assert(BN % kRowsPerPass == 0, "BN must be a multiple of the rows per pass");
+  static_assert(MODE == SMode::Down || kCB % 2 == 0, "gate/up needs gate and up blocks");
+};
+
+// Weight row of the LDS B tile read by column block j of wave w (lane row r).
+// Gate/up tiles hold BN/2 gate rows then the BN/2 up rows of the same columns;
+// wave w takes the gate and up rows of intermediate columns [w*BN/8, (w+1)*BN/8).
+template <SMode MODE, int BN, int kCB>
+__device__ __forceinline__ int stream_b_row(int w, int j, int r) {
+  if constexpr (MODE == SMode::GateUp) {
+    const int half = kCB / 2;
+    const int jh = (j < half) ? j : j - half;
+    return ((j < half) ? 0 : BN / 2) + w * (BN / 8) + 16 * jh + r;
+  } else {
+    return w * (BN / 4) + 16 * j + r;
+  }
+}
+
+template <SMode MODE, int BM, int BN, bool FP8>
+__global__ void __launch_bounds__(kStreamThreads) stream_expert_kernel(ExpertArgs a) {
+  using C = StreamCfg<MODE, BM, BN, FP8>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::kSmem];
+  __shared__ __attribute__((aligned(16))) float sscale[FP8 ? BM + BN : 4];
+  __shared__ int prefix[kMaxExperts + 2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+
+  const bool has_shared = a.S > 0;
+  const int G = a.E + (has_shared ? 1 : 0);
+  const int H = a.H;
+  const int bn_cols = (MODE == SMode::GateUp) ? BN / 2 : BN;
+  const int nt_r = (MODE == SMode::GateUp) ? a.I / bn_cols : H / bn_cols;
+  const int nt_s = has_shared ? ((MODE == SMode::GateUp) ? a.S / bn_cols : H / bn_cols) : 0;
+  const int total = build_tile_prefix(prefix, a.counts, a.E, a.T, has_shared, BM, nt_r, nt_s);
+
+  // Workgroup b runs on XCD b % 8: consecutive tiles (same weight slab, next m-tile)
+  // go to the same XCD.
+  const int per_xcd = gridDim.x / kXcdCount;
+  const int first = (blockIdx.x % kXcdCount) * per_xcd + blockIdx.x / kXcdCount;
+
+  const int lrow = tid / C::kLanesPerRow;            // row inside a load pass
+  const int lcol = (tid % C::kLanesPerRow) * 16;     // byte offset inside the stage slice
+
+  for (int tile = first; tile < total; tile += gridDim.x) {
+    const TileInfo t = find_tile(prefix, G, tile, a, BM);
+    const int kdim = (MODE == SMode::GateUp) ? H : (t.shared ? a.S : a.I);
+    const int nk = kdim / C::kElems;
+    const int n0 = t.nt * bn_cols;
+    const size_t esz = FP8 ? 1 : 2;
+    const int ng = kdim / kGroup;
+    auto hrow = [&](int m) -> size_t {
+      return t.shared ? a.h_shared + static_cast<size_t>(m) * kdim
+                      : static_cast<size_t>(t.rowbase + m) * kdim;
+    };
+
+    // ---- sources of this thread's 16-byte pieces
+    const uint8_t* asrc[C::kAPasses];
+    bool aload[C::kAPasses];
+#pragma unroll
+    for (int q = 0; q < C::kAPasses; ++q) {
+      const int row = lrow + q * C::kRowsPerPass;
+      aload[q] = row < BM;
+      const int m = min(t.m0 + min(row, BM - 1), t.rows - 1);
+      if constexpr (MODE == SMode::GateUp)
+        asrc[q] = (FP8 ? a.xq : static_cast<const uint8_t*>(a.x)) +
+                  static_cast<size_t>(row_token(a, t, m)) * H * esz;
+      else
+        asrc[q] = (FP8 ? a.hq : static_cast<const uint8_t*>(a.h)) + hrow(m) * esz;
+    }
+    const uint8_t* w0;
+    const uint8_t* w1 = nullptr;
+    const float* sw0 = nullptr;
+    const float* sw1 = nullptr;
+    if constexpr (MODE == SMode::GateUp) {
+      w0 = static_cast<const uint8_t*>(t.shared ? a.ws_gate : a.w_gate);
+      w1 = static_cast<const uint8_t*>(t.shared ? a.ws_up : a.w_up);
+      if (!t.shared) {
+        w0 += static_cast<size_t>(t.group) * a.I * H * esz;
+        w1 += static_cast<size_t>(t.group) * a.I * H * esz;
+      }
+      if constexpr (FP8) {
+        sw0 = t.shared ? a.ss_gate : a.s_gate + static_cast<size_t>(t.group) * a.I * ng;
+        sw1 = t.shared ? a.ss_up : a.s_up + static_cast<size_t>(t.group) * a.I * ng;
+      }
+    } else {
+      w0 = static_cast<const uint8_t*>(t.shared ? a.ws_down : a.w_down);
+      if (!t.shared) w0 += static_cast<size_t>(t.group) * H * a.I * esz;
+      if constexpr (FP8) sw0 = t.shared ? a.ss_down : a.s_down + static_cast<size_t>(t.group) * H * ng;
+    }
+    const uint8_t* bsrc[C::kBPasses];
+#pragma unroll
+    for (int q = 0; q < C::kBPasses; ++q) {
+      const int br = lrow + q * C::kRowsPerPass;
+      if constexpr (MODE == SMode::GateUp)
+        bsrc[q] = (br < BN / 2) ? w0 + static_cast<size_t>(n0 + br) * kdim * esz
+                                : w1 + static_cast<size_t>(n0 + br - BN / 2) * kdim * esz;
+      else
+        bsrc[q] = w0 + static_cast<size_t>(n0 + br) * kdim * esz;
+    }
+    const float* sptr = nullptr;
+    if constexpr (FP8) {
+      if (tid < BM) {
+        const int m = min(t.m0 + tid, t.rows - 1);
+        if constexpr (MODE == SMode::GateUp) sptr = a.xs + static_cast<size_t>(row_token(a, t, m)) * ng;
+        else sptr = a.hs + hrow(m) / kGroup;
+      } else if (tid < BM + BN) {
+        const int br = tid - BM;
+        if constexpr (MODE == SMode::GateUp)
+          sptr = (br < BN / 2) ? sw0 + static_cast<size_t>(n0 + br) * ng
+                               : sw1 + static_cast<size_t>(n0 + br - BN / 2) * ng;
+        else
+          sptr = sw0 + static_cast<size_t>(n0 + br) * ng;
+      }
+    }
+
+    struct Regs {
+      uint4 a[C::kAPasses], b[C::kBPasses];
+      float s;
+    };
+    auto gload = [&](Regs& R, int ks) {
+      const size_t off = static_cast<size_t>(ks) * C::kRowData + lcol;
+#pragma unroll
+      for (int q = 0; q < C::kBPasses; ++q) R.b[q] = ld16_stream(bsrc[q] + off);
+#pragma unroll
+      for (int q = 0; q < C::kAPasses; ++q)
+        if (aload[q]) R.a[q] = ld16(asrc[q] + off);
+      if constexpr (FP8) {
+        if (sptr) R.s = sptr[ks];
+      }
+    };
+    auto lstore = [&](const Regs& R) {
+#pragma unroll
+      for (int q = 0; q < C::kAPasses; ++q)
+        if (aload[q])
+          *reinterpret_cast<uint4*>(smem + (lrow + q * C::kRowsPerPass) * C::kRowStride + lcol) = R.a[q];
+#pragma unroll
+      for (int q = 0; q < C::kBPasses; ++q)
+        *reinterpret_cast<uint4*>(smem + (BM + lrow + q * C::kRowsPerPass) * C::kRowStride + lcol) = R.b[q];
+      if constexpr (FP8) {
+        if (tid < BM + BN) sscale[tid] = R.s;
+      }
+    };
+
+    f32x4 acc[C::kRM][C::kCB];
+#pragma unroll
+    for (int i = 0; i < C::kRM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::kCB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&]() {
+      const uint8_t* As = smem + r * C::kRowStride;
+      const uint8_t* Bs = smem + BM * C::kRowStride;
+      if constexpr (!FP8) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          uint4 af[C::kRM], bf[C::kCB];
+#pragma unroll
+          for (int i = 0; i < C::kRM; ++i)
+            af[i] = *reinterpret_cast<const uint4*>(As + 16 * i * C::kRowStride + 64 * s + 16 * g);
+#pragma unroll
+          for (int j = 0; j < C::kCB; ++j)
+            bf[j] = *reinterpret_cast<const uint4*>(
+                Bs + stream_b_row<MODE, BN, C::kCB>(wave, j, r) * C::kRowStride + 64 * s + 16 * g);
+#pragma unroll
+          for (int i = 0; i < C::kRM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::kCB; ++j) acc[i][j] = mfma_bf16_16x16x32(af[i], bf[j], acc[i][j]);
+        }
+      } else {
+        // Lane group g holds bytes [16g, +16) and [64+16g, +16) of its row's 128-byte group.
+        i32x8 af[C::kRM], bf[C::kCB];
+        f32x4 sa[C::kRM];
+        float sb[C::kCB];
+#pragma unroll
+        for (int i = 0; i < C::kRM; ++i) {
+          const uint8_t* p = As + 16 * i * C::kRowStride;
+          const uint4 lo = *reinterpret_cast<const uint4*>(p + 16 * g);
+          const uint4 hi = *reinterpret_cast<const uint4*>(p + 64 + 16 * g);
+          af[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          sa[i] = *reinterpret_cast<const f32x4*>(&sscale[16 * i + 4 * g]);
+        }
+#pragma unroll
+        for (int j = 0; j < C::kCB; ++j) {
+          const int br = stream_b_row<MODE, BN, C::kCB>(wave, j, r);
+          const uint8_t* p = Bs + br * C::kRowStride;
+          const uint4 lo = *reinterpret_cast<const uint4*>(p + 16 * g);
+          const uint4 hi = *reinterpret_cast<const uint4*>(p + 64 + 16 * g);
+          bf[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          sb[j] = sscale[BM + br];
+        }
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < C::kRM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::kCB; ++j) {
+            const f32x4 p = mfma_fp8_16x16x128(af[i], bf[j], zero);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(p[e], sa[i][e] * sb[j], acc[i][j][e]);
+          }
+      }
+    };
+
+    // Two stages in flight in registers (R0 / R1 alternate), one LDS stage consumed.
+    Regs R0, R1;
+    gload(R0, 0);
+    if (nk > 1) gload(R1, 1);
+    for (int ks = 0; ks < nk; ks += 2) {
+      __syncthreads();                   // the previous stage's readers are done
+      lstore(R0);
+      __syncthreads();
+      if (ks + 2 < nk) gload(R0, ks + 2);
+      compute();
+      if (ks + 1 >= nk) break;
+      __syncthreads();
+      lstore(R1);
+      __syncthreads();
+      if (ks + 3 < nk) gload(R1, ks + 3);
+      compute();
+    }
+
+    // ---- epilogue
+    if constexpr (MODE == SMode::GateUp) {
+      const int width = t.shared ? a.S : a.I;
+#pragma unroll
+      for (int i = 0; i < C::kRM; ++i)
+#pragma unroll
+        for (int jh = 0; jh < C::kCB / 2; ++jh) {
+          const int col = n0 + wave * (BN / 8) + 16 * jh + r;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int m = t.m0 + 16 * i + 4 * g + e;
+            if (m < t.rows) {
+              const float hv = silu_f32(acc[i][jh][e]) * acc[i][jh + C::kCB / 2][e];
+              const size_t idx = t.shared ? a.h_shared + static_cast<size_t>(m) * width + col
+                                          : static_cast<size_t>(t.rowbase + m) * width + col;
+              if constexpr (FP8) static_cast<float*>(a.h)[idx] = hv;
+              else static_cast<uint16_t*>(a.h)[idx] = f32_to_bf16_bits(hv);
+            }
+          }
+        }
+    } else {
+      // Stage the BM x BN tile in LDS (the operand tiles are no longer needed),
+      // then each wave adds whole BN-column row segments of y.
+      __syncthreads();
+      float* out = reinterpret_cast<float*>(smem);
+      constexpr int ld = BN + 4;
+#pragma unroll
+      for (int i = 0; i < C::kRM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kCB; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            out[(16 * i + 4 * g + e) * ld + wave * (BN / 4) + 16 * j + r] = acc[i][j][e];
+      __syncthreads();
+      for (int q = wave; q < BM; q += 4) {
+        const int m = t.m0 + q;
+        if (m >= t.rows) break;
+        const DownDst dst = down_row(a, t, m);
+        float* yr = dst.row + n0;
+#pragma unroll
+        for (int c = lane; c < BN; c += kWave) yr[c] = dst.w * out[q * ld + c];
+      }
+    }
+  }
+}
+
+int stream_grid(const ExpertArgs& a, int BM, int nt_routed, int nt_shared, int per_cu) {
+  const int64_t slots = static_cast<int64_t>(a.T) * a.K;
+  int64_t b = (slots / BM + std::min<int64_t>(a.E, slots)) * nt_routed;
+  if (a.S > 0) b += ceil_div(a.T, BM) * nt_shared;
+  b = std::min<int64_t>(b, 256LL * per_cu);
+  return static_cast<int>(std::max<int64_t>(kXcdCount, ceil_div(b, kXcdCount) * kXcdCount));
+}
+
+template <SMode MODE, int BM, bool FP8>
+hipError_t launch_stream(const ExpertArgs& a, hipStream_t stream) {
+  constexpr int BN = 128;
+  const int bn_cols = (MODE == SMode::GateUp) ? BN / 2 : BN;
+  const int nt_r = (MODE == SMode::GateUp) ? a.I / bn_cols : a.H / bn_cols;
+  const int nt_s = (MODE == SMode::GateUp) ? a.S / bn_cols : a.H / bn_cols;
+  const int grid = stream_grid(a, BM, nt_r, nt_s, 3);
+  stream_expert_kernel<MODE, BM, BN, FP8><<<grid, kStreamThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Row tile height from the average rows per expert rho = T*K/E.
+hipError_t launch_gate_up_stream(const ExpertArgs& a, bool fp8, int64_t rho, hipStream_t stream) {
+  if (rho <= 12) return fp8 ? launch_stream<SMode::GateUp, 16, true>(a, stream)
+                            : launch_stream<SMode::GateUp, 16, false>(a, stream);
+  if (rho <= 24) return fp8 ? launch_stream<SMode::GateUp, 32, true>(a, stream)
+                            : launch_stream<SMode::GateUp, 32, false>(a, stream);
+  return fp8 ? launch_stream<SMode::GateUp, 64, true>(a, stream)
+             : launch_stream<SMode::GateUp, 64, false>(a, stream);
+}
+
+hipError_t launch_down_stream(const ExpertArgs& a, bool fp8, int64_t rho, hipStream_t stream) {
+  if (rho <= 12) return fp8 ? launch_stream<SMode::Down, 16, true>(a, stream)
+                            : launch_stream<SMode::Down, 16, false>(a, stream);
+  if (rho <= 24) return fp8 ? launch_stream<SMode::Down, 32, true>(a, stream)
+                            : launch_stream<SMode::Down, 32, false>(a, stream);
+  return fp8 ? launch_stream<SMode::Down, 64, true>(a, stream)
+             : launch_stream<SMode::Down, 64, false>(a, stream);
+}
+
+}  // namespace moe

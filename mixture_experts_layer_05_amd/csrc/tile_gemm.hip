@@ -1,8 +1,8 @@
 // LDS-tiled grouped expert GEMMs for prefill-sized M (many rows per expert).
 //
-// Same contract as the streaming kernels in experts.hip (gate/up + SwiGLU into
-// h; down + gate-weighted float32 combine into y), organised for MFMA
-// throughput instead of weight streaming:
+// Same contract as the streaming kernels in stream_gemm.hip (gate/up + SwiGLU
+// into h; down into the per-slot output rows), organised for MFMA throughput
+// instead of weight streaming:
 //
 //   * a workgroup of 8 waves owns a BM x BN output tile of one group (routed
 //     expert or the shared expert); BM = 256 or 128 rows, BN = 256 columns (for
@@ -69,7 +69,6 @@ __global__ void __launch_bounds__(kTileThreads) tiled_expert_kernel(ExpertArgs a
   const int r = lane & 15, g = lane >> 4;
   const int wm = wave / C::kWGN, wn = wave % C::kWGN;
 
-  if constexpr (MODE == Mode::GateUp) zero_output(a);
   const bool has_shared = a.S > 0;
   const int G = a.E + (has_shared ? 1 : 0);
   const int H = a.H;
@@ -274,19 +273,10 @@ __global__ void __launch_bounds__(kTileThreads) tiled_expert_kernel(ExpertArgs a
         for (int e = 0; e < 4; ++e) {
           const int m = t.m0 + wm * 64 + 16 * i + 4 * g + e;
           if (m >= t.rows) continue;
-          int tok;
-          float wgt;
-          if (t.shared) {
-            tok = m;
-            wgt = a.shared_gate[m];
-          } else {
-            const int slot = a.perm[t.rowbase + m];
-            tok = slot / a.K;
-            wgt = a.topk_w[slot];
-          }
-          float* yr = a.y + static_cast<size_t>(tok) * H + n0 + wn * C::kWN + r;
+          const DownDst dst = down_row(a, t, m);
+          float* yr = dst.row + n0 + wn * C::kWN + r;
 #pragma unroll
-          for (int j = 0; j < C::kNB; ++j) atomicAdd(yr + 16 * j, wgt * acc[i][j][e]);
+          for (int j = 0; j < C::kNB; ++j) yr[16 * j] = dst.w * acc[i][j][e];
         }
     }
   }

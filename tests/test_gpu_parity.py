@@ -148,7 +148,7 @@ def test_routing_is_deterministic():
     b = Hn.run_gpu(case)
     for k in ("ids", "w", "counts", "offsets", "perm", "stats"):
         assert np.array_equal(a[k], b[k]), k
-    assert Hn.rel_l2(a["y"], b["y"]) < 1e-6
+    assert np.array_equal(a["y"], b["y"])   # no atomics: bit-reproducible
 
 
 def test_halves_equal_forward():

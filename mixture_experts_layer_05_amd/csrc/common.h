@@ -23,6 +23,20 @@ __device__ __forceinline__ uint4 ld16_stream(const void* p) {
   return uint4{v.x, v.y, v.z, v.w};
 }
 
+// 16-byte LDS accesses at 8-byte aligned addresses (issued as ds_read2_b64 /
+// ds_write2_b64).  Measured on MI355X for the MFMA fragment pattern (16 rows x
+// 64 bytes per wave read): row strides of 8 mod 16 bytes sustain ~235 B/clk/CU,
+// 16-byte aligned strides ~125 B/clk/CU.  LDS tiles therefore pad rows by 8 bytes.
+__device__ __forceinline__ uint4 lds_ld16(const uint8_t* p) {
+  const uint2 lo = *reinterpret_cast<const uint2*>(p);
+  const uint2 hi = *reinterpret_cast<const uint2*>(p + 8);
+  return uint4{lo.x, lo.y, hi.x, hi.y};
+}
+__device__ __forceinline__ void lds_st16(uint8_t* p, uint4 v) {
+  *reinterpret_cast<uint2*>(p) = uint2{v.x, v.y};
+  *reinterpret_cast<uint2*>(p + 8) = uint2{v.z, v.w};
+}
+
 // ---------------------------------------------------------------- conversions
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {

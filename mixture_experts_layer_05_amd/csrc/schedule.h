@@ -70,6 +70,22 @@ __device__ __forceinline__ TileInfo find_tile(const int* prefix, int G, int tile
   return t;
 }
 
+// Persistent walk over [0, total): the tiles are cut into 8 contiguous ranges, one
+// per XCD (workgroup b runs on XCD b % 8), and the workgroups of an XCD stride
+// through its range.  Neighbouring tiles share a weight slab, so the m-tiles of a
+// slab run at the same time on one XCD and share its L2, and every XCD gets an
+// equal share whatever the grid size.  gridDim.x must be a multiple of 8.
+struct XcdWalk {
+  int tile, end, step;
+  __device__ __forceinline__ XcdWalk(int total) {
+    const int per = (total + 7) / 8;
+    const int xcd = blockIdx.x % 8;
+    tile = xcd * per + blockIdx.x / 8;
+    end = min(total, xcd * per + per);
+    step = gridDim.x / 8;
+  }
+};
+
 // Token behind row m of a tile (m clamped into the group by the caller).
 __device__ __forceinline__ int row_token(const ExpertArgs& a, const TileInfo& t, int m) {
   return t.shared ? m : a.perm[t.rowbase + m] / a.K;

@@ -27,51 +27,57 @@ namespace moe {
 namespace {
 
 constexpr int kStreamThreads = 256;
-constexpr int kXcdCount = 8;
+constexpr int kXcdCount = 8;   // the tile walk assumes grids that are multiples of 8
 
 enum class SMode { GateUp, Down };
 
-template <SMode MODE, int BM, int BN, bool FP8>
+template <SMode MODE, int BM, int BN, int WM, bool FP8>
 struct StreamCfg {
+  static constexpr int kWM = WM;                               // waves along rows
+  static constexpr int kWN = 4 / WM;                           // waves along weight rows
   static constexpr int kRowData = FP8 ? 128 : 256;            // bytes per row per stage
-  static constexpr int kRowStride = kRowData + 16;            // padded LDS row
+  static constexpr int kRowStride = kRowData + 8;             // padded LDS row (8 mod 16)
   static constexpr int kLanesPerRow = kRowData / 16;
   static constexpr int kRowsPerPass = kStreamThreads / kLanesPerRow;
   static constexpr int kAPasses = (BM + kRowsPerPass - 1) / kRowsPerPass;
   static constexpr int kBPasses = BN / kRowsPerPass;
-  static constexpr int kRM = BM / 16;                          // row blocks
-  static constexpr int kCB = BN / 4 / 16;                      // column blocks per wave
+  static constexpr int kRM = BM / WM / 16;                     // row blocks per wave
+  static constexpr int kCB = BN / kWN / 16;                    // column blocks per wave
   static constexpr int kElems = FP8 ? 128 : 128;               // contraction elements per stage
   static constexpr int kStage = (BM + BN) * kRowStride;
   static constexpr int kOutBytes = MODE == SMode::Down ? BM * (BN + 4) * 4 : 0;
   static constexpr int kSmem = kStage > kOutBytes ? kStage : kOutBytes;
   static_assert(BN % kRowsPerPass == 0, "BN must be a multiple of the rows per pass");
   static_assert(MODE == SMode::Down || kCB % 2 == 0, "gate/up needs gate and up blocks");
+  static_assert(kRM >= 1 && BM % (16 * WM) == 0, "rows per wave must be a multiple of 16");
 };
 
-// Weight row of the LDS B tile read by column block j of wave w (lane row r).
-// Gate/up tiles hold BN/2 gate rows then the BN/2 up rows of the same columns;
-// wave w takes the gate and up rows of intermediate columns [w*BN/8, (w+1)*BN/8).
-template <SMode MODE, int BN, int kCB>
-__device__ __forceinline__ int stream_b_row(int w, int j, int r) {
+// Weight row of the LDS B tile read by column block j of the wave in weight-row
+// column wn of kWN (lane row r).  Gate/up tiles hold BN/2 gate rows then the BN/2
+// up rows of the same intermediate columns; wave column wn takes the gate and up
+// rows of columns [wn*BN/(2*kWN), (wn+1)*BN/(2*kWN)).
+template <SMode MODE, int BN, int kWN, int kCB>
+__device__ __forceinline__ int stream_b_row(int wn, int j, int r) {
   if constexpr (MODE == SMode::GateUp) {
     const int half = kCB / 2;
     const int jh = (j < half) ? j : j - half;
-    return ((j < half) ? 0 : BN / 2) + w * (BN / 8) + 16 * jh + r;
+    return ((j < half) ? 0 : BN / 2) + wn * (BN / (2 * kWN)) + 16 * jh + r;
   } else {
-    return w * (BN / 4) + 16 * j + r;
+    return wn * (BN / kWN) + 16 * j + r;
   }
 }
 
-template <SMode MODE, int BM, int BN, bool FP8>
+template <SMode MODE, int BM, int BN, int WM, bool FP8>
 __global__ void __launch_bounds__(kStreamThreads) stream_expert_kernel(ExpertArgs a) {
-  using C = StreamCfg<MODE, BM, BN, FP8>;
+  using C = StreamCfg<MODE, BM, BN, WM, FP8>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::kSmem];
   __shared__ __attribute__((aligned(16))) float sscale[FP8 ? BM + BN : 4];
   __shared__ int prefix[kMaxExperts + 2];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
+  const int wm = wave / C::kWN, wn = wave % C::kWN;
+  const int wrow0 = wm * (BM / WM);   // first tile row of this wave
 
   const bool has_shared = a.S > 0;
   const int G = a.E + (has_shared ? 1 : 0);
@@ -81,15 +87,12 @@ __global__ void __launch_bounds__(kStreamThreads) stream_expert_kernel(ExpertArg
   const int nt_s = has_shared ? ((MODE == SMode::GateUp) ? a.S / bn_cols : H / bn_cols) : 0;
   const int total = build_tile_prefix(prefix, a.counts, a.E, a.T, has_shared, BM, nt_r, nt_s);
 
-  // Workgroup b runs on XCD b % 8: consecutive tiles (same weight slab, next m-tile)
-  // go to the same XCD.
-  const int per_xcd = gridDim.x / kXcdCount;
-  const int first = (blockIdx.x % kXcdCount) * per_xcd + blockIdx.x / kXcdCount;
 
   const int lrow = tid / C::kLanesPerRow;            // row inside a load pass
   const int lcol = (tid % C::kLanesPerRow) * 16;     // byte offset inside the stage slice
 
-  for (int tile = first; tile < total; tile += gridDim.x) {
+  const XcdWalk walk(total);
+  for (int tile = walk.tile; tile < walk.end; tile += walk.step) {
     const TileInfo t = find_tile(prefix, G, tile, a, BM);
     const int kdim = (MODE == SMode::GateUp) ? H : (t.shared ? a.S : a.I);
     const int nk = kdim / C::kElems;
@@ -107,7 +110,9 @@ __global__ void __launch_bounds__(kStreamThreads) stream_expert_kernel(ExpertArg
 #pragma unroll
     for (int q = 0; q < C::kAPasses; ++q) {
       const int row = lrow + q * C::kRowsPerPass;
-      aload[q] = row < BM;
+      // Rows past the group's end are not loaded: their LDS rows keep stale data,
+      // which only reaches output rows that are never written.
+      aload[q] = row < BM && t.m0 + row < t.rows;
       const int m = min(t.m0 + min(row, BM - 1), t.rows - 1);
       if constexpr (MODE == SMode::GateUp)
         asrc[q] = (FP8 ? a.xq : static_cast<const uint8_t*>(a.x)) +
@@ -180,10 +185,10 @@ __global__ void __launch_bounds__(kStreamThreads) stream_expert_kernel(ExpertArg
 #pragma unroll
       for (int q = 0; q < C::kAPasses; ++q)
         if (aload[q])
-          *reinterpret_cast<uint4*>(smem + (lrow + q * C::kRowsPerPass) * C::kRowStride + lcol) = R.a[q];
+          lds_st16(smem + (lrow + q * C::kRowsPerPass) * C::kRowStride + lcol, R.a[q]);
 #pragma unroll
       for (int q = 0; q < C::kBPasses; ++q)
-        *reinterpret_cast<uint4*>(smem + (BM + lrow + q * C::kRowsPerPass) * C::kRowStride + lcol) = R.b[q];
+        lds_st16(smem + (BM + lrow + q * C::kRowsPerPass) * C::kRowStride + lcol, R.b[q]);
       if constexpr (FP8) {
         if (tid < BM + BN) sscale[tid] = R.s;
       }
@@ -196,7 +201,7 @@ __global__ void __launch_bounds__(kStreamThreads) stream_expert_kernel(ExpertArg
       for (int j = 0; j < C::kCB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&]() {
-      const uint8_t* As = smem + r * C::kRowStride;
+      const uint8_t* As = smem + (wrow0 + r) * C::kRowStride;
       const uint8_t* Bs = smem + BM * C::kRowStride;
       if constexpr (!FP8) {
 #pragma unroll
@@ -204,11 +209,11 @@ __global__ void __launch_bounds__(kStreamThreads) stream_expert_kernel(ExpertArg
           uint4 af[C::kRM], bf[C::kCB];
 #pragma unroll
           for (int i = 0; i < C::kRM; ++i)
-            af[i] = *reinterpret_cast<const uint4*>(As + 16 * i * C::kRowStride + 64 * s + 16 * g);
+            af[i] = lds_ld16(As + 16 * i * C::kRowStride + 64 * s + 16 * g);
 #pragma unroll
           for (int j = 0; j < C::kCB; ++j)
-            bf[j] = *reinterpret_cast<const uint4*>(
-                Bs + stream_b_row<MODE, BN, C::kCB>(wave, j, r) * C::kRowStride + 64 * s + 16 * g);
+            bf[j] = lds_ld16(
+                Bs + stream_b_row<MODE, BN, C::kWN, C::kCB>(wn, j, r) * C::kRowStride + 64 * s + 16 * g);
 #pragma unroll
           for (int i = 0; i < C::kRM; ++i)
 #pragma unroll
@@ -222,17 +227,17 @@ __global__ void __launch_bounds__(kStreamThreads) stream_expert_kernel(ExpertArg
 #pragma unroll
         for (int i = 0; i < C::kRM; ++i) {
           const uint8_t* p = As + 16 * i * C::kRowStride;
-          const uint4 lo = *reinterpret_cast<const uint4*>(p + 16 * g);
-          const uint4 hi = *reinterpret_cast<const uint4*>(p + 64 + 16 * g);
+          const uint4 lo = lds_ld16(p + 16 * g);
+          const uint4 hi = lds_ld16(p + 64 + 16 * g);
           af[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-          sa[i] = *reinterpret_cast<const f32x4*>(&sscale[16 * i + 4 * g]);
+          sa[i] = *reinterpret_cast<const f32x4*>(&sscale[wrow0 + 16 * i + 4 * g]);
         }
 #pragma unroll
         for (int j = 0; j < C::kCB; ++j) {
-          const int br = stream_b_row<MODE, BN, C::kCB>(wave, j, r);
+          const int br = stream_b_row<MODE, BN, C::kWN, C::kCB>(wn, j, r);
           const uint8_t* p = Bs + br * C::kRowStride;
-          const uint4 lo = *reinterpret_cast<const uint4*>(p + 16 * g);
-          const uint4 hi = *reinterpret_cast<const uint4*>(p + 64 + 16 * g);
+          const uint4 lo = lds_ld16(p + 16 * g);
+          const uint4 hi = lds_ld16(p + 64 + 16 * g);
           bf[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
           sb[j] = sscale[BM + br];
         }
@@ -273,10 +278,10 @@ __global__ void __launch_bounds__(kStreamThreads) stream_expert_kernel(ExpertArg
       for (int i = 0; i < C::kRM; ++i)
 #pragma unroll
         for (int jh = 0; jh < C::kCB / 2; ++jh) {
-          const int col = n0 + wave * (BN / 8) + 16 * jh + r;
+          const int col = n0 + wn * (BN / (2 * C::kWN)) + 16 * jh + r;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int m = t.m0 + 16 * i + 4 * g + e;
+            const int m = t.m0 + wrow0 + 16 * i + 4 * g + e;
             if (m < t.rows) {
               const float hv = silu_f32(acc[i][jh][e]) * acc[i][jh + C::kCB / 2][e];
               const size_t idx = t.shared ? a.h_shared + static_cast<size_t>(m) * width + col
@@ -298,7 +303,7 @@ __global__ void __launch_bounds__(kStreamThreads) stream_expert_kernel(ExpertArg
         for (int j = 0; j < C::kCB; ++j)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            out[(16 * i + 4 * g + e) * ld + wave * (BN / 4) + 16 * j + r] = acc[i][j][e];
+            out[(wrow0 + 16 * i + 4 * g + e) * ld + wn * (BN / C::kWN) + 16 * j + r] = acc[i][j][e];
       __syncthreads();
       for (int q = wave; q < BM; q += 4) {
         const int m = t.m0 + q;
@@ -320,36 +325,44 @@ int stream_grid(const ExpertArgs& a, int BM, int nt_routed, int nt_shared, int p
   return static_cast<int>(std::max<int64_t>(kXcdCount, ceil_div(b, kXcdCount) * kXcdCount));
 }
 
-template <SMode MODE, int BM, bool FP8>
+template <SMode MODE, int BM, int BN, int WM, bool FP8>
 hipError_t launch_stream(const ExpertArgs& a, hipStream_t stream) {
-  constexpr int BN = 128;
   const int bn_cols = (MODE == SMode::GateUp) ? BN / 2 : BN;
   const int nt_r = (MODE == SMode::GateUp) ? a.I / bn_cols : a.H / bn_cols;
   const int nt_s = (MODE == SMode::GateUp) ? a.S / bn_cols : a.H / bn_cols;
-  const int grid = stream_grid(a, BM, nt_r, nt_s, 3);
-  stream_expert_kernel<MODE, BM, BN, FP8><<<grid, kStreamThreads, 0, stream>>>(a);
+  const int grid = stream_grid(a, BM, nt_r, nt_s, 4);
+  stream_expert_kernel<MODE, BM, BN, WM, FP8><<<grid, kStreamThreads, 0, stream>>>(a);
   return hipGetLastError();
+}
+
+// Tile shape from the average rows per expert rho = T*K/E: 16-row tiles up to 12
+// rows, 32 up to 24, 64 above.  Tiles of 32 or 64 rows use 64 weight rows split
+// over 2 waves (the other 2 waves split the rows) when 128-row tiles would leave
+// fewer than ~3 tiles per CU, so that every CU streams from several workgroups.
+template <SMode MODE, bool FP8>
+hipError_t launch_stream_rho(const ExpertArgs& a, int64_t rho, hipStream_t stream) {
+  const int64_t slots = static_cast<int64_t>(a.T) * a.K;
+  const int64_t touched = std::min<int64_t>(a.E, slots);
+  const int64_t n_out = (MODE == SMode::GateUp) ? a.I : a.H;
+  const int64_t tiles128 = touched * (MODE == SMode::GateUp ? n_out / 64 : n_out / 128);
+  const bool narrow = tiles128 < 3 * 256;
+  if (rho <= 12) return launch_stream<MODE, 16, 128, 1, FP8>(a, stream);
+  if (rho <= 24) return narrow ? launch_stream<MODE, 32, 64, 2, FP8>(a, stream)
+                               : launch_stream<MODE, 32, 128, 1, FP8>(a, stream);
+  return narrow ? launch_stream<MODE, 64, 64, 2, FP8>(a, stream)
+                : launch_stream<MODE, 64, 128, 1, FP8>(a, stream);
 }
 
 }  // namespace
 
-// Row tile height from the average rows per expert rho = T*K/E.
 hipError_t launch_gate_up_stream(const ExpertArgs& a, bool fp8, int64_t rho, hipStream_t stream) {
-  if (rho <= 12) return fp8 ? launch_stream<SMode::GateUp, 16, true>(a, stream)
-                            : launch_stream<SMode::GateUp, 16, false>(a, stream);
-  if (rho <= 24) return fp8 ? launch_stream<SMode::GateUp, 32, true>(a, stream)
-                            : launch_stream<SMode::GateUp, 32, false>(a, stream);
-  return fp8 ? launch_stream<SMode::GateUp, 64, true>(a, stream)
-             : launch_stream<SMode::GateUp, 64, false>(a, stream);
+  return fp8 ? launch_stream_rho<SMode::GateUp, true>(a, rho, stream)
+             : launch_stream_rho<SMode::GateUp, false>(a, rho, stream);
 }
 
 hipError_t launch_down_stream(const ExpertArgs& a, bool fp8, int64_t rho, hipStream_t stream) {
-  if (rho <= 12) return fp8 ? launch_stream<SMode::Down, 16, true>(a, stream)
-                            : launch_stream<SMode::Down, 16, false>(a, stream);
-  if (rho <= 24) return fp8 ? launch_stream<SMode::Down, 32, true>(a, stream)
-                            : launch_stream<SMode::Down, 32, false>(a, stream);
-  return fp8 ? launch_stream<SMode::Down, 64, true>(a, stream)
-             : launch_stream<SMode::Down, 64, false>(a, stream);
+  return fp8 ? launch_stream_rho<SMode::Down, true>(a, rho, stream)
+             : launch_stream_rho<SMode::Down, false>(a, rho, stream);
 }
 
 }  // namespace moe

@@ -12,8 +12,8 @@
 //     128-element fp8 scale group).  Each stage of A (token rows, gathered
 //     through the dispatch permutation) and B (weight rows) is loaded with
 //     16-byte coalesced loads into registers one stage ahead, then written to a
-//     double-buffered LDS tile whose rows are padded to 144 bytes so that the
-//     MFMA fragment reads are free of bank conflicts;
+//     double-buffered LDS tile whose rows are padded to 136 bytes (8 mod 16:
+//     the MFMA fragment reads then run at full LDS rate, see common.h);
 //   * each wave computes a 64-row x BN/WGN-column sub-tile with 16x16x32 bf16
 //     MFMAs (two per stage and block pair) or 16x16x128 fp8 MFMAs (one per stage,
 //     rescaled by the row and column group scales staged in LDS);
@@ -27,7 +27,7 @@ namespace moe {
 namespace {
 
 constexpr int kTileThreads = 512;
-constexpr int kRowBytes = 144;   // 128 data bytes + 16 padding bytes per LDS row
+constexpr int kRowBytes = 136;   // 128 data bytes + 8 padding bytes per LDS row
 constexpr int kXcds = 8;
 
 enum class Mode { GateUp, Down };
@@ -77,14 +77,12 @@ __global__ void __launch_bounds__(kTileThreads) tiled_expert_kernel(ExpertArgs a
   const int nt_s = has_shared ? ((MODE == Mode::GateUp) ? a.S / bn_cols : H / bn_cols) : 0;
   const int total = build_tile_prefix(prefix, a.counts, a.E, a.T, has_shared, BM, nt_r, nt_s);
 
-  // Workgroup b runs on XCD b % 8; give each XCD a contiguous run of tiles.
-  const int per_xcd = gridDim.x / kXcds;
-  const int first = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
 
   const int crow = tid >> 3;          // first row this thread loads (then +64, +128, ...)
   const int ccol = (tid & 7) * 16;    // byte offset inside the row's 128-byte stage slice
 
-  for (int tile = first; tile < total; tile += gridDim.x) {
+  const XcdWalk walk(total);
+  for (int tile = walk.tile; tile < walk.end; tile += walk.step) {
     const TileInfo t = find_tile(prefix, G, tile, a, BM);
     const int kdim = (MODE == Mode::GateUp) ? H : (t.shared ? a.S : a.I);
     const int nk = kdim / C::kBK;
@@ -172,10 +170,10 @@ __global__ void __launch_bounds__(kTileThreads) tiled_expert_kernel(ExpertArgs a
       uint8_t* base = smem + buf * C::kStage;
 #pragma unroll
       for (int q = 0; q < C::kAChunks; ++q)
-        *reinterpret_cast<uint4*>(base + (crow + 64 * q) * kRowBytes + ccol) = ra[q];
+        lds_st16(base + (crow + 64 * q) * kRowBytes + ccol, ra[q]);
 #pragma unroll
       for (int q = 0; q < C::kBChunks; ++q)
-        *reinterpret_cast<uint4*>(base + (BM + crow + 64 * q) * kRowBytes + ccol) = rb[q];
+        lds_st16(base + (BM + crow + 64 * q) * kRowBytes + ccol, rb[q]);
       if constexpr (FP8) {
         if (tid < BM + BN) sscale[buf][tid] = rs;
       }
@@ -201,10 +199,10 @@ __global__ void __launch_bounds__(kTileThreads) tiled_expert_kernel(ExpertArgs a
           uint4 af[4], bf[C::kNB];
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            af[i] = *reinterpret_cast<const uint4*>(As + i * 16 * kRowBytes + 64 * s + 16 * g);
+            af[i] = lds_ld16(As + i * 16 * kRowBytes + 64 * s + 16 * g);
 #pragma unroll
           for (int j = 0; j < C::kNB; ++j)
-            bf[j] = *reinterpret_cast<const uint4*>(
+            bf[j] = lds_ld16(
                 Bs + b_tile_row<MODE, BN, C::kWN, C::kNB>(wn, j, r) * kRowBytes + 64 * s + 16 * g);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -218,8 +216,8 @@ __global__ void __launch_bounds__(kTileThreads) tiled_expert_kernel(ExpertArgs a
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint8_t* p = As + i * 16 * kRowBytes;
-          const uint4 lo = *reinterpret_cast<const uint4*>(p + 16 * g);
-          const uint4 hi = *reinterpret_cast<const uint4*>(p + 64 + 16 * g);
+          const uint4 lo = lds_ld16(p + 16 * g);
+          const uint4 hi = lds_ld16(p + 64 + 16 * g);
           af[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
           sa[i] = *reinterpret_cast<const f32x4*>(&sscale[buf][wm * 64 + 16 * i + 4 * g]);
         }
@@ -227,8 +225,8 @@ __global__ void __launch_bounds__(kTileThreads) tiled_expert_kernel(ExpertArgs a
         for (int j = 0; j < C::kNB; ++j) {
           const int br = b_tile_row<MODE, BN, C::kWN, C::kNB>(wn, j, r);
           const uint8_t* p = Bs + br * kRowBytes;
-          const uint4 lo = *reinterpret_cast<const uint4*>(p + 16 * g);
-          const uint4 hi = *reinterpret_cast<const uint4*>(p + 64 + 16 * g);
+          const uint4 lo = lds_ld16(p + 16 * g);
+          const uint4 hi = lds_ld16(p + 64 + 16 * g);
           bf[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
           sb[j] = sscale[buf][BM + br];
         }

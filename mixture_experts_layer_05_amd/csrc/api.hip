@@ -11,6 +11,10 @@ using namespace moe;
 namespace {
 
 constexpr size_t kAlign = 256;
+// From this many tokens the router logits run on the LDS-staged streaming kernel
+// (64-token x 128-column tiles); below it, on 16 x 16 tiles whose waves split H,
+// which spreads the router weights over more workgroups.
+constexpr int32_t kRouterTiledTokens = 256;
 
 bool valid_dtype(int d) { return d == MOE_DTYPE_F32 || d == MOE_DTYPE_BF16 || d == MOE_DTYPE_FP8_E4M3_G128; }
 
@@ -46,7 +50,7 @@ int check_tokens(const moe_config* c, int32_t T) {
 }
 
 struct Layout {
-  size_t z, h, o, xq, xs, hq, hs, total;
+  size_t z, h, o, xq, xs, hq, hs, chunks, ranks, total;
   int ldz;
   size_t h_shared;  // element offset of the shared expert's rows in h
 };
@@ -62,6 +66,8 @@ Layout layout(const moe_config& c, int64_t T) {
   const int E = c.n_routed_experts;
   L.ldz = static_cast<int>(align_up(E + 1, 16));
   L.z = take(static_cast<size_t>(T) * L.ldz * sizeof(float));
+  L.chunks = take(static_cast<size_t>(ceil_div(T, 1024)) * E * sizeof(int32_t));
+  L.ranks = take(static_cast<size_t>(T) * c.num_experts_per_tok * sizeof(int32_t));
   const size_t routed = static_cast<size_t>(T) * c.num_experts_per_tok * c.moe_intermediate_size;
   const size_t elems = routed + static_cast<size_t>(T) * c.shared_expert_intermediate_size;
   L.h_shared = routed;
@@ -190,7 +196,19 @@ int moe_route(const moe_config* cfg, int32_t T, const void* x, const void* w_rou
   const int E = cfg->n_routed_experts, H = cfg->hidden_size, K = cfg->num_experts_per_tok;
   const int ncols = E + (has_shared ? 1 : 0);
   float* z = at<float>(ws, L.z);
-  if (cfg->act_dtype == MOE_DTYPE_BF16) {
+  if (cfg->act_dtype == MOE_DTYPE_BF16 && T >= kRouterTiledTokens) {
+    ExpertArgs r{};
+    r.x = x;
+    r.w_router = w_router;
+    r.w_gcol = has_shared ? w_shared_gate : nullptr;
+    r.z = z;
+    r.ldz = L.ldz;
+    r.ncols = ncols;
+    r.T = T;
+    r.H = H;
+    r.E = E;
+    if ((st = launched(launch_router_stream(r, s)))) return st;
+  } else if (cfg->act_dtype == MOE_DTYPE_BF16) {
     dim3 grid(static_cast<unsigned>(ceil_div(T, 16)), static_cast<unsigned>(ceil_div(ncols, 16)));
     router_logits_bf16_kernel<<<grid, 256, 0, s>>>(
         static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
@@ -224,8 +242,21 @@ int moe_dispatch(const moe_config* cfg, int32_t T, const int32_t* topk_ids, int3
   Layout L;
   if ((st = check_workspace(*cfg, T, ws, ws_bytes, &L))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  dispatch_kernel<<<1, 1024, 0, s>>>(topk_ids, T, cfg->n_routed_experts, cfg->num_experts_per_tok,
-                                     counts, offsets, perm);
+  const int E = cfg->n_routed_experts, K = cfg->num_experts_per_tok;
+  if (T <= 1024) {
+    dispatch_kernel<<<1, 1024, 0, s>>>(topk_ids, T, E, K, counts, offsets, perm);
+    return launched(hipGetLastError());
+  }
+  const int nchunks = static_cast<int>(ceil_div(T, 1024));
+  int32_t* chunk = at<int32_t>(ws, L.chunks);
+  int32_t* ranks = at<int32_t>(ws, L.ranks);
+  dispatch_chunk_kernel<<<nchunks, 1024, 0, s>>>(topk_ids, T, E, K, chunk, ranks);
+  if ((st = launched(hipGetLastError()))) return st;
+  dispatch_scan_kernel<<<1, 1024, 0, s>>>(nchunks, E, chunk, counts, offsets);
+  if ((st = launched(hipGetLastError()))) return st;
+  const int64_t slots = static_cast<int64_t>(T) * K;
+  dispatch_scatter_kernel<<<static_cast<unsigned>(std::min<int64_t>(ceil_div(slots, 256), 4096)), 256, 0, s>>>(
+      topk_ids, T, E, K, chunk, ranks, perm);
   return launched(hipGetLastError());
 }
 

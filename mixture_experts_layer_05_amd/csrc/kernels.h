@@ -35,6 +35,12 @@ struct ExpertArgs {
   const float* hs;               // fp8: scales of h
   float* o;                      // [T*K, H] unweighted routed outputs, row = slot t*K+k
   float* y;                      // [T, H]
+  // Router logits (router mode of the streaming kernel): z[t, c] = x_t . col_c with
+  // col_c = w_router[c] for c < E and col_E = w_gcol (the shared gate) if present.
+  const void* w_router;          // [E, H]
+  const void* w_gcol;            // [H] or null
+  float* z;                      // [T, ldz]
+  int ldz, ncols;
   int T, H, I, S, E, K;
 };
 
@@ -49,6 +55,10 @@ __global__ void budget_kernel(int32_t*, float*, int, int, int, int, int, int32_t
 
 // dispatch.hip
 __global__ void dispatch_kernel(const int32_t*, int, int, int, int32_t*, int32_t*, int32_t*);
+__global__ void dispatch_chunk_kernel(const int32_t*, int, int, int, int32_t*, int32_t*);
+__global__ void dispatch_scan_kernel(int, int, int32_t*, int32_t*, int32_t*);
+__global__ void dispatch_scatter_kernel(const int32_t*, int, int, int, const int32_t*, const int32_t*,
+                                        int32_t*);
 
 // experts.hip: host-side launchers (they pick tile shapes and grid sizes).
 hipError_t launch_gate_up(const ExpertArgs& a, int weight_dtype, hipStream_t stream);
@@ -58,6 +68,7 @@ hipError_t launch_down_tiled(const ExpertArgs& a, bool fp8, bool tall, hipStream
 hipError_t launch_gate_up_stream(const ExpertArgs& a, bool fp8, int64_t rho, hipStream_t stream);
 hipError_t launch_down_stream(const ExpertArgs& a, bool fp8, int64_t rho, hipStream_t stream);
 hipError_t launch_combine(const ExpertArgs& a, hipStream_t stream);
+hipError_t launch_router_stream(const ExpertArgs& a, hipStream_t stream);
 hipError_t launch_quant_x(const ExpertArgs& a, uint8_t* xq, float* xs, hipStream_t stream);
 hipError_t launch_quant_h(const ExpertArgs& a, uint8_t* hq, float* hs, hipStream_t stream);
 

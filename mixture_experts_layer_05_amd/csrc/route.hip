@@ -174,10 +174,11 @@ __global__ void __launch_bounds__(1024) budget_kernel(
   if (tid == 0) { s_union = 0; s_dropped = 0; s_empty = 0; }
   __syncthreads();
   const int nslots = T * K;
+  const bool need_agg = budget > 0;   // without a budget only the union is counted
   for (int s = tid; s < nslots; s += 1024) {
     const int e = ids[s];
     if (e >= 0) {
-      atomicAdd(&agg[wave][e], static_cast<double>(w[s]));
+      if (need_agg) atomicAdd(&agg[wave][e], static_cast<double>(w[s]));
       present[e] = 1;
     }
   }

@@ -29,7 +29,9 @@ namespace {
 constexpr int kStreamThreads = 256;
 constexpr int kXcdCount = 8;   // the tile walk assumes grids that are multiples of 8
 
-enum class SMode { GateUp, Down };
+// GateUp: h = SwiGLU(x W_gate^T, x W_up^T); Down: o / y = h W_down^T; Router: the
+// router logits z = x [W_r; w_g]^T over all T tokens (one group of T rows).
+enum class SMode { GateUp, Down, Router };
 
 template <SMode MODE, int BM, int BN, int WM, bool FP8>
 struct StreamCfg {
@@ -83,9 +85,14 @@ __global__ void __launch_bounds__(kStreamThreads) stream_expert_kernel(ExpertArg
   const int G = a.E + (has_shared ? 1 : 0);
   const int H = a.H;
   const int bn_cols = (MODE == SMode::GateUp) ? BN / 2 : BN;
-  const int nt_r = (MODE == SMode::GateUp) ? a.I / bn_cols : H / bn_cols;
-  const int nt_s = has_shared ? ((MODE == SMode::GateUp) ? a.S / bn_cols : H / bn_cols) : 0;
-  const int total = build_tile_prefix(prefix, a.counts, a.E, a.T, has_shared, BM, nt_r, nt_s);
+  int total;
+  if constexpr (MODE == SMode::Router) {
+    total = static_cast<int>(ceil_div(a.T, BM) * ceil_div(a.ncols, BN));
+  } else {
+    const int nt_r = (MODE == SMode::GateUp) ? a.I / bn_cols : H / bn_cols;
+    const int nt_s = has_shared ? ((MODE == SMode::GateUp) ? a.S / bn_cols : H / bn_cols) : 0;
+    total = build_tile_prefix(prefix, a.counts, a.E, a.T, has_shared, BM, nt_r, nt_s);
+  }
 
 
   const int lrow = tid / C::kLanesPerRow;            // row inside a load pass
@@ -93,8 +100,20 @@ __global__ void __launch_bounds__(kStreamThreads) stream_expert_kernel(ExpertArg
 
   const XcdWalk walk(total);
   for (int tile = walk.tile; tile < walk.end; tile += walk.step) {
-    const TileInfo t = find_tile(prefix, G, tile, a, BM);
-    const int kdim = (MODE == SMode::GateUp) ? H : (t.shared ? a.S : a.I);
+    TileInfo t;
+    if constexpr (MODE == SMode::Router) {
+      // One group of T rows read straight from x (the shared-expert row rule).
+      const int mt = static_cast<int>(ceil_div(a.T, BM));
+      t.group = 0;
+      t.shared = true;
+      t.rows = a.T;
+      t.rowbase = 0;
+      t.m0 = (tile % mt) * BM;
+      t.nt = tile / mt;
+    } else {
+      t = find_tile(prefix, G, tile, a, BM);
+    }
+    const int kdim = (MODE != SMode::Down) ? H : (t.shared ? a.S : a.I);
     const int nk = kdim / C::kElems;
     const int n0 = t.nt * bn_cols;
     const size_t esz = FP8 ? 1 : 2;
@@ -114,7 +133,7 @@ __global__ void __launch_bounds__(kStreamThreads) stream_expert_kernel(ExpertArg
       // which only reaches output rows that are never written.
       aload[q] = row < BM && t.m0 + row < t.rows;
       const int m = min(t.m0 + min(row, BM - 1), t.rows - 1);
-      if constexpr (MODE == SMode::GateUp)
+      if constexpr (MODE != SMode::Down)
         asrc[q] = (FP8 ? a.xq : static_cast<const uint8_t*>(a.x)) +
                   static_cast<size_t>(row_token(a, t, m)) * H * esz;
       else
@@ -135,6 +154,8 @@ __global__ void __launch_bounds__(kStreamThreads) stream_expert_kernel(ExpertArg
         sw0 = t.shared ? a.ss_gate : a.s_gate + static_cast<size_t>(t.group) * a.I * ng;
         sw1 = t.shared ? a.ss_up : a.s_up + static_cast<size_t>(t.group) * a.I * ng;
       }
+    } else if constexpr (MODE == SMode::Router) {
+      w0 = static_cast<const uint8_t*>(a.w_router);
     } else {
       w0 = static_cast<const uint8_t*>(t.shared ? a.ws_down : a.w_down);
       if (!t.shared) w0 += static_cast<size_t>(t.group) * H * a.I * esz;
@@ -144,11 +165,18 @@ __global__ void __launch_bounds__(kStreamThreads) stream_expert_kernel(ExpertArg
 #pragma unroll
     for (int q = 0; q < C::kBPasses; ++q) {
       const int br = lrow + q * C::kRowsPerPass;
-      if constexpr (MODE == SMode::GateUp)
+      if constexpr (MODE == SMode::GateUp) {
         bsrc[q] = (br < BN / 2) ? w0 + static_cast<size_t>(n0 + br) * kdim * esz
                                 : w1 + static_cast<size_t>(n0 + br - BN / 2) * kdim * esz;
-      else
+      } else if constexpr (MODE == SMode::Router) {
+        // Column c < E: router row c; c == E: the shared gate vector; columns past
+        // the last one re-read a valid row and are never stored.
+        const int c = min(n0 + br, a.ncols - 1);
+        bsrc[q] = (c < a.E) ? w0 + static_cast<size_t>(c) * kdim * esz
+                            : static_cast<const uint8_t*>(a.w_gcol);
+      } else {
         bsrc[q] = w0 + static_cast<size_t>(n0 + br) * kdim * esz;
+      }
     }
     const float* sptr = nullptr;
     if constexpr (FP8) {
@@ -272,7 +300,19 @@ __global__ void __launch_bounds__(kStreamThreads) stream_expert_kernel(ExpertArg
     }
 
     // ---- epilogue
-    if constexpr (MODE == SMode::GateUp) {
+    if constexpr (MODE == SMode::Router) {
+#pragma unroll
+      for (int i = 0; i < C::kRM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kCB; ++j) {
+          const int col = n0 + wn * (BN / C::kWN) + 16 * j + r;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int m = t.m0 + wrow0 + 16 * i + 4 * g + e;
+            if (m < t.rows && col < a.ncols) a.z[static_cast<size_t>(m) * a.ldz + col] = acc[i][j][e];
+          }
+        }
+    } else if constexpr (MODE == SMode::GateUp) {
       const int width = t.shared ? a.S : a.I;
 #pragma unroll
       for (int i = 0; i < C::kRM; ++i)
@@ -354,6 +394,14 @@ hipError_t launch_stream_rho(const ExpertArgs& a, int64_t rho, hipStream_t strea
 }
 
 }  // namespace
+
+hipError_t launch_router_stream(const ExpertArgs& a, hipStream_t stream) {
+  const int64_t tiles = ceil_div(a.T, 64) * ceil_div(a.ncols, 128);
+  const int grid = static_cast<int>(std::max<int64_t>(
+      kXcdCount, ceil_div(std::min<int64_t>(tiles, 256LL * 4), kXcdCount) * kXcdCount));
+  stream_expert_kernel<SMode::Router, 64, 128, 1, false><<<grid, kStreamThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
 
 hipError_t launch_gate_up_stream(const ExpertArgs& a, bool fp8, int64_t rho, hipStream_t stream) {
   return fp8 ? launch_stream_rho<SMode::GateUp, true>(a, rho, stream)

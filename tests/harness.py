@@ -22,7 +22,11 @@ TOPK_MARGIN = 1e-3
 BUDGET_MARGIN = 1e-4
 
 TOL = {"f32": 1e-5, "bf16": 2e-3, "fp8_e4m3_g128": 1e-2}   # relative L2 of y
-W_TOL = 1e-6                                                   # routing weights, absolute
+# Routing weights, absolute.  The pages fix no tolerance here; the bound comes from
+# the arithmetic: the logits are float32 sums of H <= 7168 bf16 products with
+# |z| = O(1), whose rounding (random-walk ~ sqrt(H) * 2^-24 * |partial sums|) is a
+# few 1e-6, and a renormalised softmax weight moves by at most about that much.
+W_TOL = 1e-5
 
 
 @dataclasses.dataclass

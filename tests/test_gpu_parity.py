@@ -1,7 +1,7 @@
 """GPU parity: the HIP library through its C ABI vs the CPU oracle.
 
 Ids, counts, offsets, the permutation and the budget statistics must match
-bit-exactly; routing weights within 1e-6; y within the relative-L2 bar of its
+bit-exactly; routing weights within 1e-5; y within the relative-L2 bar of its
 weight dtype (fp32 1e-5, bf16 2e-3, fp8 1e-2).  Sizes the oracle finishes in
 seconds are compared on every token; the full-size workloads on sampled tokens.
 """

@@ -3,7 +3,7 @@
 // read back to the host.
 #include <algorithm>
 
-#include "../../include/moe_mi355x.h"
+#include "moe_mi355x.h"
 #include "kernels.h"
 
 using namespace moe;
@@ -14,7 +14,7 @@ constexpr size_t kAlign = 256;
 // From this many tokens the router logits run on the LDS-staged streaming kernel
 // (64-token x 128-column tiles); below it, on 16 x 16 tiles whose waves split H,
 // which spreads the router weights over more workgroups.
-constexpr int32_t kRouterTiledTokens = 256;
+constexpr int32_t kRouterTiledTokens = 4096;
 
 bool valid_dtype(int d) { return d == MOE_DTYPE_F32 || d == MOE_DTYPE_BF16 || d == MOE_DTYPE_FP8_E4M3_G128; }
 

@@ -25,10 +25,10 @@ namespace {
 
 // Tile of 16 rows x 16 columns, one output per thread of a 256-thread block.
 __global__ void __launch_bounds__(256) gate_up_f32_kernel(ExpertArgs a) {
-  __shared__ int prefix[kMaxExperts + 2];
+  __shared__ int prefix[kSchedInts];
   const bool has_shared = a.S > 0;
   const int G = a.E + (has_shared ? 1 : 0);
-  const int total = build_tile_prefix(prefix, a.counts, a.E, a.T, has_shared, 16, (a.I + 15) / 16,
+  const int total = build_tile_prefix(prefix, a.counts, a.offsets, a.E, a.T, has_shared, 16, (a.I + 15) / 16,
                                       has_shared ? (a.S + 15) / 16 : 0);
   const int H = a.H;
   const float* x = static_cast<const float*>(a.x);
@@ -59,11 +59,11 @@ __global__ void __launch_bounds__(256) gate_up_f32_kernel(ExpertArgs a) {
 }
 
 __global__ void __launch_bounds__(256) down_f32_kernel(ExpertArgs a) {
-  __shared__ int prefix[kMaxExperts + 2];
+  __shared__ int prefix[kSchedInts];
   const bool has_shared = a.S > 0;
   const int G = a.E + (has_shared ? 1 : 0);
   const int H = a.H;
-  const int total = build_tile_prefix(prefix, a.counts, a.E, a.T, has_shared, 16, (H + 15) / 16,
+  const int total = build_tile_prefix(prefix, a.counts, a.offsets, a.E, a.T, has_shared, 16, (H + 15) / 16,
                                       has_shared ? (H + 15) / 16 : 0);
   const float* hb = static_cast<const float*>(a.h);
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {

@@ -13,11 +13,19 @@ namespace {
 
 constexpr int kDtypeF32 = 0, kDtypeBf16 = 1, kDtypeFp8 = 2;
 
-// prefix[g+1] - prefix[g] = ceil(rows_g / BM) * ntiles_g for g in [0, G), where
-// group E (if has_shared) is the shared expert with T rows.  Wave 0 scans.
-__device__ int build_tile_prefix(int* prefix, const int32_t* counts, int E, int T, bool has_shared,
-                                 int BM, int nt_routed, int nt_shared) {
+// The schedule lives in LDS: prefix[0..G] of per-group tile counts, then each
+// group's row count and first dispatch row, so that finding a tile's group reads no
+// global memory.  prefix[g+1] - prefix[g] = ceil(rows_g / BM) * ntiles_g for g in
+// [0, G), where group E (if has_shared) is the shared expert with T rows.
+constexpr int kSchedStride = kMaxExperts + 2;
+constexpr int kSchedInts = 3 * kSchedStride;
+
+__device__ int build_tile_prefix(int* sched, const int32_t* counts, const int32_t* offsets, int E, int T,
+                                 bool has_shared, int BM, int nt_routed, int nt_shared) {
   const int G = E + (has_shared ? 1 : 0);
+  int* prefix = sched;
+  int* rows_of = sched + kSchedStride;
+  int* base_of = sched + 2 * kSchedStride;
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
     int carry = 0;
@@ -26,6 +34,8 @@ __device__ int build_tile_prefix(int* prefix, const int32_t* counts, int E, int 
       int v = 0;
       if (g < G) {
         const int rows = (g < E) ? counts[g] : T;
+        rows_of[g] = rows;
+        base_of[g] = (g < E) ? offsets[g] : 0;
         v = static_cast<int>(ceil_div(rows, BM)) * ((g < E) ? nt_routed : nt_shared);
       }
 #pragma unroll
@@ -51,8 +61,15 @@ struct TileInfo {
   int nt;      // n-tile index
 };
 
-__device__ __forceinline__ TileInfo find_tile(const int* prefix, int G, int tile, const ExpertArgs& a,
-                                              int BM) {
+// Tile order inside a group: bands of `band` m-tiles; within a band the n-tiles are
+// walked in order and, for each n-tile, the band's m-tiles are consecutive.  A run
+// of consecutive tiles (the ones an XCD works on at once) then covers a few weight
+// slabs x a few row blocks, so both operands are reused from that XCD's L2 instead
+// of one operand being re-fetched for every tile.  band >= m-tiles gives plain
+// m-fastest order.
+__device__ __forceinline__ TileInfo find_tile(const int* sched, int G, int tile, const ExpertArgs& a,
+                                              int BM, int band = 1 << 30) {
+  const int* prefix = sched;
   int lo = 0, hi = G;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -61,12 +78,22 @@ __device__ __forceinline__ TileInfo find_tile(const int* prefix, int G, int tile
   TileInfo t;
   t.group = lo;
   t.shared = lo == a.E;
-  t.rows = t.shared ? a.T : a.counts[lo];
-  t.rowbase = t.shared ? 0 : a.offsets[lo];
+  t.rows = sched[kSchedStride + lo];
+  t.rowbase = sched[2 * kSchedStride + lo];
   const int mt = static_cast<int>(ceil_div(t.rows, BM));
   const int local = tile - prefix[lo];
-  t.nt = local / mt;
-  t.m0 = (local % mt) * BM;
+  if (band >= mt) {
+    t.nt = local / mt;
+    t.m0 = (local % mt) * BM;
+    return t;
+  }
+  const int ntile = (prefix[lo + 1] - prefix[lo]) / mt;
+  const int per_band = band * ntile;
+  const int first_m = (local / per_band) * band;
+  const int bm = min(mt - first_m, band);
+  const int in_band = local - (first_m / band) * per_band;
+  t.nt = in_band / bm;
+  t.m0 = (first_m + in_band % bm) * BM;
   return t;
 }
 

@@ -74,7 +74,7 @@ __global__ void __launch_bounds__(kStreamThreads) stream_expert_kernel(ExpertArg
   using C = StreamCfg<MODE, BM, BN, WM, FP8>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::kSmem];
   __shared__ __attribute__((aligned(16))) float sscale[FP8 ? BM + BN : 4];
-  __shared__ int prefix[kMaxExperts + 2];
+  __shared__ int prefix[kSchedInts];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
@@ -91,53 +91,69 @@ __global__ void __launch_bounds__(kStreamThreads) stream_expert_kernel(ExpertArg
   } else {
     const int nt_r = (MODE == SMode::GateUp) ? a.I / bn_cols : H / bn_cols;
     const int nt_s = has_shared ? ((MODE == SMode::GateUp) ? a.S / bn_cols : H / bn_cols) : 0;
-    total = build_tile_prefix(prefix, a.counts, a.E, a.T, has_shared, BM, nt_r, nt_s);
+    total = build_tile_prefix(prefix, a.counts, a.offsets, a.E, a.T, has_shared, BM, nt_r, nt_s);
   }
-
+  const XcdWalk walk(total);
+  if (walk.tile >= walk.end) return;   // uniform across the workgroup
 
   const int lrow = tid / C::kLanesPerRow;            // row inside a load pass
   const int lcol = (tid % C::kLanesPerRow) * 16;     // byte offset inside the stage slice
+  const size_t esz = FP8 ? 1 : 2;
 
-  const XcdWalk walk(total);
-  for (int tile = walk.tile; tile < walk.end; tile += walk.step) {
+  // ---- tile geometry
+  struct Tile {
     TileInfo t;
+    int kdim, nk, n0;
+  };
+  auto make_tile = [&](int tile) {
+    Tile d;
     if constexpr (MODE == SMode::Router) {
       // One group of T rows read straight from x (the shared-expert row rule).
       const int mt = static_cast<int>(ceil_div(a.T, BM));
-      t.group = 0;
-      t.shared = true;
-      t.rows = a.T;
-      t.rowbase = 0;
-      t.m0 = (tile % mt) * BM;
-      t.nt = tile / mt;
+      d.t.group = 0;
+      d.t.shared = true;
+      d.t.rows = a.T;
+      d.t.rowbase = 0;
+      d.t.m0 = (tile % mt) * BM;
+      d.t.nt = tile / mt;
     } else {
-      t = find_tile(prefix, G, tile, a, BM);
+      d.t = find_tile(prefix, G, tile, a, BM);
     }
-    const int kdim = (MODE != SMode::Down) ? H : (t.shared ? a.S : a.I);
-    const int nk = kdim / C::kElems;
-    const int n0 = t.nt * bn_cols;
-    const size_t esz = FP8 ? 1 : 2;
-    const int ng = kdim / kGroup;
-    auto hrow = [&](int m) -> size_t {
-      return t.shared ? a.h_shared + static_cast<size_t>(m) * kdim
-                      : static_cast<size_t>(t.rowbase + m) * kdim;
-    };
+    d.kdim = (MODE != SMode::Down) ? H : (d.t.shared ? a.S : a.I);
+    d.nk = d.kdim / C::kElems;
+    d.n0 = d.t.nt * bn_cols;
+    return d;
+  };
+  auto hrow = [&](const Tile& d, int m) -> size_t {   // element offset of row m in h / hq
+    return d.t.shared ? a.h_shared + static_cast<size_t>(m) * d.kdim
+                      : static_cast<size_t>(d.t.rowbase + m) * d.kdim;
+  };
+  // Rows past the group's end are not loaded: their LDS rows keep stale data, which
+  // only reaches output rows that are never written.
+  auto a_live = [&](const Tile& d, int q) {
+    const int row = lrow + q * C::kRowsPerPass;
+    return row < BM && d.t.m0 + row < d.t.rows;
+  };
 
-    // ---- sources of this thread's 16-byte pieces
-    const uint8_t* asrc[C::kAPasses];
-    bool aload[C::kAPasses];
+  // ---- sources of this thread's 16-byte pieces for one tile
+  struct Src {
+    const uint8_t* a[C::kAPasses];
+    const uint8_t* b[C::kBPasses];
+    const float* s;
+  };
+  auto make_src = [&](const Tile& d) {
+    Src S;
+    const TileInfo& t = d.t;
+    const int ng = d.kdim / kGroup;
 #pragma unroll
     for (int q = 0; q < C::kAPasses; ++q) {
       const int row = lrow + q * C::kRowsPerPass;
-      // Rows past the group's end are not loaded: their LDS rows keep stale data,
-      // which only reaches output rows that are never written.
-      aload[q] = row < BM && t.m0 + row < t.rows;
       const int m = min(t.m0 + min(row, BM - 1), t.rows - 1);
       if constexpr (MODE != SMode::Down)
-        asrc[q] = (FP8 ? a.xq : static_cast<const uint8_t*>(a.x)) +
-                  static_cast<size_t>(row_token(a, t, m)) * H * esz;
+        S.a[q] = (FP8 ? a.xq : static_cast<const uint8_t*>(a.x)) +
+                 static_cast<size_t>(row_token(a, t, m)) * H * esz;
       else
-        asrc[q] = (FP8 ? a.hq : static_cast<const uint8_t*>(a.h)) + hrow(m) * esz;
+        S.a[q] = (FP8 ? a.hq : static_cast<const uint8_t*>(a.h)) + hrow(d, m) * esz;
     }
     const uint8_t* w0;
     const uint8_t* w1 = nullptr;
@@ -161,151 +177,138 @@ __global__ void __launch_bounds__(kStreamThreads) stream_expert_kernel(ExpertArg
       if (!t.shared) w0 += static_cast<size_t>(t.group) * H * a.I * esz;
       if constexpr (FP8) sw0 = t.shared ? a.ss_down : a.s_down + static_cast<size_t>(t.group) * H * ng;
     }
-    const uint8_t* bsrc[C::kBPasses];
 #pragma unroll
     for (int q = 0; q < C::kBPasses; ++q) {
       const int br = lrow + q * C::kRowsPerPass;
       if constexpr (MODE == SMode::GateUp) {
-        bsrc[q] = (br < BN / 2) ? w0 + static_cast<size_t>(n0 + br) * kdim * esz
-                                : w1 + static_cast<size_t>(n0 + br - BN / 2) * kdim * esz;
+        S.b[q] = (br < BN / 2) ? w0 + static_cast<size_t>(d.n0 + br) * d.kdim * esz
+                               : w1 + static_cast<size_t>(d.n0 + br - BN / 2) * d.kdim * esz;
       } else if constexpr (MODE == SMode::Router) {
         // Column c < E: router row c; c == E: the shared gate vector; columns past
         // the last one re-read a valid row and are never stored.
-        const int c = min(n0 + br, a.ncols - 1);
-        bsrc[q] = (c < a.E) ? w0 + static_cast<size_t>(c) * kdim * esz
-                            : static_cast<const uint8_t*>(a.w_gcol);
+        const int c = min(d.n0 + br, a.ncols - 1);
+        S.b[q] = (c < a.E) ? w0 + static_cast<size_t>(c) * d.kdim * esz
+                           : static_cast<const uint8_t*>(a.w_gcol);
       } else {
-        bsrc[q] = w0 + static_cast<size_t>(n0 + br) * kdim * esz;
+        S.b[q] = w0 + static_cast<size_t>(d.n0 + br) * d.kdim * esz;
       }
     }
-    const float* sptr = nullptr;
+    S.s = nullptr;
     if constexpr (FP8) {
+      // Thread tid < BM stages the scale of tile row tid, BM <= tid < BM+BN that of
+      // B row tid-BM.
       if (tid < BM) {
         const int m = min(t.m0 + tid, t.rows - 1);
-        if constexpr (MODE == SMode::GateUp) sptr = a.xs + static_cast<size_t>(row_token(a, t, m)) * ng;
-        else sptr = a.hs + hrow(m) / kGroup;
+        if constexpr (MODE == SMode::GateUp) S.s = a.xs + static_cast<size_t>(row_token(a, t, m)) * ng;
+        else S.s = a.hs + hrow(d, m) / kGroup;
       } else if (tid < BM + BN) {
         const int br = tid - BM;
         if constexpr (MODE == SMode::GateUp)
-          sptr = (br < BN / 2) ? sw0 + static_cast<size_t>(n0 + br) * ng
-                               : sw1 + static_cast<size_t>(n0 + br - BN / 2) * ng;
+          S.s = (br < BN / 2) ? sw0 + static_cast<size_t>(d.n0 + br) * ng
+                              : sw1 + static_cast<size_t>(d.n0 + br - BN / 2) * ng;
         else
-          sptr = sw0 + static_cast<size_t>(n0 + br) * ng;
+          S.s = sw0 + static_cast<size_t>(d.n0 + br) * ng;
       }
     }
+    return S;
+  };
 
-    struct Regs {
-      uint4 a[C::kAPasses], b[C::kBPasses];
-      float s;
-    };
-    auto gload = [&](Regs& R, int ks) {
-      const size_t off = static_cast<size_t>(ks) * C::kRowData + lcol;
+  struct Regs {
+    uint4 a[C::kAPasses], b[C::kBPasses];
+    float s;
+  };
+  auto gload = [&](Regs& R, const Tile& d, const Src& S, int ks) {
+    const size_t off = static_cast<size_t>(ks) * C::kRowData + lcol;
 #pragma unroll
-      for (int q = 0; q < C::kBPasses; ++q) R.b[q] = ld16_stream(bsrc[q] + off);
+    for (int q = 0; q < C::kBPasses; ++q) R.b[q] = ld16_stream(S.b[q] + off);
 #pragma unroll
-      for (int q = 0; q < C::kAPasses; ++q)
-        if (aload[q]) R.a[q] = ld16(asrc[q] + off);
-      if constexpr (FP8) {
-        if (sptr) R.s = sptr[ks];
-      }
-    };
-    auto lstore = [&](const Regs& R) {
+    for (int q = 0; q < C::kAPasses; ++q)
+      if (a_live(d, q)) R.a[q] = ld16(S.a[q] + off);
+    if constexpr (FP8) {
+      if (S.s) R.s = S.s[ks];
+    }
+  };
+  auto lstore = [&](const Regs& R, const Tile& d) {
 #pragma unroll
-      for (int q = 0; q < C::kAPasses; ++q)
-        if (aload[q])
-          lds_st16(smem + (lrow + q * C::kRowsPerPass) * C::kRowStride + lcol, R.a[q]);
+    for (int q = 0; q < C::kAPasses; ++q)
+      if (a_live(d, q))
+        lds_st16(smem + (lrow + q * C::kRowsPerPass) * C::kRowStride + lcol, R.a[q]);
 #pragma unroll
-      for (int q = 0; q < C::kBPasses; ++q)
-        lds_st16(smem + (BM + lrow + q * C::kRowsPerPass) * C::kRowStride + lcol, R.b[q]);
-      if constexpr (FP8) {
-        if (tid < BM + BN) sscale[tid] = R.s;
-      }
-    };
+    for (int q = 0; q < C::kBPasses; ++q)
+      lds_st16(smem + (BM + lrow + q * C::kRowsPerPass) * C::kRowStride + lcol, R.b[q]);
+    if constexpr (FP8) {
+      if (tid < BM + BN) sscale[tid] = R.s;
+    }
+  };
 
-    f32x4 acc[C::kRM][C::kCB];
+  f32x4 acc[C::kRM][C::kCB];
+  auto clear_acc = [&]() {
 #pragma unroll
     for (int i = 0; i < C::kRM; ++i)
 #pragma unroll
       for (int j = 0; j < C::kCB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
 
-    auto compute = [&]() {
-      const uint8_t* As = smem + (wrow0 + r) * C::kRowStride;
-      const uint8_t* Bs = smem + BM * C::kRowStride;
-      if constexpr (!FP8) {
+  auto compute = [&]() {
+    const uint8_t* As = smem + (wrow0 + r) * C::kRowStride;
+    const uint8_t* Bs = smem + BM * C::kRowStride;
+    if constexpr (!FP8) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          uint4 af[C::kRM], bf[C::kCB];
+      for (int s = 0; s < 4; ++s) {
+        uint4 af[C::kRM], bf[C::kCB];
 #pragma unroll
-          for (int i = 0; i < C::kRM; ++i)
-            af[i] = lds_ld16(As + 16 * i * C::kRowStride + 64 * s + 16 * g);
+        for (int i = 0; i < C::kRM; ++i) af[i] = lds_ld16(As + 16 * i * C::kRowStride + 64 * s + 16 * g);
 #pragma unroll
-          for (int j = 0; j < C::kCB; ++j)
-            bf[j] = lds_ld16(
-                Bs + stream_b_row<MODE, BN, C::kWN, C::kCB>(wn, j, r) * C::kRowStride + 64 * s + 16 * g);
-#pragma unroll
-          for (int i = 0; i < C::kRM; ++i)
-#pragma unroll
-            for (int j = 0; j < C::kCB; ++j) acc[i][j] = mfma_bf16_16x16x32(af[i], bf[j], acc[i][j]);
-        }
-      } else {
-        // Lane group g holds bytes [16g, +16) and [64+16g, +16) of its row's 128-byte group.
-        i32x8 af[C::kRM], bf[C::kCB];
-        f32x4 sa[C::kRM];
-        float sb[C::kCB];
-#pragma unroll
-        for (int i = 0; i < C::kRM; ++i) {
-          const uint8_t* p = As + 16 * i * C::kRowStride;
-          const uint4 lo = lds_ld16(p + 16 * g);
-          const uint4 hi = lds_ld16(p + 64 + 16 * g);
-          af[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-          sa[i] = *reinterpret_cast<const f32x4*>(&sscale[wrow0 + 16 * i + 4 * g]);
-        }
-#pragma unroll
-        for (int j = 0; j < C::kCB; ++j) {
-          const int br = stream_b_row<MODE, BN, C::kWN, C::kCB>(wn, j, r);
-          const uint8_t* p = Bs + br * C::kRowStride;
-          const uint4 lo = lds_ld16(p + 16 * g);
-          const uint4 hi = lds_ld16(p + 64 + 16 * g);
-          bf[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-          sb[j] = sscale[BM + br];
-        }
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < C::kCB; ++j)
+          bf[j] = lds_ld16(Bs + stream_b_row<MODE, BN, C::kWN, C::kCB>(wn, j, r) * C::kRowStride + 64 * s +
+                           16 * g);
 #pragma unroll
         for (int i = 0; i < C::kRM; ++i)
 #pragma unroll
-          for (int j = 0; j < C::kCB; ++j) {
-            const f32x4 p = mfma_fp8_16x16x128(af[i], bf[j], zero);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(p[e], sa[i][e] * sb[j], acc[i][j][e]);
-          }
+          for (int j = 0; j < C::kCB; ++j) acc[i][j] = mfma_bf16_16x16x32(af[i], bf[j], acc[i][j]);
       }
-    };
-
-    // Two stages in flight in registers (R0 / R1 alternate), one LDS stage consumed.
-    Regs R0, R1;
-    gload(R0, 0);
-    if (nk > 1) gload(R1, 1);
-    for (int ks = 0; ks < nk; ks += 2) {
-      __syncthreads();                   // the previous stage's readers are done
-      lstore(R0);
-      __syncthreads();
-      if (ks + 2 < nk) gload(R0, ks + 2);
-      compute();
-      if (ks + 1 >= nk) break;
-      __syncthreads();
-      lstore(R1);
-      __syncthreads();
-      if (ks + 3 < nk) gload(R1, ks + 3);
-      compute();
+    } else {
+      // Lane group g holds bytes [16g, +16) and [64+16g, +16) of its row's 128-byte group.
+      i32x8 af[C::kRM], bf[C::kCB];
+      f32x4 sa[C::kRM];
+      float sb[C::kCB];
+#pragma unroll
+      for (int i = 0; i < C::kRM; ++i) {
+        const uint8_t* p = As + 16 * i * C::kRowStride;
+        const uint4 lo = lds_ld16(p + 16 * g);
+        const uint4 hi = lds_ld16(p + 64 + 16 * g);
+        af[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        sa[i] = *reinterpret_cast<const f32x4*>(&sscale[wrow0 + 16 * i + 4 * g]);
+      }
+#pragma unroll
+      for (int j = 0; j < C::kCB; ++j) {
+        const int br = stream_b_row<MODE, BN, C::kWN, C::kCB>(wn, j, r);
+        const uint8_t* p = Bs + br * C::kRowStride;
+        const uint4 lo = lds_ld16(p + 16 * g);
+        const uint4 hi = lds_ld16(p + 64 + 16 * g);
+        bf[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        sb[j] = sscale[BM + br];
+      }
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < C::kRM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kCB; ++j) {
+          const f32x4 p = mfma_fp8_16x16x128(af[i], bf[j], zero);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(p[e], sa[i][e] * sb[j], acc[i][j][e]);
+        }
     }
+  };
 
-    // ---- epilogue
+  auto epilogue = [&](const Tile& d) {
+    const TileInfo& t = d.t;
     if constexpr (MODE == SMode::Router) {
 #pragma unroll
       for (int i = 0; i < C::kRM; ++i)
 #pragma unroll
         for (int j = 0; j < C::kCB; ++j) {
-          const int col = n0 + wn * (BN / C::kWN) + 16 * j + r;
+          const int col = d.n0 + wn * (BN / C::kWN) + 16 * j + r;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int m = t.m0 + wrow0 + 16 * i + 4 * g + e;
@@ -318,7 +321,7 @@ __global__ void __launch_bounds__(kStreamThreads) stream_expert_kernel(ExpertArg
       for (int i = 0; i < C::kRM; ++i)
 #pragma unroll
         for (int jh = 0; jh < C::kCB / 2; ++jh) {
-          const int col = n0 + wn * (BN / (2 * C::kWN)) + 16 * jh + r;
+          const int col = d.n0 + wn * (BN / (2 * C::kWN)) + 16 * jh + r;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int m = t.m0 + wrow0 + 16 * i + 4 * g + e;
@@ -332,8 +335,8 @@ __global__ void __launch_bounds__(kStreamThreads) stream_expert_kernel(ExpertArg
           }
         }
     } else {
-      // Stage the BM x BN tile in LDS (the operand tiles are no longer needed),
-      // then each wave adds whole BN-column row segments of y.
+      // Stage the BM x BN tile in LDS (all waves are past their last read of the
+      // operand tile), then each wave stores whole BN-column row segments.
       __syncthreads();
       float* out = reinterpret_cast<float*>(smem);
       constexpr int ld = BN + 4;
@@ -349,11 +352,63 @@ __global__ void __launch_bounds__(kStreamThreads) stream_expert_kernel(ExpertArg
         const int m = t.m0 + q;
         if (m >= t.rows) break;
         const DownDst dst = down_row(a, t, m);
-        float* yr = dst.row + n0;
+        float* yr = dst.row + d.n0;
 #pragma unroll
         for (int c = lane; c < BN; c += kWave) yr[c] = dst.w * out[q * ld + c];
       }
     }
+  };
+
+  // ---- the stage stream
+  // The workgroup's tiles are consumed as one stream of stages.  Two stages are in
+  // flight in registers (R0 / R1 alternate) while one is consumed from LDS; the load
+  // cursor runs ahead across tile boundaries, so the next tile's first stages are
+  // already in flight while the current tile finishes and writes its results.
+  Tile ld = make_tile(walk.tile);
+  Src lsrc = make_src(ld);
+  int ld_tile = walk.tile, ld_ks = 0;
+  auto issue = [&](Regs& R) {
+    if (ld_tile >= walk.end) return;
+    gload(R, ld, lsrc, ld_ks);
+    if (++ld_ks == ld.nk) {
+      ld_ks = 0;
+      ld_tile += walk.step;
+      if (ld_tile < walk.end) {
+        ld = make_tile(ld_tile);
+        lsrc = make_src(ld);
+      }
+    }
+  };
+  Tile cp = ld;
+  int cp_tile = walk.tile, cp_ks = 0;
+  // Consume one stage; returns false after the workgroup's last tile is written.
+  auto consume = [&]() {
+    compute();
+    if (++cp_ks < cp.nk) return true;
+    epilogue(cp);
+    clear_acc();
+    cp_ks = 0;
+    cp_tile += walk.step;
+    if (cp_tile >= walk.end) return false;
+    cp = make_tile(cp_tile);
+    return true;
+  };
+
+  Regs R0, R1;
+  clear_acc();
+  issue(R0);
+  issue(R1);
+  while (true) {
+    __syncthreads();                   // every wave is past its reads of the LDS stage
+    lstore(R0, cp);
+    __syncthreads();
+    issue(R0);
+    if (!consume()) break;
+    __syncthreads();
+    lstore(R1, cp);
+    __syncthreads();
+    issue(R1);
+    if (!consume()) break;
   }
 }
 
@@ -370,7 +425,7 @@ hipError_t launch_stream(const ExpertArgs& a, hipStream_t stream) {
   const int bn_cols = (MODE == SMode::GateUp) ? BN / 2 : BN;
   const int nt_r = (MODE == SMode::GateUp) ? a.I / bn_cols : a.H / bn_cols;
   const int nt_s = (MODE == SMode::GateUp) ? a.S / bn_cols : a.H / bn_cols;
-  const int grid = stream_grid(a, BM, nt_r, nt_s, 4);
+  const int grid = stream_grid(a, BM, nt_r, nt_s, 2);
   stream_expert_kernel<MODE, BM, BN, WM, FP8><<<grid, kStreamThreads, 0, stream>>>(a);
   return hipGetLastError();
 }

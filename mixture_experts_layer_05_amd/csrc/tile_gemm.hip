@@ -29,6 +29,9 @@ namespace {
 constexpr int kTileThreads = 512;
 constexpr int kRowBytes = 136;   // 128 data bytes + 8 padding bytes per LDS row
 constexpr int kXcds = 8;
+// m-tiles per band of the tile order (see find_tile): 8 row blocks x 4 weight slabs
+// per 32 consecutive tiles.
+constexpr int kBand = 8;
 
 enum class Mode { GateUp, Down };
 
@@ -63,7 +66,7 @@ __global__ void __launch_bounds__(kTileThreads) tiled_expert_kernel(ExpertArgs a
   using C = TileCfg<MODE, BM, BN, FP8>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::kStage];
   __shared__ __attribute__((aligned(16))) float sscale[2][FP8 ? BM + BN : 4];
-  __shared__ int prefix[kMaxExperts + 2];
+  __shared__ int prefix[kSchedInts];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
@@ -75,7 +78,7 @@ __global__ void __launch_bounds__(kTileThreads) tiled_expert_kernel(ExpertArgs a
   const int bn_cols = (MODE == Mode::GateUp) ? BN / 2 : BN;   // output columns per tile
   const int nt_r = (MODE == Mode::GateUp) ? a.I / bn_cols : H / bn_cols;
   const int nt_s = has_shared ? ((MODE == Mode::GateUp) ? a.S / bn_cols : H / bn_cols) : 0;
-  const int total = build_tile_prefix(prefix, a.counts, a.E, a.T, has_shared, BM, nt_r, nt_s);
+  const int total = build_tile_prefix(prefix, a.counts, a.offsets, a.E, a.T, has_shared, BM, nt_r, nt_s);
 
 
   const int crow = tid >> 3;          // first row this thread loads (then +64, +128, ...)
@@ -83,7 +86,7 @@ __global__ void __launch_bounds__(kTileThreads) tiled_expert_kernel(ExpertArgs a
 
   const XcdWalk walk(total);
   for (int tile = walk.tile; tile < walk.end; tile += walk.step) {
-    const TileInfo t = find_tile(prefix, G, tile, a, BM);
+    const TileInfo t = find_tile(prefix, G, tile, a, BM, kBand);
     const int kdim = (MODE == Mode::GateUp) ? H : (t.shared ? a.S : a.I);
     const int nk = kdim / C::kBK;
     const int n0 = t.nt * bn_cols;

@@ -23,6 +23,16 @@ __device__ __forceinline__ uint4 ld16_stream(const void* p) {
   return uint4{v.x, v.y, v.z, v.w};
 }
 
+// Raw buffer loads: a scalar resource (base, size in bytes) plus a 32-bit
+// per-lane offset and a scalar offset.  Loads past `bytes` return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 // 16-byte LDS accesses at 8-byte aligned addresses (issued as ds_read2_b64 /
 // ds_write2_b64).  Measured on MI355X for the MFMA fragment pattern (16 rows x
 // 64 bytes per wave read): row strides of 8 mod 16 bytes sustain ~235 B/clk/CU,

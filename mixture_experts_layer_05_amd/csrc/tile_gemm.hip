@@ -2,24 +2,25 @@
 //
 // Same contract as the streaming kernels in stream_gemm.hip (gate/up + SwiGLU
 // into h; down into the per-slot output rows), organised for MFMA throughput
-// instead of weight streaming:
+// instead of weight streaming.  A workgroup owns a BM x BN output tile of one
+// group (routed expert or the shared expert); for gate/up, BN covers 128 gate
+// rows and the 128 up rows of the same intermediate columns, so SwiGLU is fused
+// in registers.  The contraction runs in stages of 128 bytes per row (64 bf16 or
+// one 128-element fp8 scale group).  Tiles are walked persistently; consecutive
+// tiles share a weight slab or a row block and are given to workgroups on the
+// same XCD, so those operands are fetched from HBM once per XCD and hit that
+// XCD's L2 afterwards.  Two kernels:
 //
-//   * a workgroup of 8 waves owns a BM x BN output tile of one group (routed
-//     expert or the shared expert); BM = 256 or 128 rows, BN = 256 columns (for
-//     gate/up: 128 gate rows and the 128 up rows of the same intermediate
-//     columns, so SwiGLU is fused in registers);
-//   * the contraction runs in stages of 128 bytes per row (64 bf16 or one
-//     128-element fp8 scale group).  Each stage of A (token rows, gathered
-//     through the dispatch permutation) and B (weight rows) is loaded with
-//     16-byte coalesced loads into registers one stage ahead, then written to a
-//     double-buffered LDS tile whose rows are padded to 136 bytes (8 mod 16:
-//     the MFMA fragment reads then run at full LDS rate, see common.h);
-//   * each wave computes a 64-row x BN/WGN-column sub-tile with 16x16x32 bf16
-//     MFMAs (two per stage and block pair) or 16x16x128 fp8 MFMAs (one per stage,
-//     rescaled by the row and column group scales staged in LDS);
-//   * tiles are walked persistently; consecutive tiles share a weight slab and
-//     are given to workgroups on the same XCD, so the slab is fetched from HBM
-//     once per XCD and the other m-tiles hit that XCD's L2.
+//   * tiled4_expert_kernel (bf16, 256-row tiles): 4 waves of 128 x 128 with
+//     32x32x16 MFMAs; see its own description below.
+//   * tiled_expert_kernel (128-row tiles, bf16 and fp8): 8 waves of 64 x 64.
+//     Each stage of A (token rows, gathered through the dispatch permutation)
+//     and B (weight rows) is loaded with 16-byte coalesced loads into registers
+//     one stage ahead, then written to a double-buffered LDS tile whose rows are
+//     padded to 136 bytes (8 mod 16: the MFMA fragment reads then run at full
+//     LDS rate, see common.h).  16x16x32 bf16 MFMAs (two per stage and block
+//     pair) or 16x16x128 fp8 MFMAs (one per stage, rescaled by the row and
+//     column group scales staged in LDS).
 #include "kernels.h"
 #include "schedule.h"
 
@@ -283,6 +284,303 @@ __global__ void __launch_bounds__(kTileThreads) tiled_expert_kernel(ExpertArgs a
   }
 }
 
+// ---------------------------------------------------------------- 256 x 256, 4 waves (bf16)
+//
+// The bf16 prefill tile: 256 x 256 outputs per workgroup of 4 waves, each wave a
+// 128 x 128 sub-tile held as 4 x 4 blocks of 32x32 (the 256 accumulator
+// registers; one wave per SIMD).  With one wave per SIMD the 32x32x16 bf16 MFMA
+// sustains close to the chip's peak, the 16x16x32 one about half of it
+// (measured), and a 128 x 128 wave tile needs half the LDS fragment bytes per
+// flop of a 64 x 64 one.
+//
+// A stage is 64 contraction elements: 128 bytes of each of the 256 A rows and 256
+// B rows (64 KiB), double-buffered in LDS.  Full 128-byte row pieces matter: from
+// L2, a CU receives about 2.5x the bytes per clock with 128-byte pieces than with
+// 64-byte ones (measured).
+//   * A (gathered activation rows, mostly L2 hits) goes memory -> LDS directly,
+//     one stage ahead, with buffer loads carrying the LDS flag (each wave
+//     instruction writes 64 lanes x 16 bytes = 1 KiB of consecutive LDS);
+//   * B (weight rows, streamed from HBM) is loaded into registers two stages
+//     ahead and written to LDS one stage ahead, which keeps two stages of the
+//     HBM stream in flight per CU within the LDS budget.
+// Rows are stored unpadded with their eight 16-byte pieces permuted by
+// (row / 2) mod 8; a fragment read (32 rows x one piece) then touches each
+// 16-byte bank group of the 256-byte bank width once per 16 rows.
+constexpr int kT4Threads = 256;
+constexpr int kT4RowBytes = 128;                        // 64 bf16 per row per stage
+constexpr int kT4Stage = (256 + 256) * kT4RowBytes;     // 64 KiB
+constexpr int kT4Insts = 256 * kT4RowBytes / 1024 / 4;  // DMA instructions per wave per operand (8)
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)p));
+}
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Buffer resource words for a raw byte buffer.
+__device__ __forceinline__ i32x4_t dma_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4_t r = {static_cast<int>(static_cast<uint32_t>(p)), static_cast<int>(static_cast<uint32_t>(p >> 32) & 0xffff),
+               static_cast<int>(bytes), 0x00020000};
+  r.x = __builtin_amdgcn_readfirstlane(r.x);
+  r.y = __builtin_amdgcn_readfirstlane(r.y);
+  r.z = __builtin_amdgcn_readfirstlane(r.z);
+  return r;
+}
+
+// Eight wave instructions of buffer loads with the LDS flag.  Instruction q: lane l
+// loads 16 bytes at resource offset voff[q] + soff and writes them to LDS at
+// lds + 1024 q + 16 l (M0 holds the LDS address; a write of M0 needs one wait
+// state before the load that uses it).  Completion is
+// counted by vmcnt like any load; the caller waits for it explicitly.  The
+// compiler does not see these accesses: it neither waits for them nor moves LDS
+// accesses across them ("memory" clobber).
+#define MOE_DMA_LINE(V, S) "s_nop 0\n\tbuffer_load_dwordx4 " V ", %[rs], " S " offen lds\n\t"
+#define MOE_DMA_NEXT "s_add_u32 m0, m0, 0x400\n\t"
+
+__device__ __forceinline__ void dma8_rows(i32x4_t rsrc, const uint32_t (&voff)[8], uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %[lds]\n\t"
+               MOE_DMA_LINE("%[v0]", "%[so]") MOE_DMA_NEXT MOE_DMA_LINE("%[v1]", "%[so]") MOE_DMA_NEXT
+               MOE_DMA_LINE("%[v2]", "%[so]") MOE_DMA_NEXT MOE_DMA_LINE("%[v3]", "%[so]") MOE_DMA_NEXT
+               MOE_DMA_LINE("%[v4]", "%[so]") MOE_DMA_NEXT MOE_DMA_LINE("%[v5]", "%[so]") MOE_DMA_NEXT
+               MOE_DMA_LINE("%[v6]", "%[so]") MOE_DMA_NEXT MOE_DMA_LINE("%[v7]", "%[so]")
+               :
+               : [v0] "v"(voff[0]), [v1] "v"(voff[1]), [v2] "v"(voff[2]), [v3] "v"(voff[3]),
+                 [v4] "v"(voff[4]), [v5] "v"(voff[5]), [v6] "v"(voff[6]), [v7] "v"(voff[7]),
+                 [rs] "s"(rsrc), [so] "s"(soff), [lds] "s"(lds)
+               : "memory", "scc");
+}
+
+#undef MOE_DMA_LINE
+#undef MOE_DMA_NEXT
+
+// Wait until at most N vector-memory instructions of this wave are outstanding
+// (they complete in issue order).  vmcnt sits in bits 3:0 and 15:14; expcnt and
+// lgkmcnt are left at "no wait".
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xf00);
+}
+
+__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(uint4 a, uint4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+template <Mode MODE>
+__global__ void __launch_bounds__(kT4Threads) tiled4_expert_kernel(ExpertArgs a) {
+  constexpr int BM = 256, BN = 256;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kT4Stage];
+  __shared__ int prefix[kSchedInts];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const bool has_shared = a.S > 0;
+  const int G = a.E + (has_shared ? 1 : 0);
+  const int H = a.H;
+  const int bn_cols = (MODE == Mode::GateUp) ? BN / 2 : BN;
+  const int nt_r = (MODE == Mode::GateUp) ? a.I / bn_cols : H / bn_cols;
+  const int nt_s = has_shared ? ((MODE == Mode::GateUp) ? a.S / bn_cols : H / bn_cols) : 0;
+  const int total = build_tile_prefix(prefix, a.counts, a.offsets, a.E, a.T, has_shared, BM, nt_r, nt_s);
+
+  // DMA lane mapping: instruction q of this wave covers tile rows
+  // 8 (kT4Insts wave + q) + lane / 8; LDS piece lane % 8 holds global piece
+  // (lane % 8) ^ ((row / 2) mod 8), which depends only on q's parity here.
+  const int drow = lane >> 3;
+  uint32_t dpiece[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) dpiece[h] = static_cast<uint32_t>(((lane & 7) ^ ((4 * h + (drow >> 1)) & 7)) * 16);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(smem));
+  // Fragment reads (32x32x16): lane row r32 = lane % 32 of a 32-row block, piece
+  // 2 kk + lane / 32 for contraction step kk of the stage.
+  const int r32 = lane & 31, hi = lane >> 5;
+  const uint32_t fswz = static_cast<uint32_t>(hi ^ ((r32 >> 1) & 7));
+  // B register rows t / 8 + 32 q: the piece permutation depends on t / 8 only.
+  const uint32_t bldsoff = static_cast<uint32_t>((tid >> 3) * kT4RowBytes + (((tid & 7) ^ ((tid >> 4) & 7)) * 16));
+
+  const XcdWalk walk(total);
+  for (int tile = walk.tile; tile < walk.end; tile += walk.step) {
+    TileInfo t = find_tile(prefix, G, tile, a, BM, kBand);
+    t.group = __builtin_amdgcn_readfirstlane(t.group);
+    t.shared = __builtin_amdgcn_readfirstlane(static_cast<int>(t.shared)) != 0;
+    t.rows = __builtin_amdgcn_readfirstlane(t.rows);
+    t.rowbase = __builtin_amdgcn_readfirstlane(t.rowbase);
+    t.m0 = __builtin_amdgcn_readfirstlane(t.m0);
+    t.nt = __builtin_amdgcn_readfirstlane(t.nt);
+    const int kdim = (MODE == Mode::GateUp) ? H : (t.shared ? a.S : a.I);
+    const int nk = kdim / 64;
+    const int n0 = t.nt * bn_cols;
+    const uint32_t krow = static_cast<uint32_t>(kdim) * 2;   // bytes per operand row
+
+    i32x4_t ra;
+    const uint8_t* b0p;   // B rows [0, 128) of the tile
+    const uint8_t* b1p;   // B rows [128, 256)
+    uint32_t aoff[kT4Insts];
+#pragma unroll
+    for (int q = 0; q < kT4Insts; ++q) {
+      const int m = min(t.m0 + 8 * (kT4Insts * wave + q) + drow, t.rows - 1);
+      if constexpr (MODE == Mode::GateUp)
+        aoff[q] = static_cast<uint32_t>(row_token(a, t, m)) * krow + dpiece[q & 1];
+      else
+        aoff[q] = static_cast<uint32_t>(m) * krow + dpiece[q & 1];
+    }
+    if constexpr (MODE == Mode::GateUp) {
+      ra = dma_rsrc(a.x, static_cast<uint32_t>(a.T) * krow);
+      const uint8_t* wg = static_cast<const uint8_t*>(t.shared ? a.ws_gate : a.w_gate);
+      const uint8_t* wu = static_cast<const uint8_t*>(t.shared ? a.ws_up : a.w_up);
+      const size_t eoff = (t.shared ? 0 : static_cast<size_t>(t.group) * a.I * krow) +
+                          static_cast<size_t>(n0) * krow;
+      b0p = wg + eoff;
+      b1p = wu + eoff;
+    } else {
+      const size_t hrow = t.shared ? static_cast<size_t>(a.h_shared) : static_cast<size_t>(t.rowbase) * kdim;
+      ra = dma_rsrc(static_cast<const uint8_t*>(a.h) + hrow * 2, static_cast<uint32_t>(t.rows) * krow);
+      const uint8_t* wd = static_cast<const uint8_t*>(t.shared ? a.ws_down : a.w_down);
+      const size_t eoff = (t.shared ? 0 : static_cast<size_t>(t.group) * H * krow) +
+                          static_cast<size_t>(n0) * krow;
+      b0p = wd + eoff;
+      b1p = wd + eoff + 128 * static_cast<size_t>(krow);
+    }
+    const __amdgpu_buffer_rsrc_t rb0v = buf_rsrc(b0p, 128 * krow);
+    const __amdgpu_buffer_rsrc_t rb1v = buf_rsrc(b1p, 128 * krow);
+    const uint32_t bvoff = static_cast<uint32_t>(tid >> 3) * krow + (tid & 7) * 16;
+
+    // A (activation rows, mostly L2 hits) goes memory -> LDS by DMA one stage
+    // ahead.  B (weight rows, streamed from HBM) is loaded into registers two
+    // stages ahead and written to LDS one stage ahead: thread t holds rows
+    // t / 8 + 32 q (q < 8; q < 4 from rb0, the rest from rb1), piece t % 8.
+    auto issue_a = [&](int ks) {
+      const uint32_t buf = lds0 + static_cast<uint32_t>(ks & 1) * kT4Stage + kT4Insts * wave * 1024;
+      dma8_rows(ra, aoff, static_cast<uint32_t>(ks) * kT4RowBytes, buf);
+    };
+    struct BRegs {
+      uint4 v[8];
+    };
+    auto load_b = [&](BRegs& R, int ks) {
+      const uint32_t kb = static_cast<uint32_t>(ks) * kT4RowBytes;
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        R.v[q] = buf_ld16(q < 4 ? rb0v : rb1v, bvoff, kb + 32 * (q & 3) * krow);
+    };
+    auto store_b = [&](const BRegs& R, int ks) {
+      uint8_t* dst = smem + (ks & 1) * kT4Stage + BM * kT4RowBytes + bldsoff;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) *reinterpret_cast<uint4*>(dst + 32 * q * kT4RowBytes) = R.v[q];
+    };
+
+    constexpr int NI = 4;                      // 32-row blocks per wave
+    constexpr int NJ = 4;                      // 32-column blocks per wave
+    const int arow0 = wm * 128;
+
+    // LDS row of B feeding 32-column block j.  Gate/up: the first half of the
+    // blocks are gate rows, the second half the up rows of the same columns.
+    auto brow = [&](int j) -> int {
+      if constexpr (MODE == Mode::GateUp) return ((j < 2) ? 0 : BN / 2) + wn * 64 + 32 * (j & 1) + r32;
+      else return wn * 128 + 32 * j + r32;
+    };
+
+    f32x16 acc[NI][NJ];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    auto compute = [&](int ks) {
+      const uint8_t* base = smem + (ks & 1) * kT4Stage;
+      const uint8_t* As = base + (arow0 + r32) * kT4RowBytes;
+      const uint8_t* Bs = base + BM * kT4RowBytes;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint32_t piece = ((2 * kk) ^ fswz) * 16;
+        uint4 af[NI], bf[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) bf[j] = *reinterpret_cast<const uint4*>(Bs + brow(j) * kT4RowBytes + piece);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) af[i] = *reinterpret_cast<const uint4*>(As + i * 32 * kT4RowBytes + piece);
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_bf16_32x32x16(af[i], bf[j], acc[i][j]);
+      }
+    };
+
+    // nk is even (contractions are multiples of 128).  Iteration ks: wait for
+    // A(ks); barrier; write B(ks + 1) from registers and start A(ks + 1) into
+    // the other buffer; refill those registers with B(ks + 3); multiply stage
+    // ks.  The register loads are issued unconditionally (past the end they
+    // re-read the last stage, an L2 hit), so every iteration has the same
+    // number of loads in flight and the compiler's waits for the registers stay
+    // exact.
+    BRegs R0, R1;
+    load_b(R0, 0);
+    load_b(R1, 1);
+    __syncthreads();                 // the previous tile is done with both buffers
+    store_b(R0, 0);                  // (the compiler waits for R0's loads)
+    issue_a(0);
+    load_b(R0, min(2, nk - 1));
+    for (int ks = 0; ks < nk; ks += 2) {
+      // Even stage ks: after A(ks) come B(ks + 2)'s 8 register loads.
+      wait_vm<8>();
+      __syncthreads();
+      store_b(R1, ks + 1);
+      issue_a(ks + 1);
+      load_b(R1, min(ks + 3, nk - 1));
+      compute(ks);
+      // Odd stage ks + 1: after A(ks + 1) come B(ks + 3)'s 8 register loads.
+      wait_vm<8>();
+      __syncthreads();
+      if (ks + 2 < nk) {
+        store_b(R0, ks + 2);
+        issue_a(ks + 2);
+      }
+      load_b(R0, min(ks + 4, nk - 1));
+      compute(ks + 1);
+    }
+    wait_vm<0>();                    // no load may still be writing registers or LDS
+
+    // 32x32 output placement: lane l, element v -> row 8 (v / 4) + 4 (l / 32) +
+    // v % 4, column l % 32.
+    if constexpr (MODE == Mode::GateUp) {
+      const int width = t.shared ? a.S : a.I;
+      uint16_t* hbase = static_cast<uint16_t*>(a.h) +
+                        (t.shared ? static_cast<size_t>(a.h_shared) : static_cast<size_t>(t.rowbase) * width);
+      const int col0 = n0 + wn * 64 + r32;
+      constexpr int NH = NJ / 2;             // gate blocks (each paired with an up block)
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = t.m0 + arow0 + 32 * i + 8 * (v >> 2) + 4 * hi + (v & 3);
+          if (m < t.rows) {
+            uint16_t* hr = hbase + static_cast<size_t>(m) * width + col0;
+#pragma unroll
+            for (int jh = 0; jh < NH; ++jh)
+              hr[32 * jh] = f32_to_bf16_bits(silu_f32(acc[i][jh][v]) * acc[i][jh + NH][v]);
+          }
+        }
+    } else {
+      const int col0 = n0 + wn * 128 + r32;
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = t.m0 + arow0 + 32 * i + 8 * (v >> 2) + 4 * hi + (v & 3);
+          if (m < t.rows) {
+            const DownDst dst = down_row(a, t, m);
+            float* yr = dst.row + col0;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) yr[32 * j] = dst.w * acc[i][j][v];
+          }
+        }
+    }
+  }
+}
+
 int tiled_grid(const ExpertArgs& a, int BM, int nt_routed, int nt_shared) {
   const int64_t slots = static_cast<int64_t>(a.T) * a.K;
   int64_t b = (slots / BM + std::min<int64_t>(a.E, slots)) * nt_routed;
@@ -292,15 +590,22 @@ int tiled_grid(const ExpertArgs& a, int BM, int nt_routed, int nt_shared) {
   return static_cast<int>(std::max<int64_t>(kXcds, ceil_div(b, kXcds) * kXcds));
 }
 
+// The 256-row kernel addresses operands with 32-bit buffer offsets: every
+// activation matrix it reads (x, or one group's rows of h) must stay below 4 GiB.
+bool dma_offsets_fit(const ExpertArgs& a) {
+  const int64_t widest = std::max<int64_t>(a.H, std::max(a.I, a.S));
+  return static_cast<int64_t>(a.T) * widest * 2 < (int64_t{1} << 32);
+}
+
 }  // namespace
 
 // fp8 uses 128-row tiles only: the 256-row fp8 tile does not fit 256 registers per lane.
 hipError_t launch_gate_up_tiled(const ExpertArgs& a, bool fp8, bool tall, hipStream_t stream) {
-  tall = tall && !fp8;
+  tall = tall && !fp8 && dma_offsets_fit(a);
   const int BM = tall ? 256 : 128;
   const int grid = tiled_grid(a, BM, a.I / 128, a.S / 128);
   if (tall) {
-    tiled_expert_kernel<Mode::GateUp, 256, 256, false><<<grid, kTileThreads, 0, stream>>>(a);
+    tiled4_expert_kernel<Mode::GateUp><<<grid, kT4Threads, 0, stream>>>(a);
   } else {
     if (fp8) tiled_expert_kernel<Mode::GateUp, 128, 256, true><<<grid, kTileThreads, 0, stream>>>(a);
     else tiled_expert_kernel<Mode::GateUp, 128, 256, false><<<grid, kTileThreads, 0, stream>>>(a);
@@ -309,11 +614,11 @@ hipError_t launch_gate_up_tiled(const ExpertArgs& a, bool fp8, bool tall, hipStr
 }
 
 hipError_t launch_down_tiled(const ExpertArgs& a, bool fp8, bool tall, hipStream_t stream) {
-  tall = tall && !fp8;
+  tall = tall && !fp8 && dma_offsets_fit(a);
   const int BM = tall ? 256 : 128;
   const int grid = tiled_grid(a, BM, a.H / 256, a.H / 256);
   if (tall) {
-    tiled_expert_kernel<Mode::Down, 256, 256, false><<<grid, kTileThreads, 0, stream>>>(a);
+    tiled4_expert_kernel<Mode::Down><<<grid, kT4Threads, 0, stream>>>(a);
   } else {
     if (fp8) tiled_expert_kernel<Mode::Down, 128, 256, true><<<grid, kTileThreads, 0, stream>>>(a);
     else tiled_expert_kernel<Mode::Down, 128, 256, false><<<grid, kTileThreads, 0, stream>>>(a);

@@ -91,6 +91,15 @@ def test_tiled_fp8_kernels_with_partial_tiles(T):
     _run(TILED.with_(name="tiled_rows_fp8", weight_dtype=W.DT_FP8), T, 30 + T)
 
 
+# 256-row tiles with the shortest contractions the kernels accept (128 elements)
+# and a single n-tile per group.
+SHORT_K = W.LayerShape("tiled_short_k", 256, 2, 128, 1, 128, W.DT_BF16, W.DT_BF16)
+
+
+def test_tall_tiles_with_short_contractions():
+    _run(SHORT_K, 600, 41)
+
+
 def test_k_equals_e_with_ragged_tokens():
     _run(EDGE, 13, 5)
 

@@ -348,8 +348,35 @@ __device__ __forceinline__ void dma8_rows(i32x4_t rsrc, const uint32_t (&voff)[8
                :
                : [v0] "v"(voff[0]), [v1] "v"(voff[1]), [v2] "v"(voff[2]), [v3] "v"(voff[3]),
                  [v4] "v"(voff[4]), [v5] "v"(voff[5]), [v6] "v"(voff[6]), [v7] "v"(voff[7]),
-                 [rs] "s"(rsrc), [so] "s"(soff), [lds] "s"(lds)
+                 [rs] "s"(rsrc), [so] "s"(__builtin_amdgcn_readfirstlane(soff)),
+                 [lds] "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "scc");
+}
+
+// Four 16-byte instructions over rows `step` bytes apart: instruction q uses
+// voff[q & 1] and soff + q * step, and writes LDS at lds + 1024 q.
+__device__ __forceinline__ void dma4_step(i32x4_t rsrc, const uint32_t (&voff)[2], uint32_t soff, uint32_t step,
+                                          uint32_t lds) {
+  uint32_t so;
+  asm volatile("s_mov_b32 m0, %[lds]\n\ts_mov_b32 %[so], %[s0]\n\t"
+               MOE_DMA_LINE("%[va]", "%[so]") MOE_DMA_NEXT "s_add_u32 %[so], %[so], %[st]\n\t"
+               MOE_DMA_LINE("%[vb]", "%[so]") MOE_DMA_NEXT "s_add_u32 %[so], %[so], %[st]\n\t"
+               MOE_DMA_LINE("%[va]", "%[so]") MOE_DMA_NEXT "s_add_u32 %[so], %[so], %[st]\n\t"
+               MOE_DMA_LINE("%[vb]", "%[so]")
+               : [so] "=&s"(so)
+               : [va] "v"(voff[0]), [vb] "v"(voff[1]), [rs] "s"(rsrc),
+                 [s0] "s"(__builtin_amdgcn_readfirstlane(soff)), [st] "s"(__builtin_amdgcn_readfirstlane(step)),
+                 [lds] "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "scc");
+}
+
+// One 4-byte instruction: lane l loads the dword at voff + soff into LDS at lds + 4 l.
+__device__ __forceinline__ void dma1_dword(i32x4_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %[lds]\n\ts_nop 0\n\tbuffer_load_dword %[v], %[rs], %[so] offen lds"
+               :
+               : [v] "v"(voff), [rs] "s"(rsrc), [so] "s"(__builtin_amdgcn_readfirstlane(soff)),
+                 [lds] "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
 }
 
 #undef MOE_DMA_LINE
@@ -581,6 +608,246 @@ __global__ void __launch_bounds__(kT4Threads) tiled4_expert_kernel(ExpertArgs a)
   }
 }
 
+// ---------------------------------------------------------------- 256 x 128, 4 waves (fp8)
+//
+// The fp8 prefill tile: 256 x 128 outputs per workgroup of 4 waves, each wave
+// 128 x 64 as 8 x 4 blocks of 16x16 from 16x16x128 fp8 MFMAs.  A stage is one
+// 128-element scale group (128 bytes per row).  Every product is rescaled by its
+// row and column group scales on the VALU, which cannot reach the accumulation
+// registers; the 128 accumulators therefore live in ordinary registers.
+//
+// Everything a stage needs goes memory -> LDS by DMA: the 256 activation rows,
+// the 128 weight rows and both sets of group scales (48 KiB + 1.5 KiB).  Three
+// stage buffers keep two stages in flight while one is multiplied out; the
+// waits are explicit (every wave issues the same 14 instructions per stage and
+// they complete in order), so nothing else shortens the prefetch distance.
+// Same unpadded, piece-permuted row layout as the bf16 tile.
+constexpr int kF8Bufs = 3;
+constexpr int kF8Stage = (256 + 128) * kT4RowBytes;   // 48 KiB
+constexpr int kF8DmaPerStage = 8 + 4 + 1 + 1;        // per wave: A rows, B rows, A scales, B scales
+
+template <Mode MODE>
+__global__ void __launch_bounds__(kT4Threads) tiled8_expert_kernel(ExpertArgs a) {
+  constexpr int BM = 256, BN = 128;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kF8Bufs * kF8Stage];
+  __shared__ __attribute__((aligned(16))) float sscale[kF8Bufs][BM + BN];
+  __shared__ int prefix[kSchedInts];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const bool has_shared = a.S > 0;
+  const int G = a.E + (has_shared ? 1 : 0);
+  const int H = a.H;
+  const int bn_cols = (MODE == Mode::GateUp) ? BN / 2 : BN;
+  const int nt_r = (MODE == Mode::GateUp) ? a.I / bn_cols : H / bn_cols;
+  const int nt_s = has_shared ? ((MODE == Mode::GateUp) ? a.S / bn_cols : H / bn_cols) : 0;
+  const int total = build_tile_prefix(prefix, a.counts, a.offsets, a.E, a.T, has_shared, BM, nt_r, nt_s);
+
+  // DMA lane mapping (16-byte pieces): instruction q of a wave covers 8 rows,
+  // row 8 q' + lane / 8 with LDS piece lane % 8 holding global piece
+  // (lane % 8) ^ ((row / 2) mod 8); the permutation depends on q's parity only.
+  const int drow = lane >> 3;
+  uint32_t dpiece[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) dpiece[h] = static_cast<uint32_t>(((lane & 7) ^ ((4 * h + (drow >> 1)) & 7)) * 16);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(smem));
+  const uint32_t sc0 = __builtin_amdgcn_readfirstlane(lds_address(&sscale[0][0]));
+  // Fragment reads: lane row r16 = lane % 16, pieces g and 4 + g (g = lane / 16).
+  const int r16 = lane & 15, g = lane >> 4;
+  const uint32_t fsw = static_cast<uint32_t>((r16 >> 1) & 7);
+  const uint32_t pc0 = (static_cast<uint32_t>(g) ^ fsw) * 16, pc1 = (static_cast<uint32_t>(4 + g) ^ fsw) * 16;
+
+  const XcdWalk walk(total);
+  for (int tile = walk.tile; tile < walk.end; tile += walk.step) {
+    TileInfo t = find_tile(prefix, G, tile, a, BM, kBand);
+    t.group = __builtin_amdgcn_readfirstlane(t.group);
+    t.shared = __builtin_amdgcn_readfirstlane(static_cast<int>(t.shared)) != 0;
+    t.rows = __builtin_amdgcn_readfirstlane(t.rows);
+    t.rowbase = __builtin_amdgcn_readfirstlane(t.rowbase);
+    t.m0 = __builtin_amdgcn_readfirstlane(t.m0);
+    t.nt = __builtin_amdgcn_readfirstlane(t.nt);
+    const int kdim = (MODE == Mode::GateUp) ? H : (t.shared ? a.S : a.I);
+    const int nk = kdim / kGroup;               // one scale group per stage
+    const int ng = nk;
+    const int n0 = t.nt * bn_cols;
+    const uint32_t krow = static_cast<uint32_t>(kdim);          // bytes per fp8 row
+    const size_t hrow0 = t.shared ? static_cast<size_t>(a.h_shared) : static_cast<size_t>(t.rowbase) * kdim;
+
+    // A rows of this wave: 64 wave + 8 q + lane / 8 (q < 8); its scale row: 64 wave + lane.
+    i32x4_t ra, rsa, rb, rsb;
+    uint32_t aoff[8];
+    uint32_t saoff;
+    {
+      const int ms = min(t.m0 + 64 * wave + lane, t.rows - 1);
+      if constexpr (MODE == Mode::GateUp) {
+        ra = dma_rsrc(a.xq, static_cast<uint32_t>(a.T) * krow);
+        rsa = dma_rsrc(a.xs, static_cast<uint32_t>(a.T) * ng * 4);
+        saoff = static_cast<uint32_t>(row_token(a, t, ms)) * ng * 4;
+      } else {
+        ra = dma_rsrc(a.hq + hrow0, static_cast<uint32_t>(t.rows) * krow);
+        rsa = dma_rsrc(a.hs + hrow0 / kGroup, static_cast<uint32_t>(t.rows) * ng * 4);
+        saoff = static_cast<uint32_t>(ms) * ng * 4;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int m = min(t.m0 + 64 * wave + 8 * q + drow, t.rows - 1);
+        if constexpr (MODE == Mode::GateUp)
+          aoff[q] = static_cast<uint32_t>(row_token(a, t, m)) * krow + dpiece[q & 1];
+        else
+          aoff[q] = static_cast<uint32_t>(m) * krow + dpiece[q & 1];
+      }
+    }
+    // B rows: waves w and w + 2 cover the same 64-row half (w & 1) of the tile:
+    // gate / up rows (gate/up) or output rows n0 + 64 (w & 1) ... (down).  Each
+    // wave loads 32 of the half's rows; the scale DMA of the half is issued by
+    // both waves (identical values to the same place).
+    const int half = wave & 1;
+    uint32_t boff[2];
+    uint32_t sboff;
+    {
+      const uint8_t* wb;
+      const float* sbp;
+      if constexpr (MODE == Mode::GateUp) {
+        const uint8_t* wsrc = static_cast<const uint8_t*>(t.shared ? (half ? a.ws_up : a.ws_gate) : (half ? a.w_up : a.w_gate));
+        const float* ssrc = t.shared ? (half ? a.ss_up : a.ss_gate) : (half ? a.s_up : a.s_gate);
+        const size_t erow = (t.shared ? 0 : static_cast<size_t>(t.group) * a.I) + n0;
+        wb = wsrc + erow * krow;
+        sbp = ssrc + erow * ng;
+      } else {
+        const uint8_t* wsrc = static_cast<const uint8_t*>(t.shared ? a.ws_down : a.w_down);
+        const float* ssrc = t.shared ? a.ss_down : a.s_down;
+        const size_t erow = (t.shared ? 0 : static_cast<size_t>(t.group) * H) + n0 + 64 * half;
+        wb = wsrc + erow * krow;
+        sbp = ssrc + erow * ng;
+      }
+      rb = dma_rsrc(wb, 64 * krow);
+      rsb = dma_rsrc(sbp, 64 * ng * 4);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) boff[h] = static_cast<uint32_t>(drow) * krow + dpiece[h];
+      sboff = static_cast<uint32_t>(lane) * ng * 4;
+    }
+
+    // Stage ks -> buffer ks % 3: A rows at [0, 32 KiB), B rows after; scales in sscale.
+    auto issue = [&](int ks) {
+      const int b = ks % kF8Bufs;
+      const uint32_t buf = lds0 + static_cast<uint32_t>(b) * kF8Stage;
+      const uint32_t kb = static_cast<uint32_t>(ks) * kT4RowBytes;
+      dma8_rows(ra, aoff, kb, buf + 8 * wave * 1024);
+      dma4_step(rb, boff, kb + 8 * 4 * (wave >> 1) * krow, 8 * krow,
+                buf + BM * kT4RowBytes + (64 * half + 32 * (wave >> 1)) * kT4RowBytes);
+      const uint32_t sbuf = sc0 + static_cast<uint32_t>(b) * (BM + BN) * 4;
+      dma1_dword(rsa, saoff, static_cast<uint32_t>(ks) * 4, sbuf + 64 * wave * 4);
+      dma1_dword(rsb, sboff, static_cast<uint32_t>(ks) * 4, sbuf + (BM + 64 * half) * 4);
+    };
+
+    // LDS row of B feeding 16-column block j.  Gate/up: blocks 0, 1 are gate
+    // rows, 2, 3 the up rows of the same columns.
+    auto brow = [&](int j) -> int {
+      if constexpr (MODE == Mode::GateUp) return ((j < 2) ? 0 : BN / 2) + wn * 32 + 16 * (j & 1) + r16;
+      else return wn * 64 + 16 * j + r16;
+    };
+    auto frag = [&](const uint8_t* row) -> i32x8 {
+      const uint4 lo = *reinterpret_cast<const uint4*>(row + pc0);
+      const uint4 hi = *reinterpret_cast<const uint4*>(row + pc1);
+      return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int ks) {
+      const int b = ks % kF8Bufs;
+      const uint8_t* base = smem + b * kF8Stage;
+      const uint8_t* As = base + (wm * 128 + r16) * kT4RowBytes;
+      const uint8_t* Bs = base + BM * kT4RowBytes;
+      const float* sA = &sscale[b][wm * 128 + 4 * g];
+      const float* sB = &sscale[b][BM];
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      i32x8 bf[4];
+      float sb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf[j] = frag(Bs + brow(j) * kT4RowBytes);
+        sb[j] = sB[brow(j)];
+      }
+      // Products are formed one row block ahead of their rescale, so the matrix
+      // pipe always has independent work while the VALU waits for results.
+      f32x4 pc[4], pn[4];
+      {
+        const i32x8 af = frag(As);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pc[j] = mfma_fp8_16x16x128(af, bf[j], zero);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i + 1 < 8) {
+          const i32x8 af = frag(As + (i + 1) * 16 * kT4RowBytes);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pn[j] = mfma_fp8_16x16x128(af, bf[j], zero);
+        }
+        const f32x4 sa = *reinterpret_cast<const f32x4*>(sA + 16 * i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(pc[j][e], sa[e] * sb[j], acc[i][j][e]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pc[j] = pn[j];
+      }
+    };
+
+    // Stage ks: wait for this wave's part of it (only stage ks + 1's 14
+    // instructions may still be pending); barrier (every wave's part has landed,
+    // and stage ks - 1's buffer is no longer read); start stage ks + 2 into that
+    // buffer; multiply stage ks.
+    __syncthreads();                   // the previous tile is done with every buffer
+    issue(0);
+    if (nk > 1) issue(1);
+    for (int ks = 0; ks < nk; ++ks) {
+      if (ks + 1 < nk) wait_vm<kF8DmaPerStage>();
+      else wait_vm<0>();
+      __syncthreads();
+      if (ks + 2 < nk) issue(ks + 2);
+      compute(ks);
+    }
+
+    // 16x16 output placement: lane l, element e -> row 4 (l / 16) + e, column l % 16.
+    if constexpr (MODE == Mode::GateUp) {
+      const int width = t.shared ? a.S : a.I;
+      float* hbase = static_cast<float*>(a.h) +
+                     (t.shared ? static_cast<size_t>(a.h_shared) : static_cast<size_t>(t.rowbase) * width);
+      const int col0 = n0 + wn * 32 + r16;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = t.m0 + wm * 128 + 16 * i + 4 * g + e;
+          if (m < t.rows) {
+            float* hr = hbase + static_cast<size_t>(m) * width + col0;
+#pragma unroll
+            for (int jh = 0; jh < 2; ++jh) hr[16 * jh] = silu_f32(acc[i][jh][e]) * acc[i][jh + 2][e];
+          }
+        }
+    } else {
+      const int col0 = n0 + wn * 64 + r16;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = t.m0 + wm * 128 + 16 * i + 4 * g + e;
+          if (m < t.rows) {
+            const DownDst dst = down_row(a, t, m);
+            float* yr = dst.row + col0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) yr[16 * j] = dst.w * acc[i][j][e];
+          }
+        }
+    }
+  }
+}
+
 int tiled_grid(const ExpertArgs& a, int BM, int nt_routed, int nt_shared) {
   const int64_t slots = static_cast<int64_t>(a.T) * a.K;
   int64_t b = (slots / BM + std::min<int64_t>(a.E, slots)) * nt_routed;
@@ -590,8 +857,8 @@ int tiled_grid(const ExpertArgs& a, int BM, int nt_routed, int nt_shared) {
   return static_cast<int>(std::max<int64_t>(kXcds, ceil_div(b, kXcds) * kXcds));
 }
 
-// The 256-row kernel addresses operands with 32-bit buffer offsets: every
-// activation matrix it reads (x, or one group's rows of h) must stay below 4 GiB.
+// The 256-row kernels address operands with 32-bit buffer offsets: every
+// activation matrix they read (x, or one group's rows of h) must stay below 4 GiB.
 bool dma_offsets_fit(const ExpertArgs& a) {
   const int64_t widest = std::max<int64_t>(a.H, std::max(a.I, a.S));
   return static_cast<int64_t>(a.T) * widest * 2 < (int64_t{1} << 32);
@@ -599,13 +866,14 @@ bool dma_offsets_fit(const ExpertArgs& a) {
 
 }  // namespace
 
-// fp8 uses 128-row tiles only: the 256-row fp8 tile does not fit 256 registers per lane.
 hipError_t launch_gate_up_tiled(const ExpertArgs& a, bool fp8, bool tall, hipStream_t stream) {
-  tall = tall && !fp8 && dma_offsets_fit(a);
+  tall = tall && dma_offsets_fit(a);
   const int BM = tall ? 256 : 128;
-  const int grid = tiled_grid(a, BM, a.I / 128, a.S / 128);
+  const int hcols = (tall && fp8) ? 64 : 128;   // h columns per tile
+  const int grid = tiled_grid(a, BM, a.I / hcols, a.S / hcols);
   if (tall) {
-    tiled4_expert_kernel<Mode::GateUp><<<grid, kT4Threads, 0, stream>>>(a);
+    if (fp8) tiled8_expert_kernel<Mode::GateUp><<<grid, kT4Threads, 0, stream>>>(a);
+    else tiled4_expert_kernel<Mode::GateUp><<<grid, kT4Threads, 0, stream>>>(a);
   } else {
     if (fp8) tiled_expert_kernel<Mode::GateUp, 128, 256, true><<<grid, kTileThreads, 0, stream>>>(a);
     else tiled_expert_kernel<Mode::GateUp, 128, 256, false><<<grid, kTileThreads, 0, stream>>>(a);
@@ -614,11 +882,13 @@ hipError_t launch_gate_up_tiled(const ExpertArgs& a, bool fp8, bool tall, hipStr
 }
 
 hipError_t launch_down_tiled(const ExpertArgs& a, bool fp8, bool tall, hipStream_t stream) {
-  tall = tall && !fp8 && dma_offsets_fit(a);
+  tall = tall && dma_offsets_fit(a);
   const int BM = tall ? 256 : 128;
-  const int grid = tiled_grid(a, BM, a.H / 256, a.H / 256);
+  const int ycols = (tall && fp8) ? 128 : 256;  // output columns per tile
+  const int grid = tiled_grid(a, BM, a.H / ycols, a.H / ycols);
   if (tall) {
-    tiled4_expert_kernel<Mode::Down><<<grid, kT4Threads, 0, stream>>>(a);
+    if (fp8) tiled8_expert_kernel<Mode::Down><<<grid, kT4Threads, 0, stream>>>(a);
+    else tiled4_expert_kernel<Mode::Down><<<grid, kT4Threads, 0, stream>>>(a);
   } else {
     if (fp8) tiled_expert_kernel<Mode::Down, 128, 256, true><<<grid, kTileThreads, 0, stream>>>(a);
     else tiled_expert_kernel<Mode::Down, 128, 256, false><<<grid, kTileThreads, 0, stream>>>(a);

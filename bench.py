@@ -90,6 +90,30 @@ def accounting(shape, T, counts):
                 gate_up_flops=4.0 * H * I * slots + 4.0 * T * H * S)
 
 
+def gate_up_kernel(shape, T: int) -> str:
+    """Name of the gate/up kernel the library launches for this layer and T (the
+    same rows-per-expert rule as its launchers; used to label the roofline)."""
+    if shape.weight_dtype == "f32":
+        return "gate_up_f32_kernel"
+    fp8 = shape.weight_dtype != "bf16"
+    H, E, I, K, S = (shape.hidden_size, shape.n_routed_experts, shape.moe_intermediate_size,
+                     shape.num_experts_per_tok, shape.shared_expert_intermediate_size)
+    rho = T * K // E
+    if rho >= 48:
+        tall = rho >= 160 and T * max(H, I, S) * 2 < (1 << 32)
+        if tall:
+            return "tiled8_expert_kernel<GateUp> (fp8, 256x128)" if fp8 else "tiled4_expert_kernel<GateUp> (bf16, 256x256)"
+        return f"tiled_expert_kernel<GateUp, 128, 256, {'fp8' if fp8 else 'bf16'}>"
+    narrow = min(E, T * K) * (I // 64) < 3 * 256
+    if rho <= 12:
+        cfg = "16, 128, 1"
+    elif rho <= 24:
+        cfg = "32, 64, 2" if narrow else "32, 128, 1"
+    else:
+        cfg = "64, 64, 2" if narrow else "64, 128, 1"
+    return f"stream_expert_kernel<GateUp, {cfg}, {'fp8' if fp8 else 'bf16'}>"
+
+
 def library_source_hash() -> str:
     """sha256 over the HIP sources: the kernels that a stored counter reading describes."""
     import glob
@@ -228,11 +252,12 @@ def main():
     if rho >= 48 and shape.weight_dtype != "f32":
         achieved = a["gate_up_flops"] / (gate_up_ms * 1e-3) / 1e12
         peak = MFMA_PEAK_TFLOPS[shape.weight_dtype]
-        roof = {"bound": "mfma", "kernel": "tiled_expert_kernel<GateUp>", "achieved": round(achieved, 1),
-                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+        roof = {"bound": "mfma", "kernel": gate_up_kernel(shape, T), "achieved": round(achieved, 1),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": stored_traffic("gate_up", f"{args.workload}_T{T}")}
     else:
         achieved = a["gate_up_bytes"] / (gate_up_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "stream_expert_kernel<GateUp>", "achieved": round(achieved, 1),
+        roof = {"bound": "hbm", "kernel": gate_up_kernel(shape, T), "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": stored_traffic("gate_up", f"{args.workload}_T{T}")}
     line = {

@@ -9,10 +9,12 @@
 // one 128-element fp8 scale group).  Tiles are walked persistently; consecutive
 // tiles share a weight slab or a row block and are given to workgroups on the
 // same XCD, so those operands are fetched from HBM once per XCD and hit that
-// XCD's L2 afterwards.  Two kernels:
+// XCD's L2 afterwards.  Three kernels:
 //
 //   * tiled4_expert_kernel (bf16, 256-row tiles): 4 waves of 128 x 128 with
 //     32x32x16 MFMAs; see its own description below.
+//   * tiled8_expert_kernel (fp8, 256-row tiles): 4 waves of 128 x 64 with
+//     16x16x128 fp8 MFMAs and all operands loaded by LDS DMA; see below.
 //   * tiled_expert_kernel (128-row tiles, bf16 and fp8): 8 waves of 64 x 64.
 //     Each stage of A (token rows, gathered through the dispatch permutation)
 //     and B (weight rows) is loaded with 16-byte coalesced loads into registers

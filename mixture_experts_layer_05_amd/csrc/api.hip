@@ -12,9 +12,12 @@ namespace {
 
 constexpr size_t kAlign = 256;
 // From this many tokens the router logits run on the LDS-staged streaming kernel
-// (64-token x 128-column tiles); below it, on 16 x 16 tiles whose waves split H,
-// which spreads the router weights over more workgroups.
+// (64-token x 128-column tiles); below it, on 16-token x 32-column tiles whose
+// waves split H, which spreads the router weights over more workgroups.
 constexpr int32_t kRouterTiledTokens = 4096;
+// Router contraction split for decode-sized batches (see moe_route).
+constexpr int32_t kRouterPlaneTokens = 1024;
+constexpr int kRouterParts = 8;
 
 bool valid_dtype(int d) { return d == MOE_DTYPE_F32 || d == MOE_DTYPE_BF16 || d == MOE_DTYPE_FP8_E4M3_G128; }
 
@@ -52,6 +55,7 @@ int check_tokens(const moe_config* c, int32_t T) {
 struct Layout {
   size_t z, h, o, xq, xs, hq, hs, chunks, ranks, total;
   int ldz;
+  int64_t zrows;   // rows of z: T per logit plane
   size_t h_shared;  // element offset of the shared expert's rows in h
 };
 
@@ -65,7 +69,12 @@ Layout layout(const moe_config& c, int64_t T) {
   };
   const int E = c.n_routed_experts;
   L.ldz = static_cast<int>(align_up(E + 1, 16));
-  L.z = take(static_cast<size_t>(T) * L.ldz * sizeof(float));
+  // Logit planes: decode-sized batches (T <= kRouterPlaneTokens) split the router's
+  // contraction over up to kRouterParts workgroups, each writing a partial plane.
+  // max(T, kRouterParts * min(T, kRouterPlaneTokens)) rows keeps the size
+  // monotone in T, so a workspace sized for max_tokens fits every smaller call.
+  L.zrows = std::max<int64_t>(T, static_cast<int64_t>(kRouterParts) * std::min<int64_t>(T, kRouterPlaneTokens));
+  L.z = take(static_cast<size_t>(L.zrows) * L.ldz * sizeof(float));
   L.chunks = take(static_cast<size_t>(ceil_div(T, 1024)) * E * sizeof(int32_t));
   L.ranks = take(static_cast<size_t>(T) * c.num_experts_per_tok * sizeof(int32_t));
   const size_t routed = static_cast<size_t>(T) * c.num_experts_per_tok * c.moe_intermediate_size;
@@ -196,6 +205,8 @@ int moe_route(const moe_config* cfg, int32_t T, const void* x, const void* w_rou
   const int E = cfg->n_routed_experts, H = cfg->hidden_size, K = cfg->num_experts_per_tok;
   const int ncols = E + (has_shared ? 1 : 0);
   float* z = at<float>(ws, L.z);
+  int parts = 1;                                            // logit planes written
+  const size_t plane = static_cast<size_t>(T) * L.ldz;      // floats between planes
   if (cfg->act_dtype == MOE_DTYPE_BF16 && T >= kRouterTiledTokens) {
     ExpertArgs r{};
     r.x = x;
@@ -209,10 +220,18 @@ int moe_route(const moe_config* cfg, int32_t T, const void* x, const void* w_rou
     r.E = E;
     if ((st = launched(launch_router_stream(r, s)))) return st;
   } else if (cfg->act_dtype == MOE_DTYPE_BF16) {
-    dim3 grid(static_cast<unsigned>(ceil_div(T, 16)), static_cast<unsigned>(ceil_div(ncols, 16)));
+    // Enough workgroups for ~256 CUs: split the hidden dimension into parts when
+    // the token x column tiles alone are too few (at least 4 chunks of 128 per part).
+    const int64_t tiles = ceil_div(T, 16) * ceil_div(ncols, 32);
+    if (T <= kRouterPlaneTokens)
+      parts = static_cast<int>(std::max<int64_t>(
+          1, std::min<int64_t>({kRouterParts, ceil_div(256, tiles), (H / 128) / 4})));
+    dim3 grid(static_cast<unsigned>(ceil_div(T, 16)), static_cast<unsigned>(ceil_div(ncols, 32)),
+              static_cast<unsigned>(parts));
     router_logits_bf16_kernel<<<grid, 256, 0, s>>>(
         static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
-        static_cast<const uint16_t*>(has_shared ? w_shared_gate : w_router), T, H, E, ncols, z, L.ldz);
+        static_cast<const uint16_t*>(has_shared ? w_shared_gate : w_router), T, H, E, ncols, z, L.ldz,
+        plane);
   } else {
     const int64_t items = static_cast<int64_t>(T) * ncols;
     router_logits_f32_kernel<<<static_cast<unsigned>(ceil_div(items, 4)), 256, 0, s>>>(
@@ -221,8 +240,8 @@ int moe_route(const moe_config* cfg, int32_t T, const void* x, const void* w_rou
   }
   if ((st = launched(hipGetLastError()))) return st;
   topk_kernel<<<static_cast<unsigned>(ceil_div(T, 4)), 256, 0, s>>>(
-      z, L.ldz, logit_bias, T, E, K, cfg->norm_topk_prob, has_shared ? 1 : 0, topk_ids, topk_w,
-      shared_gate);
+      z, L.ldz, parts, plane, logit_bias, T, E, K, cfg->norm_topk_prob, has_shared ? 1 : 0, topk_ids,
+      topk_w, shared_gate);
   if ((st = launched(hipGetLastError()))) return st;
   if (cfg->expert_budget > 0 || route_stats) {
     budget_kernel<<<1, 1024, 0, s>>>(topk_ids, topk_w, T, E, K, cfg->expert_budget,

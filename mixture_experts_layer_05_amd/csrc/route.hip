@@ -10,51 +10,69 @@ namespace moe {
 
 // ------------------------------------------------------------------ logits, bf16 (MFMA)
 //
-// One workgroup = 4 waves computes a 16-token x 16-column tile; the waves split
-// the hidden dimension into four contiguous ranges and their partial tiles are
-// summed through LDS.  Column c < E is W_r[c], column E (if present) is w_g, the
-// rest of the padded tile is skipped.  Every product of two bf16 values is exact
-// in float32 and the MFMA accumulates in float32.
+// One workgroup = 4 waves computes a 16-token x 32-column tile (two 16-column
+// MFMA blocks sharing the token fragments) over one of P contiguous parts of the
+// hidden dimension; the waves split the part into four ranges and their partial
+// tiles are summed through LDS.  Part p writes its partial logits to plane p of
+// z (p * plane floats further on); the top-k kernel adds the planes in order
+// 0..P-1, so the result does not depend on timing.  Splitting the contraction
+// gives a decode-sized batch enough workgroups to keep its loads in flight.
+// Column c < E is W_r[c], column E (if present) is w_g, the rest of the padded
+// tile is computed on a repeated column and not stored.  Every product of two
+// bf16 values is exact in float32 and the MFMA accumulates in float32.
 __global__ void __launch_bounds__(256) router_logits_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_router,
     const uint16_t* __restrict__ w_gate_col, int T, int H, int E, int ncols,
-    float* __restrict__ z, int ldz) {
-  __shared__ f32x4 red[4][kWave];
+    float* __restrict__ z, int ldz, size_t plane) {
+  __shared__ f32x4 red[4][2][kWave];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int t0 = blockIdx.x * 16, c0 = blockIdx.y * 16;
+  const int t0 = blockIdx.x * 16, c0 = blockIdx.y * 32;
+  const int part = blockIdx.z, parts = gridDim.z;
   const int t = min(t0 + r, T - 1);
-  const int c = min(c0 + r, ncols - 1);
   const uint16_t* arow = x + static_cast<size_t>(t) * H;
-  const uint16_t* brow = (c < E) ? w_router + static_cast<size_t>(c) * H : w_gate_col;
+  const uint16_t* brow[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = min(c0 + 16 * j + r, ncols - 1);
+    brow[j] = (c < E) ? w_router + static_cast<size_t>(c) * H : w_gate_col;
+  }
   const int nch = H / 128;
-  const int kb = (wave * nch) / 4, ke = ((wave + 1) * nch) / 4;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int pb = (part * nch) / parts, pe = ((part + 1) * nch) / parts;
+  const int kb = pb + (wave * (pe - pb)) / 4, ke = pb + ((wave + 1) * (pe - pb)) / 4;
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   for (int kc = kb; kc < ke; ++kc) {
     const int k = kc * 128 + 32 * g;
-    uint4 a[4], b[4];
+    uint4 a[4], b[2][4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      a[s] = *reinterpret_cast<const uint4*>(arow + k + 8 * s);
-      b[s] = *reinterpret_cast<const uint4*>(brow + k + 8 * s);
+    for (int q = 0; q < 4; ++q) {
+      a[q] = *reinterpret_cast<const uint4*>(arow + k + 8 * q);
+      b[0][q] = *reinterpret_cast<const uint4*>(brow[0] + k + 8 * q);
+      b[1][q] = *reinterpret_cast<const uint4*>(brow[1] + k + 8 * q);
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) acc = mfma_bf16_16x16x32(a[s], b[s], acc);
+    for (int q = 0; q < 4; ++q) {
+      acc[0] = mfma_bf16_16x16x32(a[q], b[0][q], acc[0]);
+      acc[1] = mfma_bf16_16x16x32(a[q], b[1][q], acc[1]);
+    }
   }
-  red[wave][lane] = acc;
+  red[wave][0][lane] = acc[0];
+  red[wave][1][lane] = acc[1];
   __syncthreads();
-  if (wave == 0) {
-    f32x4 s = red[0][lane];
+  if (wave < 2) {
+    const int j = wave;
+    f32x4 sum = red[0][j][lane];
 #pragma unroll
     for (int w = 1; w < 4; ++w) {
-      f32x4 o = red[w][lane];
-      s[0] += o[0]; s[1] += o[1]; s[2] += o[2]; s[3] += o[3];
+      const f32x4 o = red[w][j][lane];
+      sum[0] += o[0]; sum[1] += o[1]; sum[2] += o[2]; sum[3] += o[3];
     }
-    const int col = c0 + mfma16_col(lane);
+    const int col = c0 + 16 * j + mfma16_col(lane);
+    float* zp = z + static_cast<size_t>(part) * plane;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = t0 + mfma16_row(lane, i);
-      if (row < T && col < ncols) z[static_cast<size_t>(row) * ldz + col] = s[i];
+      if (row < T && col < ncols) zp[static_cast<size_t>(row) * ldz + col] = sum[i];
     }
   }
 }
@@ -85,20 +103,26 @@ __global__ void __launch_bounds__(256) router_logits_f32_kernel(
 // order.  Weights: exp(z_k - z_max) over the K picks, divided by their sum
 // (renormalised top-k) or by the sum over all E experts (plain softmax).
 __global__ void __launch_bounds__(256) topk_kernel(
-    const float* __restrict__ z, int ldz, const float* __restrict__ bias, int T, int E, int K,
-    int norm_topk, int has_shared, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+    const float* __restrict__ z, int ldz, int parts, size_t plane, const float* __restrict__ bias, int T,
+    int E, int K, int norm_topk, int has_shared, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
     float* __restrict__ shared_gate) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* zr = z + static_cast<size_t>(t) * ldz;
+  // Logit of column c: the partial planes added in order 0..parts-1.
+  auto logit = [&](int c) {
+    float s = zr[c];
+    for (int p = 1; p < parts; ++p) s += zr[static_cast<size_t>(p) * plane + c];
+    return s;
+  };
   float v[kMaxExperts / kWave];
 #pragma unroll
   for (int j = 0; j < kMaxExperts / kWave; ++j) {
     const int e = lane + kWave * j;
     float val = -INFINITY;
     if (e < E) {
-      val = zr[e];
+      val = logit(e);
       if (bias) val += bias[static_cast<size_t>(t) * E + e];
     }
     v[j] = val;
@@ -147,7 +171,7 @@ __global__ void __launch_bounds__(256) topk_kernel(
     topk_ids[static_cast<size_t>(t) * K + lane] = my_id;
     topk_w[static_cast<size_t>(t) * K + lane] = p / denom;
   }
-  if (has_shared && lane == 0) shared_gate[t] = 1.0f / (1.0f + expf(-zr[E]));
+  if (has_shared && lane == 0) shared_gate[t] = 1.0f / (1.0f + expf(-logit(E)));
 }
 
 // ------------------------------------------------------------------ expert budget

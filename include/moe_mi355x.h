@@ -149,28 +149,35 @@ int moe_dispatch(const moe_config* cfg, int32_t num_tokens, const int32_t* topk_
  * group-128 scales (FP8).  Accumulation is float32.  Each routed slot's
  * down-projection row is kept in the workspace and the slots of a token are
  * added to y in slot order after the shared term, so y is bit-reproducible
- * (no atomics).  Slots with weight 0 (dropped by the budget) are skipped. */
+ * (no atomics).  Slots with weight 0 (dropped by the budget) are skipped.
+ * y_act (device) out [T, H] or NULL: the optional cast of y to the activation
+ * dtype, for a caller whose next layer takes activations in that dtype.  BF16
+ * activations: y rounded to bfloat16 to nearest, ties to even (NaN stays NaN);
+ * F32 activations: a copy of y.  Written from the same float32 values as y, in
+ * the same pass; y itself stays float32 (the layer's result is defined before
+ * any rounding).  y_act must be aligned to its element size
+ * (MOE_ERR_UNSUPPORTED otherwise). */
 int moe_forward(const moe_config* cfg, int32_t num_tokens, const void* x,
                 const float* topk_weights, const float* shared_gate,
                 const int32_t* expert_counts, const int32_t* expert_offsets, const int32_t* perm,
                 const moe_expert_weights* weights /* (host) struct of (device) pointers */,
-                float* y, void* workspace, size_t workspace_bytes, void* stream);
+                float* y, void* y_act, void* workspace, size_t workspace_bytes, void* stream);
 
 /* The two halves of moe_forward, same arguments, for callers that time or
  * overlap them: gate_up writes the intermediate activations to the workspace
- * (y is not touched); down reads them, writes the per-slot outputs to the
- * workspace and then y.  Calling gate_up then down on one stream with one
- * workspace equals moe_forward. */
+ * (y and y_act are not touched); down reads them, writes the per-slot outputs to
+ * the workspace and then y (and y_act if not NULL).  Calling gate_up then down
+ * on one stream with one workspace equals moe_forward. */
 int moe_forward_gate_up(const moe_config* cfg, int32_t num_tokens, const void* x,
                         const float* topk_weights, const float* shared_gate,
                         const int32_t* expert_counts, const int32_t* expert_offsets,
                         const int32_t* perm, const moe_expert_weights* weights, float* y,
-                        void* workspace, size_t workspace_bytes, void* stream);
+                        void* y_act, void* workspace, size_t workspace_bytes, void* stream);
 int moe_forward_down(const moe_config* cfg, int32_t num_tokens, const void* x,
                      const float* topk_weights, const float* shared_gate,
                      const int32_t* expert_counts, const int32_t* expert_offsets,
                      const int32_t* perm, const moe_expert_weights* weights, float* y,
-                     void* workspace, size_t workspace_bytes, void* stream);
+                     void* y_act, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* moe_status_string(int status);

@@ -63,7 +63,7 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_size.argtypes = [cfgp, i32, ctypes.POINTER(sz)]
         L.moe_route.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_dispatch.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, sz, vp]
-        fwd = [cfgp, i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(_Weights), vp, vp, sz, vp]
+        fwd = [cfgp, i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(_Weights), vp, vp, vp, sz, vp]
         for name in ("moe_forward", "moe_forward_gate_up", "moe_forward_down"):
             getattr(L, name).argtypes = fwd
         for name in ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_forward",
@@ -194,31 +194,34 @@ def expert_weights_struct(cfg: MoEConfig, w: Dict[str, torch.Tensor],
 
 
 def _forward_call(name, cfg, x, topk_weights, shared_gate, counts, offsets, perm, weights, y,
-                  workspace, stream):
+                  workspace, stream, y_act=None):
     T, H = x.shape[0], cfg.hidden_size
     _expect(y, (T, H), torch.float32, "y")
     _expect(topk_weights, (T, cfg.num_experts_per_tok), torch.float32, "topk_weights")
+    if y_act is not None:
+        act = torch.bfloat16 if cfg.act_dtype == "bf16" else torch.float32
+        _expect(y_act, (T, H), act, "y_act")
     _check(getattr(lib(), name)(ctypes.byref(cfg.c()), T, _ptr(x), _ptr(topk_weights), _ptr(shared_gate),
                                 _ptr(counts), _ptr(offsets), _ptr(perm), ctypes.byref(weights), _ptr(y),
-                                _ptr(workspace), workspace.numel(), _stream(stream)), name)
+                                _ptr(y_act), _ptr(workspace), workspace.numel(), _stream(stream)), name)
 
 
 def forward(cfg, x, topk_weights, shared_gate, counts, offsets, perm, weights: _Weights, y, workspace,
-            stream=None) -> None:
+            stream=None, y_act=None) -> None:
     _forward_call("moe_forward", cfg, x, topk_weights, shared_gate, counts, offsets, perm, weights, y,
-                  workspace, stream)
+                  workspace, stream, y_act)
 
 
 def forward_gate_up(cfg, x, topk_weights, shared_gate, counts, offsets, perm, weights, y, workspace,
-                    stream=None) -> None:
+                    stream=None, y_act=None) -> None:
     _forward_call("moe_forward_gate_up", cfg, x, topk_weights, shared_gate, counts, offsets, perm,
-                  weights, y, workspace, stream)
+                  weights, y, workspace, stream, y_act)
 
 
 def forward_down(cfg, x, topk_weights, shared_gate, counts, offsets, perm, weights, y, workspace,
-                 stream=None) -> None:
+                 stream=None, y_act=None) -> None:
     _forward_call("moe_forward_down", cfg, x, topk_weights, shared_gate, counts, offsets, perm,
-                  weights, y, workspace, stream)
+                  weights, y, workspace, stream, y_act)
 
 
 class MoELayer:
@@ -228,7 +231,7 @@ class MoELayer:
     def __init__(self, cfg: MoEConfig, weights: Dict[str, torch.Tensor], w_router: torch.Tensor,
                  w_shared_gate: Optional[torch.Tensor] = None,
                  shared: Optional[Dict[str, torch.Tensor]] = None, max_tokens: int = 1,
-                 device: str = "cuda"):
+                 device: str = "cuda", act_output: bool = False):
         self.cfg = cfg
         self.weights_dict, self.shared_dict = weights, shared
         self.weights = expert_weights_struct(cfg, weights, shared)
@@ -245,11 +248,15 @@ class MoELayer:
         self.offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
         self.perm = torch.empty(max_tokens * K, dtype=torch.int32, device=dev)
         self.y = torch.empty(max_tokens, cfg.hidden_size, dtype=torch.float32, device=dev)
+        # Optional copy of y in the activation dtype (written by the same pass).
+        act = torch.bfloat16 if cfg.act_dtype == "bf16" else torch.float32
+        self.y_act = torch.empty(max_tokens, cfg.hidden_size, dtype=act, device=dev) if act_output else None
 
     def views(self, T: int):
         K = self.cfg.num_experts_per_tok
         return dict(topk_ids=self.topk_ids[:T], topk_weights=self.topk_weights[:T],
-                    shared_gate=self.shared_gate[:T], perm=self.perm[:T * K], y=self.y[:T])
+                    shared_gate=self.shared_gate[:T], perm=self.perm[:T * K], y=self.y[:T],
+                    y_act=None if self.y_act is None else self.y_act[:T])
 
     def route(self, x, logit_bias=None, stream=None):
         v = self.views(x.shape[0])
@@ -266,7 +273,7 @@ class MoELayer:
         sg = v["shared_gate"] if self.cfg.shared_expert_intermediate_size > 0 else None
         fn = {None: forward, "gate_up": forward_gate_up, "down": forward_down}[half]
         fn(self.cfg, x, v["topk_weights"], sg, self.counts, self.offsets, v["perm"], self.weights, v["y"],
-           self.workspace, stream)
+           self.workspace, stream, v["y_act"])
 
     def __call__(self, x, logit_bias=None, stream=None) -> torch.Tensor:
         if x.shape[0] > self.max_tokens:

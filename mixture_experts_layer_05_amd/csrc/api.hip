@@ -108,6 +108,12 @@ T* at(void* base, size_t off) {
 int launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH_FAILED; }
 
 // Returns MOE_OK for T = 0 without looking at any pointer (nothing is read or written).
+// The optional activation-dtype output must be aligned to its element size.
+int check_act_output(const moe_config& c, const void* y_act) {
+  const uintptr_t size = c.act_dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  return (y_act && reinterpret_cast<uintptr_t>(y_act) % size != 0) ? MOE_ERR_UNSUPPORTED : MOE_OK;
+}
+
 int check_forward(const moe_config* cfg, int32_t T, const void* x, const float* topk_w,
                   const float* shared_gate, const int32_t* counts, const int32_t* offsets,
                   const int32_t* perm, const moe_expert_weights* w, float* y) {
@@ -281,8 +287,9 @@ int moe_dispatch(const moe_config* cfg, int32_t T, const int32_t* topk_ids, int3
 
 int moe_forward_gate_up(const moe_config* cfg, int32_t T, const void* x, const float* topk_w,
                         const float* shared_gate, const int32_t* counts, const int32_t* offsets,
-                        const int32_t* perm, const moe_expert_weights* w, float* y, void* ws,
+                        const int32_t* perm, const moe_expert_weights* w, float* y, void* y_act, void* ws,
                         size_t ws_bytes, void* stream) {
+  (void)y_act;   // written by the down half only
   int st = check_forward(cfg, T, x, topk_w, shared_gate, counts, offsets, perm, w, y);
   if (st || T == 0) return st;
   Layout L;
@@ -301,27 +308,34 @@ int moe_forward_gate_up(const moe_config* cfg, int32_t T, const void* x, const f
 
 int moe_forward_down(const moe_config* cfg, int32_t T, const void* x, const float* topk_w,
                      const float* shared_gate, const int32_t* counts, const int32_t* offsets,
-                     const int32_t* perm, const moe_expert_weights* w, float* y, void* ws,
+                     const int32_t* perm, const moe_expert_weights* w, float* y, void* y_act, void* ws,
                      size_t ws_bytes, void* stream) {
   int st = check_forward(cfg, T, x, topk_w, shared_gate, counts, offsets, perm, w, y);
   if (st || T == 0) return st;
+  if ((st = check_act_output(*cfg, y_act))) return st;
   Layout L;
   if ((st = check_workspace(*cfg, T, ws, ws_bytes, &L))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const ExpertArgs a = expert_args(*cfg, T, x, topk_w, shared_gate, counts, offsets, perm, *w, y, ws, L);
+  ExpertArgs a = expert_args(*cfg, T, x, topk_w, shared_gate, counts, offsets, perm, *w, y, ws, L);
+  a.y_act = y_act;
+  a.act_bf16 = cfg->act_dtype == MOE_DTYPE_BF16 ? 1 : 0;
   if ((st = launched(launch_down(a, cfg->weight_dtype, s)))) return st;
   return launched(launch_combine(a, s));
 }
 
 int moe_forward(const moe_config* cfg, int32_t T, const void* x, const float* topk_w,
                 const float* shared_gate, const int32_t* counts, const int32_t* offsets,
-                const int32_t* perm, const moe_expert_weights* w, float* y, void* ws, size_t ws_bytes,
-                void* stream) {
-  int st = moe_forward_gate_up(cfg, T, x, topk_w, shared_gate, counts, offsets, perm, w, y, ws,
+                const int32_t* perm, const moe_expert_weights* w, float* y, void* y_act, void* ws,
+                size_t ws_bytes, void* stream) {
+  // Everything the down half checks is checked before the gate/up half launches.
+  int st = check_forward(cfg, T, x, topk_w, shared_gate, counts, offsets, perm, w, y);
+  if (st || T == 0) return st;
+  if ((st = check_act_output(*cfg, y_act))) return st;
+  st = moe_forward_gate_up(cfg, T, x, topk_w, shared_gate, counts, offsets, perm, w, y, y_act, ws,
                                ws_bytes, stream);
   if (st) return st;
-  return moe_forward_down(cfg, T, x, topk_w, shared_gate, counts, offsets, perm, w, y, ws, ws_bytes,
-                          stream);
+  return moe_forward_down(cfg, T, x, topk_w, shared_gate, counts, offsets, perm, w, y, y_act, ws,
+                          ws_bytes, stream);
 }
 
 }  // extern "C"

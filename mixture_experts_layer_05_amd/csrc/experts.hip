@@ -88,15 +88,23 @@ __global__ void __launch_bounds__(256) down_f32_kernel(ExpertArgs a) {
 
 // y[t,:] (+)= sum over k of w[t,k] * o[t*K+k,:], k ascending, skipping dropped
 // slots (weight 0, row never written).  `accumulate` adds onto the shared
-// expert's term already stored in y.  One workgroup per token.
+// expert's term already stored in y.  If y_act is not null the same values also
+// go there in the activation dtype.  One workgroup per token.
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ o,
                                                       const float* __restrict__ topk_w,
-                                                      float* __restrict__ y, int T, int H, int K,
-                                                      int accumulate) {
+                                                      float* __restrict__ y, void* __restrict__ y_act,
+                                                      int act_bf16, int T, int H, int K, int accumulate) {
+  // The optional activation-dtype copy of an output element: bf16 rounded to
+  // nearest (ties to even), or float32 as is.
+  auto put_act = [&](size_t i, float v) {
+    if (act_bf16) static_cast<uint16_t*>(y_act)[i] = f32_to_bf16_bits(v);
+    else static_cast<float*>(y_act)[i] = v;
+  };
   for (int t = blockIdx.x; t < T; t += gridDim.x) {
     const float* wr = topk_w + static_cast<size_t>(t) * K;
     const float* orow = o + static_cast<size_t>(t) * K * H;
     float* yr = y + static_cast<size_t>(t) * H;
+    const size_t row = static_cast<size_t>(t) * H;
     if ((H & 3) == 0) {
       const int h4 = H / 4;
       for (int c = threadIdx.x; c < h4; c += blockDim.x) {
@@ -111,6 +119,12 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
           s.w = fmaf(w, v.w, s.w);
         }
         reinterpret_cast<float4*>(yr)[c] = s;
+        if (y_act) {
+          put_act(row + 4 * c, s.x);
+          put_act(row + 4 * c + 1, s.y);
+          put_act(row + 4 * c + 2, s.z);
+          put_act(row + 4 * c + 3, s.w);
+        }
       }
     } else {
       for (int c = threadIdx.x; c < H; c += blockDim.x) {
@@ -120,10 +134,12 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
           if (w != 0.f) s = fmaf(w, orow[static_cast<size_t>(k) * H + c], s);
         }
         yr[c] = s;
+        if (y_act) put_act(row + c, s);
       }
     }
   }
 }
+
 
 // ---------------------------------------------------------------- fp8 activation quantiser
 
@@ -215,7 +231,8 @@ hipError_t launch_down(const ExpertArgs& a, int weight_dtype, hipStream_t stream
 
 hipError_t launch_combine(const ExpertArgs& a, hipStream_t stream) {
   const int grid = static_cast<int>(std::min<int64_t>(a.T, 4096));
-  combine_kernel<<<grid, 256, 0, stream>>>(a.o, a.topk_w, a.y, a.T, a.H, a.K, a.S > 0 ? 1 : 0);
+  combine_kernel<<<grid, 256, 0, stream>>>(a.o, a.topk_w, a.y, a.y_act, a.act_bf16, a.T, a.H, a.K,
+                                           a.S > 0 ? 1 : 0);
   return hipGetLastError();
 }
 

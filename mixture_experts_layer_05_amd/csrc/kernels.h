@@ -35,6 +35,8 @@ struct ExpertArgs {
   const float* hs;               // fp8: scales of h
   float* o;                      // [T*K, H] unweighted routed outputs, row = slot t*K+k
   float* y;                      // [T, H]
+  void* y_act;                   // [T, H] act dtype or null: the cast of y
+  int act_bf16;                  // y_act is bf16 (else float32)
   // Router logits (router mode of the streaming kernel): z[t, c] = x_t . col_c with
   // col_c = w_router[c] for c < E and col_E = w_gcol (the shared gate) if present.
   const void* w_router;          // [E, H]

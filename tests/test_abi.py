@@ -110,8 +110,8 @@ def _forward(cfg, T=4, name="moe_forward", y=FAKE, **ptrs):
             setattr(w, k, v)
     g = lambda k: ptrs.get(k, FAKE)  # noqa: E731
     return getattr(moe.lib(), name)(ctypes.byref(cfg.c()), T, g("x"), g("topk_w"), g("shared_gate"),
-                                    g("counts"), g("offsets"), g("perm"), ctypes.byref(w), y, g("ws"),
-                                    _ws(cfg, max(T, 0))[1], None)
+                                    g("counts"), g("offsets"), g("perm"), ctypes.byref(w), y,
+                                    ptrs.get("y_act"), g("ws"), _ws(cfg, max(T, 0))[1], None)
 
 
 def test_forward_validation():
@@ -123,6 +123,8 @@ def test_forward_validation():
         assert _forward(cfg, name=name, shared_gate=None) == NULL_PTR
         assert _forward(cfg, name=name, y=FAKE + 4) == UNSUPPORTED       # y must be 16-byte aligned
         assert _forward(cfg, name=name, T=0) == OK
+    # The optional bf16 output: 2-byte aligned (checked before anything launches).
+    assert _forward(cfg, name="moe_forward_down", y_act=FAKE + 1) == UNSUPPORTED
     fp8 = _cfg(weight_dtype="fp8_e4m3_g128")
     assert _forward(fp8) == NULL_PTR                                      # scales missing
     assert _forward(_cfg(shared_expert_intermediate_size=0), T=0, ws_gate=None, ws_up=None,

@@ -100,6 +100,11 @@ def test_tall_tiles_with_short_contractions():
     _run(SHORT_K, 600, 41)
 
 
+def test_tall_fp8_tiles_with_short_contractions():
+    # fp8 256-row tiles: gate/up over 2 scale groups, down over 1 (a one-stage pipeline).
+    _run(SHORT_K.with_(name="tiled_short_k_fp8", weight_dtype=W.DT_FP8), 600, 42)
+
+
 def test_k_equals_e_with_ragged_tokens():
     _run(EDGE, 13, 5)
 
@@ -172,3 +177,29 @@ def test_halves_equal_forward():
     layer.forward(x, half="down")
     torch.cuda.synchronize()
     assert Hn.rel_l2(layer.views(56)["y"].cpu().numpy(), y1.cpu().numpy()) < 1e-6
+
+
+@pytest.mark.parametrize("shape,T", [(W.DRAFTER, 56), (W.TINY, 40)])
+def test_activation_dtype_output(shape, T):
+    """The optional y_act output: the cast of the float32 y to the activation dtype."""
+    import mixture_experts_layer_05_amd as moe
+    print(f"\n[case] y_act {shape.name} T={T}", flush=True)
+    case = Hn.make_case(shape, T, 14)
+    sg = None if case.inp.w_shared_gate is None else case.inp.w_shared_gate.cuda()
+    layer = moe.MoELayer(Hn.config(shape), case.weights, case.inp.w_router.cuda(), sg, case.shared,
+                         max_tokens=T, act_output=True)
+    bias = None if case.inp.logit_bias is None else case.inp.logit_bias.cuda()
+    y = layer(case.inp.x.cuda(), bias)
+    torch.cuda.synchronize()
+    y_act = layer.views(T)["y_act"].cpu()
+    y_host = y.cpu()
+    if shape.act_dtype == W.DT_BF16:
+        # Bit-exact against torch's host cast (round to nearest, ties to even).
+        ref = y_host.to(torch.bfloat16)
+        assert torch.equal(y_act.view(torch.int16), ref.view(torch.int16))
+        # Against the oracle: bf16 rounding adds at most 2^-9 relative error per element.
+        ora = Hn.run_oracle(case)
+        err = Hn.rel_l2(y_act.float().numpy().astype(np.float64), ora["y"])
+        assert err <= Hn.TOL["bf16"] + 2.0 ** -9, err
+    else:
+        assert torch.equal(y_act, y_host)

@@ -35,7 +35,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="drafter",
-                   choices=["drafter", "narrow", "large", "large_fp8", "tiny"])
+                   choices=["drafter", "narrow", "large", "large_fp8", "tiny", "ep_rank"])
     p.add_argument("--tokens", type=int, default=None, help="T (default: the workload's bench size)")
     p.add_argument("--alpha", type=float, default=None, help="Zipf router skew for the large layers")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -53,6 +53,7 @@ def workload(args):
         "large": (W.LARGE, 3, 8192, 1.5),
         "large_fp8": (W.LARGE_FP8, 4, 8192, 1.5),
         "tiny": (W.TINY, 0, 64, None),
+        "ep_rank": (W.EP_RANK, 5, 4096, 1.5),
     }
     shape, idx, T, alpha = table[args.workload]
     if args.tokens is not None:
@@ -66,18 +67,19 @@ def weight_bytes_per_elem(shape) -> float:
     return {"f32": 4.0, "bf16": 2.0, "fp8_e4m3_g128": 1.0 + 4.0 / 128}[shape.weight_dtype]
 
 
-def accounting(shape, T, counts):
-    """Algorithmic FLOPs and bytes of one step (from the realised routing)."""
+def accounting(shape, T, counts, router=True):
+    """Algorithmic FLOPs and bytes of one step (from the realised routing).
+    `router` False: the step starts from given ids (no router GEMV)."""
     H, I, S, E = shape.hidden_size, shape.moe_intermediate_size, shape.shared_expert_intermediate_size, \
         shape.n_routed_experts
     slots = int(counts.sum())
     touched = int((counts > 0).sum())
     bw = weight_bytes_per_elem(shape)
     ba = 4.0 if shape.act_dtype == "f32" else 2.0
-    flops = 2.0 * T * H * (E + (1 if S else 0)) + 6.0 * H * I * slots + 6.0 * T * H * S
+    flops = 2.0 * T * H * (E + (1 if S else 0)) * router + 6.0 * H * I * slots + 6.0 * T * H * S
     gate_up_w = touched * 2.0 * I * H * bw + 2.0 * S * H * bw
     down_w = touched * 1.0 * H * I * bw + 1.0 * H * S * bw
-    router_w = (E + (1 if S else 0)) * H * ba
+    router_w = (E + (1 if S else 0)) * H * ba * router
     weights = gate_up_w + down_w + router_w
     x_bytes = T * H * ba
     y_bytes = T * H * 4.0
@@ -88,6 +90,18 @@ def accounting(shape, T, counts):
     return dict(flops=flops, weight_bytes=weights, total_bytes=weights + x_bytes + y_bytes,
                 gate_up_bytes=gate_up_bytes, touched=touched, slots=slots,
                 gate_up_flops=4.0 * H * I * slots + 4.0 * T * H * S)
+
+
+def layer_roofline(shape, a, ms_per_step):
+    """The whole layer against its binding roofline: t_HBM = algorithmic bytes at
+    8 TB/s, t_MFMA = algorithmic FLOPs at the weight dtype's dense peak; the
+    binding one is the larger, and frac = that time / the measured step."""
+    peak_tf = MFMA_PEAK_TFLOPS[shape.weight_dtype]
+    t_hbm = a["total_bytes"] / (HBM_PEAK_GBPS * 1e9) * 1e3
+    t_mfma = a["flops"] / (peak_tf * 1e12) * 1e3
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    return {"bound": bound, "t_hbm_ms": round(t_hbm, 5), "t_mfma_ms": round(t_mfma, 5),
+            "frac": round(max(t_hbm, t_mfma) / ms_per_step, 4)}
 
 
 def gate_up_kernel(shape, T: int) -> str:
@@ -192,6 +206,7 @@ def main():
 
     shape, idx, T, alpha = workload(args)
     seed = W.base_seed(idx, T)
+    ep_rank = shape.name == W.EP_RANK.name
     cfg = moe.MoEConfig(shape.hidden_size, shape.n_routed_experts, shape.moe_intermediate_size,
                         shape.num_experts_per_tok, shape.shared_expert_intermediate_size,
                         shape.weight_dtype, shape.act_dtype, shape.norm_topk_prob, shape.expert_budget)
@@ -200,23 +215,49 @@ def main():
     one = (shape.n_routed_experts * 3 * shape.hidden_size * shape.moe_intermediate_size
            + 3 * shape.hidden_size * shape.shared_expert_intermediate_size) * weight_bytes_per_elem(shape)
     n_copies = int(max(1, min(8, np.ceil(2.0e9 / one))))
-    inp = W.layer_inputs(shape, T, seed, alpha)
+    # ep_rank: the rank's inputs are the global layer's (x, router, Zipf bias).
+    inp = W.layer_inputs(W.LARGE if ep_rank else shape, T, seed, alpha)
     layers = []
     for c in range(n_copies):
         wts = W.stacked_expert_weights(shape, seed + 7919 * c, "cuda")
         shw = W.shared_expert_weights(shape, seed + 7919 * c, "cuda")
-        wr = W.router_weight(shape, seed + 7919 * c).to(dev) if c else inp.w_router.to(dev)
+        if ep_rank:   # the local layer's router is unused: routing is the global layer's
+            wr = inp.w_router[:W.EP_RANK_LOCAL].to(dev)
+        else:
+            wr = W.router_weight(shape, seed + 7919 * c).to(dev) if c else inp.w_router.to(dev)
         wg = inp.w_shared_gate.to(dev) if inp.w_shared_gate is not None else None
         layers.append(moe.MoELayer(cfg, wts, wr, wg, shw, max_tokens=T))
     x = inp.x.to(dev)
     bias = inp.logit_bias.to(dev) if inp.logit_bias is not None else None
     stream = torch.cuda.current_stream()
+    ep_slots = None
+    if ep_rank:
+        # Route the global layer once (every rank does this identically), keep the
+        # slots of the busiest rank's experts [32r, 32r + 32) and time dispatch +
+        # forward of that rank's share.
+        g = W.LARGE
+        gcfg = moe.MoEConfig(g.hidden_size, g.n_routed_experts, g.moe_intermediate_size,
+                             g.num_experts_per_tok, 0, g.weight_dtype, g.act_dtype, g.norm_topk_prob, 0)
+        gws = torch.empty(moe.workspace_size(gcfg, T), dtype=torch.uint8, device=dev)
+        gids = torch.empty(T, g.num_experts_per_tok, dtype=torch.int32, device=dev)
+        gw = torch.empty(T, g.num_experts_per_tok, dtype=torch.float32, device=dev)
+        moe.route(gcfg, x, inp.w_router.to(dev), None, bias, gids, gw, None, None, gws)
+        ep_slots = torch.bincount((gids // W.EP_RANK_LOCAL).flatten().long(), minlength=W.EP_RANKS)
+        rank = int(ep_slots.argmax())
+        lids = gids - rank * W.EP_RANK_LOCAL
+        local = (lids >= 0) & (lids < W.EP_RANK_LOCAL)
+        for L in layers:
+            L.topk_ids[:T].copy_(torch.where(local, lids, torch.full_like(lids, -1)))
+            L.topk_weights[:T].copy_(torch.where(local, gw, torch.zeros_like(gw)))
+        torch.cuda.synchronize()
+        ep_slots = {"rank": rank, "slots_per_rank": ep_slots.cpu().tolist()}
 
     def step(i, ev=None):
         L = layers[i % n_copies]
         if ev is not None:
             ev[0].record(stream)
-        L.route(x, bias)
+        if not ep_rank:
+            L.route(x, bias)
         L.dispatch(T)
         if ev is not None:
             ev[1].record(stream)
@@ -238,11 +279,12 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    step_ev = np.array([e[0].elapsed_time(e[3]) for e in evs])
     gate_up_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     down_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
     route_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
 
-    acc = [accounting(shape, T, L.counts.cpu().numpy()) for L in layers]
+    acc = [accounting(shape, T, L.counts.cpu().numpy(), router=not ep_rank) for L in layers]
     a = {k: float(np.mean([d[k] for d in acc])) for k in acc[0]}
     tokens_per_s = T / (ms_per_step * 1e-3)
     # Dominant kernel: gate/up + SwiGLU.  Below 48 rows per expert it runs on the
@@ -283,11 +325,15 @@ def main():
         "stage_ms": {"route_dispatch": round(route_ms, 5), "gate_up": round(gate_up_ms, 5),
                      "down": round(down_ms, 5)},
         "experts_touched": a["touched"],
+        # Per-step GPU time (events around route .. combine), percentiles over the timed steps.
+        "step_ms_p10_p50_p90": [round(float(np.percentile(step_ev, q)), 5) for q in (10, 50, 90)],
         "roofline": roof,
+        **({"ep": ep_slots} if ep_slots else {}),
+        "layer_roofline": layer_roofline(shape, a, ms_per_step),
     }
     if shape.weight_dtype != "f32" and a["gate_up_flops"] / (gate_up_ms * 1e-3) / 1e12 > 0:
         line["gate_up_tflops"] = round(a["gate_up_flops"] / (gate_up_ms * 1e-3) / 1e12, 2)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not ep_rank:
         L0 = layers[0]
         expert_cpu = lambda e: {k: v[e].cpu() for k, v in L0.weights_dict.items()}  # noqa: E731
         shared_cpu = None if L0.shared_dict is None else {k: v.cpu() for k, v in L0.shared_dict.items()}

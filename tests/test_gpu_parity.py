@@ -58,6 +58,68 @@ def test_large_layer_8192_skewed_sampled():
     _run(W.LARGE, 8192, W.base_seed(3, 8192), 1.5, tokens=Hn.sample_tokens(8192, 16))
 
 
+def test_expert_parallel_rank_share_sampled():
+    """One GPU's share of the large layer under 8-way expert parallelism: the global
+    256-expert routing, restricted to the busiest rank's experts [32r, 32r + 32)
+    (local id = id - 32r, other slots -1 with weight 0), then dispatch + forward of
+    the rank's 32-expert layer.  Both sides route the global layer on their own;
+    ids, counts, offsets and perm bit-exact, y on sampled tokens."""
+    import mixture_experts_layer_05_amd as moe
+    from oracle import moe as O
+    g, loc, T, alpha = W.LARGE, W.EP_RANK, 4096, 1.5
+    seed = W.base_seed(5, T)
+    print(f"\n[case] {loc.name} T={T} seed={seed} alpha={alpha}", flush=True)
+    inp = W.layer_inputs(g, T, seed, alpha)
+    Hn.condition_topk(g, inp)
+    K, E = g.num_experts_per_tok, W.EP_RANK_LOCAL
+    weights = W.stacked_expert_weights(loc, seed, "cuda")
+    x, bias = inp.x.cuda(), inp.logit_bias.cuda()
+
+    gcfg = Hn.config(g)
+    gws = torch.empty(moe.workspace_size(gcfg, T), dtype=torch.uint8, device="cuda")
+    gids = torch.empty(T, K, dtype=torch.int32, device="cuda")
+    gw = torch.empty(T, K, dtype=torch.float32, device="cuda")
+    moe.route(gcfg, x, inp.w_router.cuda(), None, bias, gids, gw, None, None, gws)
+    rank = int(torch.bincount((gids // E).flatten().long(), minlength=W.EP_RANKS).argmax())
+    lids = gids - rank * E
+    local = (lids >= 0) & (lids < E)
+    layer = moe.MoELayer(Hn.config(loc), weights, inp.w_router[:E].cuda(), None, None, max_tokens=T)
+    layer.topk_ids.copy_(torch.where(local, lids, torch.full_like(lids, -1)))
+    layer.topk_weights.copy_(torch.where(local, gw, torch.zeros_like(gw)))
+    layer.dispatch(T)
+    layer.forward(x)
+    torch.cuda.synchronize()
+    ids_g = layer.topk_ids.cpu().numpy()
+    nkept = int(layer.offsets[-1].item())
+
+    r = O.route(inp.x, inp.w_router, None, inp.logit_bias, K, bool(g.norm_topk_prob), 0)
+    rank_o = int(np.argmax(np.bincount(r["ids"].ravel() // E, minlength=W.EP_RANKS)))
+    assert rank_o == rank
+    lid = r["ids"] - rank_o * E
+    keep = (lid >= 0) & (lid < E)
+    ids_o = np.where(keep, lid, -1)
+    w_o = np.where(keep, r["w"], 0.0)
+    assert np.array_equal(ids_g, ids_o), "rank-local expert ids differ"
+    werr = float(np.abs(layer.topk_weights.cpu().numpy() - w_o).max())
+    assert werr <= Hn.W_TOL, werr
+    counts, offsets, perm = O.dispatch(ids_o, E)
+    assert np.array_equal(layer.counts.cpu().numpy(), counts)
+    assert np.array_equal(layer.offsets.cpu().numpy(), offsets)
+    assert np.array_equal(layer.perm[:nkept].cpu().numpy(), perm)
+    assert 0 < nkept < T * K
+    # Sampled tokens, plus tokens the rank receives nothing for (their y must be 0).
+    tokens = Hn.sample_tokens(T, 16)
+    expert_cpu = lambda e: {k: v[e].cpu() for k, v in weights.items()}  # noqa: E731
+    y_o = O.moe_combine(inp.x, ids_o, w_o, None, expert_cpu, None, loc.weight_dtype, tokens)
+    y_g = layer.y.cpu().numpy().astype(np.float64)
+    err = Hn.rel_l2(y_g[tokens], y_o)
+    assert err <= Hn.TOL[loc.weight_dtype], err
+    empty = (ids_o < 0).all(axis=1)
+    assert empty.any() and (y_g[empty] == 0).all()
+    print(f"[case] ok y_rel_l2={err:.3e} w_max_abs={werr:.1e} rank={rank} kept={nkept} of {T * K} slots",
+          flush=True)
+
+
 def test_fp8_budget_layer_8192_sampled():
     case, gpu, ora, errs = _run(W.LARGE_FP8, 8192, W.base_seed(4, 8192), 1.5,
                                 tokens=Hn.sample_tokens(8192, 16))

@@ -68,7 +68,19 @@ NARROW = LayerShape("narrow_512x512_top10_shared2048", 5120, 512, 512, 10, 2048,
 LARGE = LayerShape("large_256x2048_top8_h7168", 7168, 256, 2048, 8, 0, DT_BF16, DT_BF16)
 LARGE_FP8 = LARGE.with_(name="large_fp8_budget64", weight_dtype=DT_FP8, expert_budget=64)
 
-SHAPES = [TINY, DRAFTER, NARROW, LARGE, LARGE_FP8]
+# One GPU's share of the large layer sharded over 8 GPUs by experts: rank r
+# holds experts [32r, 32r + 32) of the 256 (H 7168, I 2048) and receives, for a
+# 4096-token batch (512 tokens per rank x 8 ranks), every (token, slot) of the
+# global top-8 routing whose expert is one of its own.  Its problem is this
+# 32-expert layer with K = 8 slots per token, local id = global id - 32r, the
+# non-local slots marked -1 (weight 0).  The ids come from routing the global
+# layer (LARGE inputs); the caller picks the rank that receives the most slots,
+# which sets the step time of an expert-parallel layer.
+EP_RANK_LOCAL = 32
+EP_RANKS = 8
+EP_RANK = LARGE.with_(name="ep_rank_32of256x2048_top8_h7168", n_routed_experts=EP_RANK_LOCAL)
+
+SHAPES = [TINY, DRAFTER, NARROW, LARGE, LARGE_FP8, EP_RANK]
 
 TOKENS = {
     TINY.name: (64,),
@@ -76,8 +88,9 @@ TOKENS = {
     NARROW.name: (7, 56, 224),
     LARGE.name: (512, 2048, 8192),
     LARGE_FP8.name: (8192,),
+    EP_RANK.name: (4096,),
 }
-ALPHAS = {LARGE.name: (0.0, 1.0, 1.5), LARGE_FP8.name: (1.5,)}
+ALPHAS = {LARGE.name: (0.0, 1.0, 1.5), LARGE_FP8.name: (1.5,), EP_RANK.name: (1.5,)}
 
 DRAFT_BLOCK = 7                        # speculative block size
 DRAFTER_BIAS_SCALES = (0.0, 1.0, 2.0, 4.0, 8.0)  # per-block bias scale choices

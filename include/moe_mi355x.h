@@ -156,7 +156,10 @@ int moe_dispatch(const moe_config* cfg, int32_t num_tokens, const int32_t* topk_
  * F32 activations: a copy of y.  Written from the same float32 values as y, in
  * the same pass; y itself stays float32 (the layer's result is defined before
  * any rounding).  y_act must be aligned to its element size
- * (MOE_ERR_UNSUPPORTED otherwise). */
+ * (MOE_ERR_UNSUPPORTED otherwise).  Size limit: x (T * H activations) and the
+ * intermediate activations ((T * K * I + T * S) elements, 2 bytes each with BF16
+ * weights, else 4) must each stay below 3 GiB (MOE_ERR_UNSUPPORTED otherwise);
+ * the kernels address them with 32-bit offsets. */
 int moe_forward(const moe_config* cfg, int32_t num_tokens, const void* x,
                 const float* topk_weights, const float* shared_gate,
                 const int32_t* expert_counts, const int32_t* expert_offsets, const int32_t* perm,

@@ -18,6 +18,8 @@ constexpr int32_t kRouterTiledTokens = 4096;
 // Router contraction split for decode-sized batches (see moe_route).
 constexpr int32_t kRouterPlaneTokens = 1024;
 constexpr int kRouterParts = 8;
+// Upper bound (exclusive) on the byte size of x and of h; see check_forward.
+constexpr int64_t kMaxActivationBytes = 3LL << 30;
 
 bool valid_dtype(int d) { return d == MOE_DTYPE_F32 || d == MOE_DTYPE_BF16 || d == MOE_DTYPE_FP8_E4M3_G128; }
 
@@ -121,6 +123,13 @@ int check_forward(const moe_config* cfg, int32_t T, const void* x, const float* 
   if (st) return st;
   if ((st = check_tokens(cfg, T))) return st;
   if (T == 0) return MOE_OK;
+  // The expert kernels address x and h (per-slot activations) with 32-bit byte
+  // offsets, and keep offsets from 3 GiB up free to mark rows that load zeros.
+  const int64_t xbytes = static_cast<int64_t>(T) * cfg->hidden_size * (cfg->act_dtype == MOE_DTYPE_F32 ? 4 : 2);
+  const int64_t hbytes = (static_cast<int64_t>(T) * cfg->num_experts_per_tok * cfg->moe_intermediate_size +
+                          static_cast<int64_t>(T) * cfg->shared_expert_intermediate_size) *
+                         (cfg->weight_dtype == MOE_DTYPE_BF16 ? 2 : 4);
+  if (xbytes >= kMaxActivationBytes || hbytes >= kMaxActivationBytes) return MOE_ERR_UNSUPPORTED;
   if (!x || !topk_w || !counts || !offsets || !perm || !w || !y) return MOE_ERR_NULL_PTR;
   if (!w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_NULL_PTR;
   const bool fp8 = cfg->weight_dtype == MOE_DTYPE_FP8_E4M3_G128;
@@ -213,7 +222,9 @@ int moe_route(const moe_config* cfg, int32_t T, const void* x, const void* w_rou
   float* z = at<float>(ws, L.z);
   int parts = 1;                                            // logit planes written
   const size_t plane = static_cast<size_t>(T) * L.ldz;      // floats between planes
-  if (cfg->act_dtype == MOE_DTYPE_BF16 && T >= kRouterTiledTokens) {
+  // The LDS-staged router addresses x with 32-bit offsets (below 3 GiB).
+  const bool x_fits = static_cast<int64_t>(T) * H * 2 < kMaxActivationBytes;
+  if (cfg->act_dtype == MOE_DTYPE_BF16 && T >= kRouterTiledTokens && x_fits) {
     ExpertArgs r{};
     r.x = x;
     r.w_router = w_router;

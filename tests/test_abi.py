@@ -131,6 +131,20 @@ def test_forward_validation():
                     ws_down=None, shared_gate=None) == OK
 
 
+def test_forward_size_limit():
+    # x and the intermediate activations are addressed with 32-bit offsets: each
+    # must stay below 3 GiB, checked before anything launches.
+    big = dict(hidden_size=7168, moe_intermediate_size=2048, n_routed_experts=256, num_experts_per_tok=8,
+               shared_expert_intermediate_size=0)
+    for name in ("moe_forward", "moe_forward_gate_up", "moe_forward_down"):
+        # h: 110000 * 8 * 2048 bf16 = 3.6 GB
+        assert _forward(_cfg(**big), T=110000, name=name, ws_gate=None, ws_up=None, ws_down=None,
+                        shared_gate=None) == UNSUPPORTED
+        # x: 230000 * 7168 bf16 = 3.3 GB
+        assert _forward(_cfg(**dict(big, moe_intermediate_size=128, num_experts_per_tok=1)), T=230000,
+                        name=name, ws_gate=None, ws_up=None, ws_down=None, shared_gate=None) == UNSUPPORTED
+
+
 def test_dispatch_validation():
     lib = moe.lib()
     cfg = _cfg()

@@ -128,22 +128,38 @@ def gate_up_kernel(shape, T: int) -> str:
     return f"stream_expert_kernel<GateUp, {cfg}, {'fp8' if fp8 else 'bf16'}>"
 
 
-def library_source_hash() -> str:
-    """sha256 over the HIP sources: the kernels that a stored counter reading describes."""
+def kernel_source_file(kernel_label: str) -> str:
+    """HIP source file that holds the kernel named by a roofline label."""
+    if kernel_label.startswith("stream"):
+        return "stream_gemm.hip"
+    if kernel_label.startswith("tiled"):
+        return "tile_gemm.hip"
+    return "experts.hip"
+
+
+def library_source_hash(kernel_file: str = None) -> str:
+    """sha256 over the HIP sources a stored counter reading depends on: the kernel's
+    own file, the shared headers and the launch code (experts.hip, api.hip); all
+    sources if no file is named."""
     import glob
     import hashlib
+    csrc = os.path.join(ROOT, "mixture_experts_layer_05_amd", "csrc")
+    files = sorted(glob.glob(os.path.join(csrc, "*")))
+    if kernel_file is not None:
+        keep = {kernel_file, "experts.hip", "api.hip"}
+        files = [f for f in files if f.endswith(".h") or os.path.basename(f) in keep]
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "mixture_experts_layer_05_amd", "csrc", "*"))):
+    for f in files:
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode())
             h.update(fh.read())
     return h.hexdigest()
 
 
-def stored_traffic(kernel: str, workload: str):
+def stored_traffic(kernel: str, workload: str, kernel_file: str):
     """HBM bytes per launch of `kernel` on `workload` from the committed counter summary
     (profiles/<kernel>_<workload>_traffic.md), or None if there is none or the
-    kernels changed since it was taken."""
+    sources it depends on changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
@@ -152,7 +168,7 @@ def stored_traffic(kernel: str, workload: str):
         if ":" in line and line.startswith("- "):
             k, v = line[2:].split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
-    if fields.get("source_sha256") != library_source_hash():
+    if fields.get("source_sha256") != library_source_hash(kernel_file):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -296,12 +312,14 @@ def main():
         peak = MFMA_PEAK_TFLOPS[shape.weight_dtype]
         roof = {"bound": "mfma", "kernel": gate_up_kernel(shape, T), "achieved": round(achieved, 1),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": stored_traffic("gate_up", f"{args.workload}_T{T}")}
+                "traffic": stored_traffic("gate_up", f"{args.workload}_T{T}",
+                                          kernel_source_file(gate_up_kernel(shape, T)))}
     else:
         achieved = a["gate_up_bytes"] / (gate_up_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": gate_up_kernel(shape, T), "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": stored_traffic("gate_up", f"{args.workload}_T{T}")}
+                "traffic": stored_traffic("gate_up", f"{args.workload}_T{T}",
+                                          kernel_source_file(gate_up_kernel(shape, T)))}
     line = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),

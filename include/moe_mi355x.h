@@ -84,6 +84,10 @@ typedef struct moe_config {
   int32_t norm_topk_prob;                  /* 1: renormalise the kept top-k weights to sum 1 */
   int32_t expert_budget;                   /* B >= 0, 0 = off: cap on distinct routed experts
                                               over the whole batch [colibri issue_budget.md] */
+  float top_p;                             /* 0 <= p <= 1, 0 or 1 = off: per-token trim of the
+                                              top-k to its top-p mass before the budget
+                                              [colibri issue_budget.md, "Relationship to
+                                              existing features"] */
 } moe_config;
 
 /* Expert weights, all (device).  The contraction dimension is contiguous.
@@ -108,7 +112,12 @@ int moe_workspace_size(const moe_config* cfg, int32_t max_tokens, size_t* bytes)
 /* Router: logits z[t,e] = x_t . w_router[e] (+ logit_bias[t,e]) accumulated in
  * float32; softmax over the E experts, keep the K largest (ties: lower expert
  * id), renormalise them to sum 1 if norm_topk_prob [SpecForge PR #943,
- * "Modifications": softmax, renormalised top-k]; then, if expert_budget > 0 and
+ * "Modifications": softmax, renormalised top-k]; then, if 0 < top_p < 1, trim
+ * each token to the shortest prefix of its picks (by descending probability)
+ * whose summed probability reaches top_p times the summed probability of all K
+ * picks, and renormalise the kept ones if norm_topk_prob [colibri
+ * issue_budget.md, "Relationship to existing features": the per-position trim
+ * runs before the budget]; then, if expert_budget > 0 and
  * the batch uses more than B distinct experts, keep the B experts with the
  * largest summed weight (ties: lower id), drop the other slots and renormalise
  * each token's kept weights [colibri issue_budget.md, "How it works" steps 1-5].
@@ -123,7 +132,9 @@ int moe_workspace_size(const moe_config* cfg, int32_t max_tokens, size_t* bytes)
  *                iff S > 0, else ignored
  *   route_stats  (device) out int32[4] or NULL: {distinct experts before the
  *                budget, after, dropped slots, tokens left with no expert}
- * A token that loses every expert to the budget keeps ids -1 / weights 0. */
+ * A token that loses every expert to the budget keeps ids -1 / weights 0.  The
+ * top-p trim always keeps the first pick; its dropped slots are id -1 / weight 0
+ * at the end of the row and are not counted in route_stats. */
 int moe_route(const moe_config* cfg, int32_t num_tokens, const void* x, const void* w_router,
               const void* w_shared_gate, const float* logit_bias, int32_t* topk_ids,
               float* topk_weights, float* shared_gate, int32_t* route_stats, void* workspace,

@@ -39,7 +39,7 @@ class _Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "hidden_size", "n_routed_experts", "moe_intermediate_size", "num_experts_per_tok",
         "shared_expert_intermediate_size", "weight_dtype", "act_dtype", "norm_topk_prob",
-        "expert_budget")]
+        "expert_budget")] + [("top_p", ctypes.c_float)]
 
 
 class _Weights(ctypes.Structure):
@@ -95,12 +95,13 @@ class MoEConfig:
     act_dtype: str = "bf16"
     norm_topk_prob: int = 1
     expert_budget: int = 0
+    top_p: float = 0.0
 
     def c(self) -> _Config:
         return _Config(self.hidden_size, self.n_routed_experts, self.moe_intermediate_size,
                        self.num_experts_per_tok, self.shared_expert_intermediate_size,
                        DTYPES[self.weight_dtype], DTYPES[self.act_dtype], self.norm_topk_prob,
-                       self.expert_budget)
+                       self.expert_budget, self.top_p)
 
     @property
     def act_torch_dtype(self) -> torch.dtype:

@@ -36,6 +36,7 @@ int check_config(const moe_config* c) {
       (c->norm_topk_prob != 0 && c->norm_topk_prob != 1))
     return MOE_ERR_BAD_SHAPE;
   if (c->num_experts_per_tok > c->n_routed_experts) return MOE_ERR_BAD_SHAPE;
+  if (!(c->top_p >= 0.f && c->top_p <= 1.f)) return MOE_ERR_BAD_SHAPE;   // also rejects NaN
   if (c->n_routed_experts > kMaxExperts || c->num_experts_per_tok > kMaxTopK) return MOE_ERR_UNSUPPORTED;
   if (c->weight_dtype != MOE_DTYPE_F32) {
     if (c->hidden_size % 128 || c->moe_intermediate_size % 128 ||
@@ -257,8 +258,9 @@ int moe_route(const moe_config* cfg, int32_t T, const void* x, const void* w_rou
   }
   if ((st = launched(hipGetLastError()))) return st;
   topk_kernel<<<static_cast<unsigned>(ceil_div(T, 4)), 256, 0, s>>>(
-      z, L.ldz, parts, plane, logit_bias, T, E, K, cfg->norm_topk_prob, has_shared ? 1 : 0, topk_ids,
-      topk_w, shared_gate);
+      z, L.ldz, parts, plane, logit_bias, T, E, K, cfg->norm_topk_prob,
+      (cfg->top_p > 0.f && cfg->top_p < 1.f) ? cfg->top_p : 0.f, has_shared ? 1 : 0, topk_ids, topk_w,
+      shared_gate);
   if ((st = launched(hipGetLastError()))) return st;
   if (cfg->expert_budget > 0 || route_stats) {
     budget_kernel<<<1, 1024, 0, s>>>(topk_ids, topk_w, T, E, K, cfg->expert_budget,

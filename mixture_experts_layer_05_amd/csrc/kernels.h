@@ -51,8 +51,8 @@ __global__ void router_logits_bf16_kernel(const uint16_t*, const uint16_t*, cons
                                           int, int, float*, int, size_t);
 __global__ void router_logits_f32_kernel(const float*, const float*, const float*, int, int, int, int,
                                          float*, int);
-__global__ void topk_kernel(const float*, int, int, size_t, const float*, int, int, int, int, int, int32_t*,
-                            float*, float*);
+__global__ void topk_kernel(const float*, int, int, size_t, const float*, int, int, int, int, float, int,
+                            int32_t*, float*, float*);
 __global__ void budget_kernel(int32_t*, float*, int, int, int, int, int, int32_t*);
 
 // dispatch.hip

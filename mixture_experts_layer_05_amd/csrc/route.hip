@@ -102,10 +102,14 @@ __global__ void __launch_bounds__(256) router_logits_f32_kernel(
 // of a wave-wide argmax on (logit desc, id asc) pick the ids in descending
 // order.  Weights: exp(z_k - z_max) over the K picks, divided by their sum
 // (renormalised top-k) or by the sum over all E experts (plain softmax).
+// top_p in (0, 1): pick k survives iff the picks before it hold less than top_p
+// of the K picks' summed weight (so pick 0 always survives); the others become
+// id -1 / weight 0 and a renormalised top-k is taken over the survivors only.
+// The prefix sums run in pick order, the same for every lane.
 __global__ void __launch_bounds__(256) topk_kernel(
     const float* __restrict__ z, int ldz, int parts, size_t plane, const float* __restrict__ bias, int T,
-    int E, int K, int norm_topk, int has_shared, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
-    float* __restrict__ shared_gate) {
+    int E, int K, int norm_topk, float top_p, int has_shared, int32_t* __restrict__ topk_ids,
+    float* __restrict__ topk_w, float* __restrict__ shared_gate) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -166,10 +170,21 @@ __global__ void __launch_bounds__(256) topk_kernel(
   // The first pick is the maximum logit.
   const float zmax_k = __shfl(my_z, 0, kWave);
   float p = (lane < K) ? expf(my_z - zmax_k) : 0.f;
-  float denom = norm_topk ? wave_sum(p) : denom_all * expf(zmax - zmax_k);
+  bool kept = lane < K;
+  if (top_p > 0.f) {
+    float before = 0.f, all = 0.f;   // weight of the picks before this lane's, of all K
+    for (int k = 0; k < K; ++k) {
+      const float pk = __shfl(p, k, kWave);
+      if (k < lane) before += pk;
+      all += pk;
+    }
+    kept = kept && (lane == 0 || before < top_p * all);
+  }
+  const float pk = kept ? p : 0.f;
+  float denom = norm_topk ? wave_sum(pk) : denom_all * expf(zmax - zmax_k);
   if (lane < K) {
-    topk_ids[static_cast<size_t>(t) * K + lane] = my_id;
-    topk_w[static_cast<size_t>(t) * K + lane] = p / denom;
+    topk_ids[static_cast<size_t>(t) * K + lane] = kept ? my_id : -1;
+    topk_w[static_cast<size_t>(t) * K + lane] = pk / denom;
   }
   if (has_shared && lane == 0) shared_gate[t] = 1.0f / (1.0f + expf(-logit(E)));
 }

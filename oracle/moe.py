@@ -12,6 +12,9 @@ What it computes, step by step, each from the page that defines it:
    g[t] = x_t . w_g.
 2. Softmax over all experts, top-k, renormalise over the k kept
    [SpecForge PR #943, "Modifications": softmax, renormalised top-k preset].
+2b. Optional per-token top-p trim of the top-k, which runs before the budget
+   [colibri issue_budget.md, "Relationship to existing features": TOPP trims
+   within one position's top-K; TOPP then EXPERT_BUDGET compose in that order].
 3. Optional expert budget across the batch union [colibri issue_budget.md,
    "How it works"]: aggregate gate weight per distinct expert, keep the B
    heaviest, remove the others from every token's list, renormalise if
@@ -34,7 +37,15 @@ Readings where the pages are silent (all listed in the design notes):
     and marks dropped slots id -1 / weight 0; a token that loses every slot is
     not renormalised and gets no routed contribution;
   * SwiGLU is down(silu(gate x) * (up x)) with no biases; silu(a) = a / (1 + e^-a);
-  * the shared expert is not counted against the budget.
+  * the shared expert is not counted against the budget;
+  * top-p (0 < p < 1; 0 and 1 are off): the picks are taken by descending
+    probability and pick k survives iff the picks before it hold less than p of
+    the K picks' summed probability, so the survivors are the shortest prefix
+    reaching p of the top-k mass and pick 0 always survives; the survivors are
+    renormalised if norm_topk; the survive/drop decision is taken in float32,
+    as the kernel takes it (probabilities exp(z - z_max) of the float32 logits,
+    summed in pick order); dropped slots are id -1 / weight 0 at the row's end
+    and are not counted in the budget statistics.
 """
 from __future__ import annotations
 
@@ -107,6 +118,49 @@ def topk_softmax(z: np.ndarray, K: int, norm_topk: bool = True):
     w = np.take_along_axis(p, ids.astype(np.int64), axis=1)
     if norm_topk:
         w = w / w.sum(axis=1, keepdims=True)
+    return ids, w
+
+
+# ----------------------------------------------------------------------------- 2b. top-p trim
+
+
+def top_p_trim(z: np.ndarray, ids: np.ndarray, w: np.ndarray, top_p: float, norm_topk: bool = True):
+    """Trim each token's top-k picks to its top-p mass [colibri issue_budget.md,
+    "Relationship to existing features"].
+
+    Pick k (ids are by descending probability) survives iff the probability of
+    the picks before it is below top_p times that of all K picks.  The test runs
+    in float32 on exp(z - z_max) of the float32 logits, summed in pick order.
+    Survivors keep their float64 weight, renormalised over the survivors if
+    norm_topk; the other slots become id -1 / weight 0.  top_p outside (0, 1)
+    leaves the picks unchanged.
+    """
+    ids = np.array(ids, dtype=np.int32, copy=True)
+    w = np.array(w, dtype=np.float64, copy=True)
+    if not (0.0 < top_p < 1.0):
+        return ids, w
+    z32 = np.asarray(z, dtype=np.float64).astype(np.float32)
+    p_cut = np.float32(top_p)
+    T, K = ids.shape
+    for t in range(T):
+        zk = z32[t, ids[t].astype(np.int64)]
+        p = np.exp(zk - zk[0])                  # float32, pick 0 is the largest logit
+        total = np.float32(0.0)
+        for k in range(K):
+            total = np.float32(total + p[k])
+        before = np.float32(0.0)
+        n = 0
+        for k in range(K):
+            if k > 0 and not (before < p_cut * total):
+                break
+            n += 1
+            before = np.float32(before + p[k])
+        if n == K:
+            continue
+        kept = w[t, :n].copy()
+        ids[t, n:] = -1
+        w[t, n:] = 0.0
+        w[t, :n] = kept / kept.sum() if norm_topk else kept
     return ids, w
 
 
@@ -239,10 +293,12 @@ def moe_combine(x, ids, w, shared_gate: Optional[np.ndarray],
 # ----------------------------------------------------------------------------- whole layer
 
 
-def route(x, w_router, w_shared_gate, logit_bias, K: int, norm_topk: bool = True, budget: int = 0):
+def route(x, w_router, w_shared_gate, logit_bias, K: int, norm_topk: bool = True, budget: int = 0,
+          top_p: float = 0.0):
     """Steps 1-3: ids, weights, sigmoid(shared gate logit), budget stats, logits."""
     z = router_logits(x, w_router, logit_bias)
     ids, w = topk_softmax(z, K, norm_topk)
+    ids, w = top_p_trim(z, ids, w, top_p, norm_topk)
     ids, w, stats = expert_budget(ids, w, budget, norm_topk)
     sg = sigmoid(shared_gate_logit(x, w_shared_gate)) if w_shared_gate is not None else None
     return {"ids": ids, "w": w, "shared_gate": sg, "stats": stats, "logits": z}
@@ -250,9 +306,9 @@ def route(x, w_router, w_shared_gate, logit_bias, K: int, norm_topk: bool = True
 
 def moe_layer(x, w_router, w_shared_gate, logit_bias, K: int, E: int,
               expert: Callable[[int], Dict], shared: Optional[Dict], weight_dtype: str,
-              norm_topk: bool = True, budget: int = 0, tokens=None) -> Dict:
+              norm_topk: bool = True, budget: int = 0, tokens=None, top_p: float = 0.0) -> Dict:
     """The whole forward: route, dispatch, y (for `tokens`, default all)."""
-    r = route(x, w_router, w_shared_gate, logit_bias, K, norm_topk, budget)
+    r = route(x, w_router, w_shared_gate, logit_bias, K, norm_topk, budget, top_p)
     counts, offsets, perm = dispatch(r["ids"], E)
     y = moe_combine(x, r["ids"], r["w"], r["shared_gate"], expert, shared, weight_dtype, tokens)
     r.update(counts=counts, offsets=offsets, perm=perm, y=y)

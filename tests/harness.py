@@ -18,6 +18,10 @@ from oracle import moe as O
 # Top-k margin: the sorted logits of every token differ by more than this between
 # neighbours 1..K+1, so the float32 GPU logits pick the same ids in the same order.
 TOPK_MARGIN = 1e-3
+# Top-p margin: every prefix sum of a token's top-k probabilities differs from
+# top_p times their total by more than this fraction of the total, so the GPU
+# (float32 logits and sums) and the oracle trim at the same pick.
+TOPP_MARGIN = 1e-3
 # Budget margin: the B-th and (B+1)-th aggregate weights differ by more than this.
 BUDGET_MARGIN = 1e-4
 
@@ -48,12 +52,19 @@ class Case:
         return None if self.shared is None else {k: v.cpu() for k, v in self.shared.items()}
 
 
-def _topk_gaps_ok(z: np.ndarray, K: int) -> np.ndarray:
-    """Per token: the K+1 largest logits are separated by more than TOPK_MARGIN."""
+def _topk_gaps_ok(z: np.ndarray, K: int, top_p: float = 0.0) -> np.ndarray:
+    """Per token: the K+1 largest logits are separated by more than TOPK_MARGIN, and
+    (top-p on) no prefix of the top-k probabilities sits within TOPP_MARGIN of the cut."""
     E = z.shape[1]
     top = -np.sort(-z, axis=1)[:, :min(K + 1, E)]
     gaps = top[:, :-1] - top[:, 1:]
-    return (gaps > TOPK_MARGIN).all(axis=1) if gaps.shape[1] else np.ones(z.shape[0], bool)
+    ok = (gaps > TOPK_MARGIN).all(axis=1) if gaps.shape[1] else np.ones(z.shape[0], bool)
+    if 0.0 < top_p < 1.0:
+        p = np.exp(top[:, :K] - top[:, :1])
+        total = p.sum(axis=1, keepdims=True)
+        prefix = np.cumsum(p, axis=1)[:, :-1]
+        ok &= (np.abs(prefix - top_p * total) > TOPP_MARGIN * total).all(axis=1)
+    return ok
 
 
 def condition_topk(shape: W.LayerShape, inp: W.LayerInputs, max_attempts: int = 200) -> int:
@@ -61,7 +72,7 @@ def condition_topk(shape: W.LayerShape, inp: W.LayerInputs, max_attempts: int = 
     redrawn = 0
     for attempt in range(1, max_attempts + 1):
         z = O.router_logits(inp.x, inp.w_router, inp.logit_bias)
-        bad = np.nonzero(~_topk_gaps_ok(z, shape.num_experts_per_tok))[0]
+        bad = np.nonzero(~_topk_gaps_ok(z, shape.num_experts_per_tok, shape.top_p))[0]
         if len(bad) == 0:
             return redrawn
         for t in bad:
@@ -72,7 +83,7 @@ def condition_topk(shape: W.LayerShape, inp: W.LayerInputs, max_attempts: int = 
 
 def _budget_gap(shape: W.LayerShape, inp: W.LayerInputs) -> float:
     r = O.route(inp.x, inp.w_router, inp.w_shared_gate, inp.logit_bias, shape.num_experts_per_tok,
-                bool(shape.norm_topk_prob), 0)
+                bool(shape.norm_topk_prob), 0, shape.top_p)
     ids, w = r["ids"], r["w"]
     agg = sorted((float(w[ids == e].sum()) for e in set(ids.ravel().tolist())), reverse=True)
     B = shape.expert_budget
@@ -105,7 +116,8 @@ def config(shape: W.LayerShape):
     import mixture_experts_layer_05_amd as moe
     return moe.MoEConfig(shape.hidden_size, shape.n_routed_experts, shape.moe_intermediate_size,
                          shape.num_experts_per_tok, shape.shared_expert_intermediate_size,
-                         shape.weight_dtype, shape.act_dtype, shape.norm_topk_prob, shape.expert_budget)
+                         shape.weight_dtype, shape.act_dtype, shape.norm_topk_prob, shape.expert_budget,
+                         shape.top_p)
 
 
 def run_gpu(case: Case, layer=None) -> Dict[str, np.ndarray]:
@@ -136,7 +148,7 @@ def run_oracle(case: Case, tokens: Optional[Sequence[int]] = None) -> Dict[str, 
     return O.moe_layer(case.inp.x, case.inp.w_router, case.inp.w_shared_gate, case.inp.logit_bias,
                        shape.num_experts_per_tok, shape.n_routed_experts, case.expert_cpu,
                        case.shared_cpu(), shape.weight_dtype, bool(shape.norm_topk_prob),
-                       shape.expert_budget, tokens)
+                       shape.expert_budget, tokens, shape.top_p)
 
 
 def rel_l2(a: np.ndarray, b: np.ndarray) -> float:

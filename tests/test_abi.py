@@ -60,6 +60,12 @@ def _ws(cfg, T=4):
     (dict(norm_topk_prob=2), BAD_SHAPE),
     (dict(shared_expert_intermediate_size=-128), BAD_SHAPE),
     (dict(weight_dtype="f32", act_dtype="f32", hidden_size=100, moe_intermediate_size=30), OK),
+    (dict(top_p=0.0), OK),
+    (dict(top_p=0.7), OK),
+    (dict(top_p=1.0), OK),
+    (dict(top_p=-0.1), BAD_SHAPE),
+    (dict(top_p=1.5), BAD_SHAPE),
+    (dict(top_p=float("nan")), BAD_SHAPE),
 ])
 def test_workspace_size_validation(kw, status):
     assert _ws(_cfg(**kw))[0] == status

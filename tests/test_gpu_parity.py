@@ -58,6 +58,25 @@ def test_large_layer_8192_skewed_sampled():
     _run(W.LARGE, 8192, W.base_seed(3, 8192), 1.5, tokens=Hn.sample_tokens(8192, 16))
 
 
+# Top-p trim before the budget [colibri issue_budget.md, "Relationship to existing
+# features"]: the per-token trim alone, and composed with the budget.
+@pytest.mark.parametrize("shape,T,seed,top_p,tokens", [
+    (W.TINY.with_(name="tiny_topp", top_p=0.4), 64, W.base_seed(0, 64), 0.4, None),
+    (W.DRAFTER.with_(name="drafter_topp", top_p=0.8), 224, W.base_seed(1, 224), 0.8, 48),
+    (W.NARROW.with_(name="narrow_topp", top_p=0.5), 56, W.base_seed(2, 56), 0.5, None),
+    (W.LARGE_FP8.with_(name="large_fp8_topp_budget", top_p=0.7), 512, W.base_seed(4, 512), 0.7, 24),
+])
+def test_top_p_trim(shape, T, seed, top_p, tokens):
+    toks = None if tokens is None else Hn.sample_tokens(T, tokens)
+    alpha = 1.5 if shape.weight_dtype == W.DT_FP8 else None
+    case, gpu, ora, _ = _run(shape, T, seed, alpha, tokens=toks)
+    K = shape.num_experts_per_tok
+    kept = (gpu["ids"] >= 0).sum(axis=1)
+    assert kept.min() >= 1 and kept.max() <= K
+    if shape.expert_budget == 0:
+        assert (kept < K).any(), "the trim never dropped a slot on this case"
+
+
 def test_expert_parallel_rank_share_sampled():
     """One GPU's share of the large layer under 8-way expert parallelism: the global
     256-expert routing, restricted to the busiest rank's experts [32r, 32r + 32)

@@ -79,6 +79,96 @@ def test_topk_per_token_shift_invariance():
     assert np.allclose(a[1], b[1], atol=1e-15)
 
 
+# ----------------------------------------------------------------------------- top-p trim
+
+def test_top_p_worked_example():
+    # Probabilities 0.5 / 0.3 / 0.2 over three experts: cumulative 0.5, 0.8, 1.0.
+    z = np.log(np.array([[0.5, 0.3, 0.2]]))
+    ids, w = O.topk_softmax(z, 3)
+    for p, keep in ((0.45, 1), (0.7, 2), (0.79, 2), (0.81, 3), (0.99, 3)):
+        i2, w2 = O.top_p_trim(z, ids, w, p, norm_topk=True)
+        assert i2[0].tolist() == [0, 1, 2][:keep] + [-1] * (3 - keep), p
+        assert np.allclose(w2[0, :keep], np.array([0.5, 0.3, 0.2])[:keep] / [0.5, 0.8, 1.0][keep - 1], atol=1e-15)
+        assert (w2[0, keep:] == 0).all()
+    # Without renormalisation the kept slots keep their softmax probabilities.
+    ids0, w0 = O.topk_softmax(z, 3, norm_topk=False)
+    i2, w2 = O.top_p_trim(z, ids0, w0, 0.7, norm_topk=False)
+    assert i2[0].tolist() == [0, 1, -1]
+    assert np.allclose(w2[0], [0.5, 0.3, 0.0], atol=1e-15)
+
+
+def test_top_p_off_values_are_no_ops():
+    rng = np.random.default_rng(11)
+    z = rng.normal(size=(20, 9))
+    ids, w = O.topk_softmax(z, 4)
+    for p in (0.0, 1.0, -0.5, 1.5):
+        i2, w2 = O.top_p_trim(z, ids, w, p)
+        assert np.array_equal(i2, ids) and np.array_equal(w2, w)
+
+
+def test_top_p_matches_its_definition_on_random_tokens():
+    # Shortest prefix of the descending top-k probabilities whose sum reaches p of
+    # their total, computed here in float64 with scipy's softmax; tokens whose
+    # prefix sums sit within 1e-4 of the cut are skipped (the oracle decides in
+    # float32).
+    rng = np.random.default_rng(12)
+    checked = 0
+    for trial in range(30):
+        E, K = int(rng.integers(4, 20)), int(rng.integers(2, 5))
+        K = min(K, E)
+        z = rng.normal(scale=1.5, size=(40, E))
+        p = float(rng.uniform(0.2, 0.95))
+        ids, w = O.topk_softmax(z, K)
+        i2, w2 = O.top_p_trim(z, ids, w, p)
+        for t in range(z.shape[0]):
+            probs = scipy.special.softmax(z[t])[ids[t]]
+            cums = np.cumsum(probs) / probs.sum()
+            if np.min(np.abs(cums[:-1] - p)) < 1e-4:
+                continue
+            n = int(np.argmax(cums >= p)) + 1
+            assert i2[t].tolist() == ids[t, :n].tolist() + [-1] * (K - n)
+            assert np.allclose(w2[t, :n], probs[:n] / probs[:n].sum(), atol=1e-13)
+            checked += 1
+    assert checked > 1000
+
+
+def test_top_p_keeps_the_first_pick_and_a_prefix():
+    rng = np.random.default_rng(13)
+    z = rng.normal(scale=3.0, size=(200, 12))
+    ids, w = O.topk_softmax(z, 6)
+    i2, w2 = O.top_p_trim(z, ids, w, 1e-6)
+    assert (i2[:, 0] == ids[:, 0]).all() and (i2[:, 1:] == -1).all() and np.allclose(w2[:, 0], 1.0)
+    i3, w3 = O.top_p_trim(z, ids, w, 0.6)
+    n = (i3 >= 0).sum(axis=1)
+    for t in range(z.shape[0]):
+        assert i3[t, :n[t]].tolist() == ids[t, :n[t]].tolist() and (i3[t, n[t]:] == -1).all()
+    assert np.allclose(w3.sum(axis=1), 1.0, atol=1e-12)
+
+
+def test_top_p_per_token_shift_invariance():
+    rng = np.random.default_rng(14)
+    z = rng.integers(-20, 20, size=(30, 12)).astype(np.float64) / 4.0
+    shift = rng.integers(-8, 8, size=(30, 1)).astype(np.float64)  # exact in binary
+    a = O.top_p_trim(z, *O.topk_softmax(z, 4), 0.55)
+    b = O.top_p_trim(z + shift, *O.topk_softmax(z + shift, 4), 0.55)
+    assert np.array_equal(a[0], b[0]) and np.allclose(a[1], b[1], atol=1e-15)
+
+
+def test_top_p_runs_before_the_budget():
+    # Token 0 routes 0.55 / 0.45 to experts 0 / 1, tokens 1-2 route 0.9 / 0.1 to
+    # experts 2 / 1.  Budget 2 on the untrimmed routing keeps {1, 2} (aggregates
+    # 0.65 and 1.8 against 0.55 for expert 0); with top-p 0.8 first, tokens 1-2
+    # drop expert 1 and the budget keeps {0, 2} instead.
+    wr = np.log(np.array([[0.55, 1e-9, 1e-9], [0.45, 0.1, 0.1], [1e-9, 0.9, 0.9]]))
+    x = np.array([[1.0, 0, 0], [0, 1.0, 0], [0, 0, 1.0]])
+    r_plain = O.route(x, wr, None, None, 2, True, 2, 0.0)
+    r_topp = O.route(x, wr, None, None, 2, True, 2, 0.8)
+    assert set(r_plain["ids"].ravel().tolist()) - {-1} == {1, 2}
+    assert set(r_topp["ids"].ravel().tolist()) - {-1} == {0, 2}
+    assert r_topp["ids"].tolist() == [[0, -1], [2, -1], [2, -1]]
+    assert r_topp["stats"].tolist() == [3, 2, 1, 0]
+
+
 # ----------------------------------------------------------------------------- budget
 
 def _random_routing(rng, T, E, K):

@@ -48,6 +48,7 @@ class LayerShape:
     act_dtype: str                    # f32 / bf16
     norm_topk_prob: int = 1
     expert_budget: int = 0            # B, 0 = off
+    top_p: float = 0.0                # per-token top-p trim of the top-k, 0 = off
     weight_std: float = 0.02
     x_std: float = 1.0
     router_std: Optional[float] = None  # default 1/sqrt(H)

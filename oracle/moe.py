@@ -54,6 +54,7 @@ from typing import Callable, Dict, Optional, Sequence
 import numpy as np
 
 from . import e4m3
+from . import mx
 
 # ----------------------------------------------------------------------------- helpers
 
@@ -230,8 +231,15 @@ def dispatch(ids: np.ndarray, E: int):
 # ----------------------------------------------------------------------------- 5-7. experts
 
 
+def _np(a) -> np.ndarray:
+    return a.detach().cpu().numpy() if hasattr(a, "detach") else np.asarray(a)
+
+
 def _weights_f64(wdict: Dict, weight_dtype: str):
     """Expert weight dict -> float64 (gate [N,H], up [N,H], down [H,N])."""
+    if weight_dtype == "mxfp4":
+        return tuple(mx.dequant_mxfp4(_np(wdict[n]).view(np.uint8), _np(wdict[n + "_s"]).view(np.uint8))
+                     for n in ("gate", "up", "down"))
     if weight_dtype == "fp8_e4m3_g128":
         out = []
         for name in ("gate", "up", "down"):
@@ -247,20 +255,26 @@ def _fp8_activation(v: np.ndarray) -> np.ndarray:
     return e4m3.dequantise_group128(q, s)
 
 
+def _mx_activation(v: np.ndarray) -> np.ndarray:
+    return mx.dequant_mxfp8(*mx.quantise_mxfp8(v.astype(np.float32)))
+
+
 def swiglu_ffn(xrows: np.ndarray, wdict: Dict, weight_dtype: str) -> np.ndarray:
     """down(silu(gate x) * (up x)) for each row of xrows (float64).
 
     With fp8 weights the rows of x and of h are quantised per 128-group before
-    they enter the contraction, matching what an fp8 x fp8 contraction consumes.
+    they enter the contraction, matching what an fp8 x fp8 contraction consumes;
+    with MXFP4 weights they are quantised to MXFP8 (32-element blocks, E8M0
+    scales), what the block-scaled fp8 x fp4 contraction consumes.
     """
     wg, wu, wd = _weights_f64(wdict, weight_dtype)
-    fp8 = weight_dtype == "fp8_e4m3_g128"
-    xa = _fp8_activation(xrows) if fp8 else xrows
+    quant = {"fp8_e4m3_g128": _fp8_activation, "mxfp4": _mx_activation}.get(weight_dtype)
+    xa = quant(xrows) if quant else xrows
     a = xa @ wg.T
     b = xa @ wu.T
     h = silu(a) * b
-    if fp8:
-        h = _fp8_activation(h.astype(np.float32))
+    if quant:
+        h = quant(h.astype(np.float32))
     return h @ wd.T
 
 

@@ -30,7 +30,11 @@ import torch
 
 GROUP = 128  # quantisation group along the contraction dimension
 
-DT_F32, DT_BF16, DT_FP8 = "f32", "bf16", "fp8_e4m3_g128"
+DT_F32, DT_BF16, DT_FP8, DT_MXFP4 = "f32", "bf16", "fp8_e4m3_g128", "mxfp4"
+MX_BLOCK = 32
+# MXFP4 test weights: E8M0 scale codes drawn from [lo, hi] (2^-8 .. 2^-6); with
+# uniform E2M1 codes the element standard deviation is ~0.02, like the others.
+MX_SCALE_CODES = (119, 121)
 
 _TORCH_ACT = {DT_F32: torch.float32, DT_BF16: torch.bfloat16}
 
@@ -205,6 +209,8 @@ def expert_weights(shape: LayerShape, seed: int, e: int, device="cpu") -> Dict[s
     """
     H, I = shape.hidden_size, shape.moe_intermediate_size
     g = _gen(seed, _SUB_EXPERT, e, device=device)
+    if shape.weight_dtype == DT_MXFP4:
+        return _mx_random((I, H), (I, H), (H, I), g)
     wg = _normal((I, H), shape.weight_std, g)
     wu = _normal((I, H), shape.weight_std, g)
     wd = _normal((H, I), shape.weight_std, g)
@@ -217,6 +223,8 @@ def shared_expert_weights(shape: LayerShape, seed: int, device="cpu") -> Optiona
     if S == 0:
         return None
     g = _gen(seed, _SUB_SHARED, device=device)
+    if shape.weight_dtype == DT_MXFP4:
+        return _mx_random((S, H), (S, H), (H, S), g)
     wg = _normal((S, H), shape.weight_std, g)
     wu = _normal((S, H), shape.weight_std, g)
     wd = _normal((H, S), shape.weight_std, g)
@@ -234,6 +242,18 @@ def stacked_expert_weights(shape: LayerShape, seed: int, device="cpu") -> Dict[s
                    for k, v in w.items()}
         for k, v in w.items():
             out[k][e].copy_(v)
+    return out
+
+
+def _mx_random(gate_shape, up_shape, down_shape, g) -> Dict[str, torch.Tensor]:
+    """MXFP4 weights drawn directly as codes: uniform random bytes (two E2M1 codes
+    each, element 2i in the low nibble) and E8M0 scale codes from MX_SCALE_CODES,
+    one per 32 contraction elements.  No quantisation step is involved."""
+    out = {}
+    for name, (rows, k) in (("gate", gate_shape), ("up", up_shape), ("down", down_shape)):
+        out[name] = torch.randint(0, 256, (rows, k // 2), generator=g, dtype=torch.uint8, device=g.device)
+        out[name + "_s"] = torch.randint(MX_SCALE_CODES[0], MX_SCALE_CODES[1] + 1, (rows, k // MX_BLOCK),
+                                         generator=g, dtype=torch.uint8, device=g.device)
     return out
 
 

@@ -24,7 +24,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8_e4m3_g128": 5000.0, "f32": 157.3}
+# Dense MFMA peaks by weight dtype; MXFP4 weights meet MXFP8 activations, a mixed
+# fp8 x fp4 contraction, priced at the fp8 rate.
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8_e4m3_g128": 5000.0, "mxfp4": 5000.0, "f32": 157.3}
 
 METRIC = "MoE layer tokens/s + TFLOP/s (prefill M) and weight HBM GB/s (decode M), 1 GPU"
 
@@ -35,7 +37,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="drafter",
-                   choices=["drafter", "narrow", "large", "large_fp8", "tiny", "ep_rank"])
+                   choices=["drafter", "narrow", "large", "large_fp8", "tiny", "ep_rank",
+                            "drafter_mxfp4", "narrow_mxfp4", "large_mxfp4"])
     p.add_argument("--tokens", type=int, default=None, help="T (default: the workload's bench size)")
     p.add_argument("--alpha", type=float, default=None, help="Zipf router skew for the large layers")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -54,6 +57,9 @@ def workload(args):
         "large_fp8": (W.LARGE_FP8, 4, 8192, 1.5),
         "tiny": (W.TINY, 0, 64, None),
         "ep_rank": (W.EP_RANK, 5, 4096, 1.5),
+        "drafter_mxfp4": (W.DRAFTER_MX4, 1, 224, None),
+        "narrow_mxfp4": (W.NARROW_MX4, 2, 224, None),
+        "large_mxfp4": (W.LARGE_MX4, 3, 512, 0.0),
     }
     shape, idx, T, alpha = table[args.workload]
     if args.tokens is not None:
@@ -64,7 +70,8 @@ def workload(args):
 
 
 def weight_bytes_per_elem(shape) -> float:
-    return {"f32": 4.0, "bf16": 2.0, "fp8_e4m3_g128": 1.0 + 4.0 / 128}[shape.weight_dtype]
+    # MXFP4: half a byte per element plus one E8M0 byte per 32.
+    return {"f32": 4.0, "bf16": 2.0, "fp8_e4m3_g128": 1.0 + 4.0 / 128, "mxfp4": 0.5 + 1.0 / 32}[shape.weight_dtype]
 
 
 def accounting(shape, T, counts, router=True):
@@ -110,10 +117,11 @@ def gate_up_kernel(shape, T: int) -> str:
     if shape.weight_dtype == "f32":
         return "gate_up_f32_kernel"
     fp8 = shape.weight_dtype != "bf16"
+    dt = {"bf16": "bf16", "fp8_e4m3_g128": "fp8", "mxfp4": "mxfp4"}[shape.weight_dtype]
     H, E, I, K, S = (shape.hidden_size, shape.n_routed_experts, shape.moe_intermediate_size,
                      shape.num_experts_per_tok, shape.shared_expert_intermediate_size)
     rho = T * K // E
-    if rho >= 48:
+    if rho >= 48 and dt != "mxfp4":   # MXFP4 runs on the streaming kernel at every size
         tall = rho >= 160 and T * max(H, I, S) * 2 < (1 << 32)
         if tall:
             return "tiled8_expert_kernel<GateUp> (fp8, 256x128)" if fp8 else "tiled4_expert_kernel<GateUp> (bf16, 256x256)"
@@ -125,7 +133,7 @@ def gate_up_kernel(shape, T: int) -> str:
         cfg = "32, 64, 2" if narrow else "32, 128, 1"
     else:
         cfg = "64, 64, 2" if narrow else "64, 128, 1"
-    return f"stream_expert_kernel<GateUp, {cfg}, {'fp8' if fp8 else 'bf16'}>"
+    return f"stream_expert_kernel<GateUp, {cfg}, {dt}>"
 
 
 def kernel_source_file(kernel_label: str) -> str:

@@ -70,7 +70,19 @@ typedef enum moe_dtype {
    * issue_budget.md, header notes on issue_grouped_quant.md]; the fp8 x fp8
    * expert contraction follows the W8A8 MoE path that [DeepGEMM fork PR #5,
    * "Performance"] compares against. */
-  MOE_DTYPE_FP8_E4M3_G128 = 2
+  MOE_DTYPE_FP8_E4M3_G128 = 2,
+  /* OCP MX (microscaling v1.0) MXFP4 weights: E2M1 codes (sign, 2 exponent bits
+   * with bias 1, 1 mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte along
+   * the contraction dimension (element 2i in the low nibble), and one E8M0 scale
+   * byte (2^(e-127)) per 32 consecutive contraction elements: w = decode(q) * 2^(e-127).
+   * Activations (BF16 x) that meet these weights in a contraction are quantised
+   * inside the kernels to MXFP8, per token row and 32-element block: shared
+   * exponent s = floor(log2(amax)) - 8 clamped to [-127, 127] (s = 0 if amax =
+   * 0), element = RNE(clamp(v / 2^s, +-448)) as E4M3; the contraction applies both
+   * block scales in the matrix cores.  The 4-bit group-scaled weights are what
+   * the pages point to for the decode-bound layers (NVFP4 and FP8 x FP4 in
+   * [DeepGEMM fork PR #5] and [DeepGEMM PR #381]). */
+  MOE_DTYPE_MXFP4 = 3
 } moe_dtype;
 
 typedef struct moe_config {
@@ -95,12 +107,15 @@ typedef struct moe_config {
  *   s_gate, s_up   [E, I, H/128]  s_down [E, H, I/128]   (FP8 only, else NULL)
  *   ws_gate, ws_up [S, H]         ws_down [H, S]         (S > 0 only, else NULL)
  *   ss_gate, ss_up [S, H/128]     ss_down [H, S/128]     (FP8 and S > 0 only)
- * Element type is weight_dtype (one byte per element for FP8). */
+ * Element type is weight_dtype (one byte per element for FP8, half a byte for
+ * MXFP4: the last dimension of w_* holds K/2 bytes).  Scales: float32 for FP8;
+ * for MXFP4 uint8 E8M0 codes with K/32 per row in place of K/128
+ * (s_gate [E, I, H/32], s_down [E, H, I/32], ss_* likewise). */
 typedef struct moe_expert_weights {
   const void *w_gate, *w_up, *w_down;
-  const float *s_gate, *s_up, *s_down;
+  const void *s_gate, *s_up, *s_down;
   const void *ws_gate, *ws_up, *ws_down;
-  const float *ss_gate, *ss_up, *ss_down;
+  const void *ss_gate, *ss_up, *ss_down;
 } moe_expert_weights;
 
 /* Bytes of device workspace needed by moe_route / moe_dispatch / moe_forward for

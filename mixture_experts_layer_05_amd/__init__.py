@@ -24,7 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "moe_mi355x.h")
 
-DTYPES = {"f32": 0, "bf16": 1, "fp8_e4m3_g128": 2}
+DTYPES = {"f32": 0, "bf16": 1, "fp8_e4m3_g128": 2, "mxfp4": 3}
 ENTRY_POINTS = ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_forward",
                 "moe_forward_gate_up", "moe_forward_down", "moe_status_string", "moe_version")
 
@@ -172,24 +172,31 @@ def expert_weights_struct(cfg: MoEConfig, w: Dict[str, torch.Tensor],
     E, I, H, S = cfg.n_routed_experts, cfg.moe_intermediate_size, cfg.hidden_size, \
         cfg.shared_expert_intermediate_size
     fp8 = cfg.weight_dtype == "fp8_e4m3_g128"
-    wdt = torch.uint8 if fp8 else cfg.act_torch_dtype
-    _expect(w["gate"], (E, I, H), wdt, "w_gate")
-    _expect(w["up"], (E, I, H), wdt, "w_up")
-    _expect(w["down"], (E, H, I), wdt, "w_down")
+    mx = cfg.weight_dtype == "mxfp4"
+    quant = fp8 or mx
+    wdt = torch.uint8 if quant else cfg.act_torch_dtype
+    per = 2 if mx else 1                         # elements per stored byte along the contraction
+    sdt, sgroup = (torch.uint8, 32) if mx else (torch.float32, 128)
+    _expect(w["gate"], (E, I, H // per), wdt, "w_gate")
+    _expect(w["up"], (E, I, H // per), wdt, "w_up")
+    _expect(w["down"], (E, H, I // per), wdt, "w_down")
     s = _Weights(_ptr(w["gate"]), _ptr(w["up"]), _ptr(w["down"]))
-    if fp8:
-        _expect(w["gate_s"], (E, I, H // 128), torch.float32, "s_gate")
-        _expect(w["up_s"], (E, I, H // 128), torch.float32, "s_up")
-        _expect(w["down_s"], (E, H, I // 128), torch.float32, "s_down")
+    if quant:
+        _expect(w["gate_s"], (E, I, H // sgroup), sdt, "s_gate")
+        _expect(w["up_s"], (E, I, H // sgroup), sdt, "s_up")
+        _expect(w["down_s"], (E, H, I // sgroup), sdt, "s_down")
         s.s_gate, s.s_up, s.s_down = _ptr(w["gate_s"]), _ptr(w["up_s"]), _ptr(w["down_s"])
     if S > 0:
         if shared is None:
             raise ValueError("shared expert weights are required when shared_expert_intermediate_size > 0")
-        _expect(shared["gate"], (S, H), wdt, "ws_gate")
-        _expect(shared["up"], (S, H), wdt, "ws_up")
-        _expect(shared["down"], (H, S), wdt, "ws_down")
+        _expect(shared["gate"], (S, H // per), wdt, "ws_gate")
+        _expect(shared["up"], (S, H // per), wdt, "ws_up")
+        _expect(shared["down"], (H, S // per), wdt, "ws_down")
         s.ws_gate, s.ws_up, s.ws_down = _ptr(shared["gate"]), _ptr(shared["up"]), _ptr(shared["down"])
-        if fp8:
+        if quant:
+            _expect(shared["gate_s"], (S, H // sgroup), sdt, "ss_gate")
+            _expect(shared["up_s"], (S, H // sgroup), sdt, "ss_up")
+            _expect(shared["down_s"], (H, S // sgroup), sdt, "ss_down")
             s.ss_gate, s.ss_up, s.ss_down = _ptr(shared["gate_s"]), _ptr(shared["up_s"]), _ptr(shared["down_s"])
     return s
 

@@ -21,7 +21,10 @@ constexpr int kRouterParts = 8;
 // Upper bound (exclusive) on the byte size of x and of h; see check_forward.
 constexpr int64_t kMaxActivationBytes = 3LL << 30;
 
-bool valid_dtype(int d) { return d == MOE_DTYPE_F32 || d == MOE_DTYPE_BF16 || d == MOE_DTYPE_FP8_E4M3_G128; }
+bool valid_dtype(int d) {
+  return d == MOE_DTYPE_F32 || d == MOE_DTYPE_BF16 || d == MOE_DTYPE_FP8_E4M3_G128 || d == MOE_DTYPE_MXFP4;
+}
+bool quantised_weights(int d) { return d == MOE_DTYPE_FP8_E4M3_G128 || d == MOE_DTYPE_MXFP4; }
 
 // Shape and dtype checks shared by every entry point.
 int check_config(const moe_config* c) {
@@ -29,7 +32,8 @@ int check_config(const moe_config* c) {
   if (!valid_dtype(c->weight_dtype) || !valid_dtype(c->act_dtype)) return MOE_ERR_BAD_DTYPE;
   const bool combo = (c->weight_dtype == MOE_DTYPE_F32 && c->act_dtype == MOE_DTYPE_F32) ||
                      (c->weight_dtype == MOE_DTYPE_BF16 && c->act_dtype == MOE_DTYPE_BF16) ||
-                     (c->weight_dtype == MOE_DTYPE_FP8_E4M3_G128 && c->act_dtype == MOE_DTYPE_BF16);
+                     (c->weight_dtype == MOE_DTYPE_FP8_E4M3_G128 && c->act_dtype == MOE_DTYPE_BF16) ||
+                     (c->weight_dtype == MOE_DTYPE_MXFP4 && c->act_dtype == MOE_DTYPE_BF16);
   if (!combo) return MOE_ERR_BAD_DTYPE;
   if (c->hidden_size <= 0 || c->moe_intermediate_size <= 0 || c->n_routed_experts <= 0 ||
       c->num_experts_per_tok <= 0 || c->shared_expert_intermediate_size < 0 || c->expert_budget < 0 ||
@@ -91,6 +95,11 @@ Layout layout(const moe_config& c, int64_t T) {
     L.xs = take(static_cast<size_t>(T) * (c.hidden_size / kGroup) * sizeof(float));
     L.hq = take(elems);
     L.hs = take(elems / kGroup * sizeof(float));
+  } else if (c.weight_dtype == MOE_DTYPE_MXFP4) {
+    L.xq = take(static_cast<size_t>(T) * c.hidden_size);
+    L.xs = take(static_cast<size_t>(T) * (c.hidden_size / kMxBlock));
+    L.hq = take(elems);
+    L.hs = take(elems / kMxBlock);
   }
   L.total = std::max<size_t>(off, kAlign);
   return L;
@@ -133,7 +142,7 @@ int check_forward(const moe_config* cfg, int32_t T, const void* x, const float* 
   if (xbytes >= kMaxActivationBytes || hbytes >= kMaxActivationBytes) return MOE_ERR_UNSUPPORTED;
   if (!x || !topk_w || !counts || !offsets || !perm || !w || !y) return MOE_ERR_NULL_PTR;
   if (!w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_NULL_PTR;
-  const bool fp8 = cfg->weight_dtype == MOE_DTYPE_FP8_E4M3_G128;
+  const bool fp8 = quantised_weights(cfg->weight_dtype);   // scales required
   if (fp8 && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_NULL_PTR;
   if (cfg->shared_expert_intermediate_size > 0) {
     if (!shared_gate || !w->ws_gate || !w->ws_up || !w->ws_down) return MOE_ERR_NULL_PTR;
@@ -155,16 +164,31 @@ ExpertArgs expert_args(const moe_config& c, int32_t T, const void* x, const floa
   a.topk_w = topk_w;
   a.shared_gate = shared_gate;
   a.w_gate = w.w_gate; a.w_up = w.w_up; a.w_down = w.w_down;
-  a.s_gate = w.s_gate; a.s_up = w.s_up; a.s_down = w.s_down;
   a.ws_gate = w.ws_gate; a.ws_up = w.ws_up; a.ws_down = w.ws_down;
-  a.ss_gate = w.ss_gate; a.ss_up = w.ss_up; a.ss_down = w.ss_down;
   a.h = at<void>(ws, L.h);
   a.h_shared = L.h_shared;
   if (c.weight_dtype == MOE_DTYPE_FP8_E4M3_G128) {
+    a.s_gate = static_cast<const float*>(w.s_gate);
+    a.s_up = static_cast<const float*>(w.s_up);
+    a.s_down = static_cast<const float*>(w.s_down);
+    a.ss_gate = static_cast<const float*>(w.ss_gate);
+    a.ss_up = static_cast<const float*>(w.ss_up);
+    a.ss_down = static_cast<const float*>(w.ss_down);
     a.xq = at<uint8_t>(ws, L.xq);
     a.xs = at<float>(ws, L.xs);
     a.hq = at<uint8_t>(ws, L.hq);
     a.hs = at<float>(ws, L.hs);
+  } else if (c.weight_dtype == MOE_DTYPE_MXFP4) {
+    a.e8_gate = static_cast<const uint8_t*>(w.s_gate);
+    a.e8_up = static_cast<const uint8_t*>(w.s_up);
+    a.e8_down = static_cast<const uint8_t*>(w.s_down);
+    a.e8s_gate = static_cast<const uint8_t*>(w.ss_gate);
+    a.e8s_up = static_cast<const uint8_t*>(w.ss_up);
+    a.e8s_down = static_cast<const uint8_t*>(w.ss_down);
+    a.xq = at<uint8_t>(ws, L.xq);
+    a.xe8 = at<uint8_t>(ws, L.xs);
+    a.hq = at<uint8_t>(ws, L.hq);
+    a.he8 = at<uint8_t>(ws, L.hs);
   }
   a.o = at<float>(ws, L.o);
   a.y = y;
@@ -311,10 +335,14 @@ int moe_forward_gate_up(const moe_config* cfg, int32_t T, const void* x, const f
   const ExpertArgs a = expert_args(*cfg, T, x, topk_w, shared_gate, counts, offsets, perm, *w, y, ws, L);
   if (cfg->weight_dtype == MOE_DTYPE_FP8_E4M3_G128) {
     if ((st = launched(launch_quant_x(a, at<uint8_t>(ws, L.xq), at<float>(ws, L.xs), s)))) return st;
+  } else if (cfg->weight_dtype == MOE_DTYPE_MXFP4) {
+    if ((st = launched(launch_quant_x_mx(a, at<uint8_t>(ws, L.xq), at<uint8_t>(ws, L.xs), s)))) return st;
   }
   if ((st = launched(launch_gate_up(a, cfg->weight_dtype, s)))) return st;
   if (cfg->weight_dtype == MOE_DTYPE_FP8_E4M3_G128) {
     if ((st = launched(launch_quant_h(a, at<uint8_t>(ws, L.hq), at<float>(ws, L.hs), s)))) return st;
+  } else if (cfg->weight_dtype == MOE_DTYPE_MXFP4) {
+    if ((st = launched(launch_quant_h_mx(a, at<uint8_t>(ws, L.hq), at<uint8_t>(ws, L.hs), s)))) return st;
   }
   return MOE_OK;
 }

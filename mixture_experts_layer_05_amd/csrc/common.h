@@ -8,6 +8,7 @@ namespace moe {
 
 constexpr int kWave = 64;          // CDNA wavefront
 constexpr int kGroup = 128;        // fp8 scale group along the contraction dim
+constexpr int kMxBlock = 32;       // MX (microscaling) block along the contraction dim
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 16;
 
@@ -80,6 +81,17 @@ __device__ __forceinline__ f32x4 mfma_bf16_16x16x32(uint4 a, uint4 b, f32x4 c) {
 // the plain fp8 product; group scales are applied by the caller in float32.
 __device__ __forceinline__ f32x4 mfma_fp8_16x16x128(i32x8 a, i32x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// D(16x16,f32) += A(16x128, MXFP8 e4m3 codes) * B(128x16, MXFP4 e2m1 codes), both
+// scaled by E8M0 block scales in the matrix core.  Lane l supplies A row / B column
+// l%16.  A uses the 8-bit operand layout (lane group g = l/16 holds contraction
+// elements [16g, +16) in bytes 0..15 and [64+16g, +16) in bytes 16..31); B the
+// 4-bit layout (lane group g holds elements [32g, +32), element 2i in the low
+// nibble of byte i, upper four dwords unused).  sa / sb: the E8M0 code of
+// contraction block g (elements [32g, +32)) of the lane's row / column.
+__device__ __forceinline__ f32x4 mfma_mxfp8_mxfp4_16x16x128(i32x8 a, i32x8 b, f32x4 c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, sa, 0, sb);
 }
 
 // Output placement of the 16x16 MFMAs: lane l, element i -> row 4*(l/16)+i, column l%16.

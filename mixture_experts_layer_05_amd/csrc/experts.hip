@@ -182,6 +182,50 @@ __global__ void __launch_bounds__(256) quant_g128_kernel(const void* __restrict_
   }
 }
 
+// MXFP8 activations for the MXFP4 contraction [OCP MX v1.0 scale rule]: per row
+// and 32-element block, amax, shared exponent s = floor(log2(amax)) - 8 clamped to
+// >= -127 (0 for an all-zero block), scale byte s + 127, element = e4m3 RNE of
+// clamp(v * 2^-s, +-448).  2^-s is built from its exponent bits, so the product is
+// exact.  Eight lanes per block, four elements per lane.  Rows [0, rows_host) of
+// src, or [0, *rows_dev) if rows_dev.
+template <bool SRC_BF16>
+__global__ void __launch_bounds__(256) quant_mx8_kernel(const void* __restrict__ src, int rows_host,
+                                                        const int32_t* __restrict__ rows_dev, int cols,
+                                                        uint8_t* __restrict__ q, uint8_t* __restrict__ e8) {
+  const int rows = rows_dev ? *rows_dev : rows_host;
+  const size_t items = static_cast<size_t>(rows) * (cols / kMxBlock);
+  const int blk = threadIdx.x >> 3, bl = threadIdx.x & 7;
+  for (size_t it = static_cast<size_t>(blockIdx.x) * 32 + blk; it < items;
+       it += static_cast<size_t>(gridDim.x) * 32) {
+    const size_t base = it * kMxBlock + 4 * bl;   // rows are contiguous: (row, block) -> it*32
+    float v[4];
+    if constexpr (SRC_BF16) {
+      const uint2 p = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(src) + base);
+      v[0] = bf16_bits_to_f32(p.x & 0xffffu);
+      v[1] = bf16_bits_to_f32(p.x >> 16);
+      v[2] = bf16_bits_to_f32(p.y & 0xffffu);
+      v[3] = bf16_bits_to_f32(p.y >> 16);
+    } else {
+      const float4 p = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + base);
+      v[0] = p.x; v[1] = p.y; v[2] = p.z; v[3] = p.w;
+    }
+    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+#pragma unroll
+    for (int o = 4; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+    const int ebits = static_cast<int>((__float_as_uint(amax) >> 23) & 0xff);
+    int s = 0;
+    if (amax > 0.f) s = (ebits == 0) ? -127 : max(ebits - 127 - 8, -127);
+    const float mul = __uint_as_float(static_cast<uint32_t>(127 - s) << 23);   // 2^-s
+    float r[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = fminf(fmaxf(v[e] * mul, -448.0f), 448.0f);
+    int packed = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+    packed = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], packed, true);
+    *reinterpret_cast<int*>(q + base) = packed;
+    if (bl == 0) e8[it] = static_cast<uint8_t>(s + 127);
+  }
+}
+
 // ---------------------------------------------------------------- launch helpers
 
 constexpr int kMaxGrid = 2048;
@@ -211,10 +255,12 @@ hipError_t launch_gate_up(const ExpertArgs& a, int weight_dtype, hipStream_t str
     gate_up_f32_kernel<<<grid, 256, 0, stream>>>(a);
     return hipGetLastError();
   }
-  const bool fp8 = weight_dtype == kDtypeFp8;
   const int64_t rho = rows_per_expert(a);
+  // MXFP4 weights run on the streaming kernel at every size (no LDS-tiled form).
+  if (weight_dtype == kDtypeMxfp4) return launch_gate_up_stream(a, kDtypeMxfp4, rho, stream);
+  const bool fp8 = weight_dtype == kDtypeFp8;
   if (rho >= kTiledRows) return launch_gate_up_tiled(a, fp8, rho >= kTallRows, stream);
-  return launch_gate_up_stream(a, fp8, rho, stream);
+  return launch_gate_up_stream(a, weight_dtype, rho, stream);
 }
 
 hipError_t launch_down(const ExpertArgs& a, int weight_dtype, hipStream_t stream) {
@@ -223,10 +269,11 @@ hipError_t launch_down(const ExpertArgs& a, int weight_dtype, hipStream_t stream
     down_f32_kernel<<<grid, 256, 0, stream>>>(a);
     return hipGetLastError();
   }
-  const bool fp8 = weight_dtype == kDtypeFp8;
   const int64_t rho = rows_per_expert(a);
+  if (weight_dtype == kDtypeMxfp4) return launch_down_stream(a, kDtypeMxfp4, rho, stream);
+  const bool fp8 = weight_dtype == kDtypeFp8;
   if (rho >= kTiledRows && a.H % 256 == 0) return launch_down_tiled(a, fp8, rho >= kTallRows, stream);
-  return launch_down_stream(a, fp8, rho, stream);
+  return launch_down_stream(a, weight_dtype, rho, stream);
 }
 
 hipError_t launch_combine(const ExpertArgs& a, hipStream_t stream) {
@@ -240,6 +287,27 @@ hipError_t launch_quant_x(const ExpertArgs& a, uint8_t* xq, float* xs, hipStream
   const int64_t items = static_cast<int64_t>(a.T) * (a.H / kGroup);
   const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(ceil_div(items, 8), 4096)));
   quant_g128_kernel<true><<<grid, 256, 0, stream>>>(a.x, a.T, nullptr, a.H, xq, xs);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_x_mx(const ExpertArgs& a, uint8_t* xq, uint8_t* xe8, hipStream_t stream) {
+  const int64_t items = static_cast<int64_t>(a.T) * (a.H / kMxBlock);
+  const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(ceil_div(items, 32), 4096)));
+  quant_mx8_kernel<true><<<grid, 256, 0, stream>>>(a.x, a.T, nullptr, a.H, xq, xe8);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_h_mx(const ExpertArgs& a, uint8_t* hq, uint8_t* he8, hipStream_t stream) {
+  // Routed rows: as many as the dispatch kept (read on the device from offsets[E]).
+  const int64_t items = static_cast<int64_t>(a.T) * a.K * (a.I / kMxBlock);
+  int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(ceil_div(items, 32), 4096)));
+  quant_mx8_kernel<false><<<grid, 256, 0, stream>>>(a.h, 0, a.offsets + a.E, a.I, hq, he8);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || a.S == 0) return err;
+  const int64_t items_s = static_cast<int64_t>(a.T) * (a.S / kMxBlock);
+  grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(ceil_div(items_s, 32), 4096)));
+  quant_mx8_kernel<false><<<grid, 256, 0, stream>>>(static_cast<const float*>(a.h) + a.h_shared, a.T,
+                                                    nullptr, a.S, hq + a.h_shared, he8 + a.h_shared / kMxBlock);
   return hipGetLastError();
 }
 

@@ -33,6 +33,12 @@ struct ExpertArgs {
   const float* xs;               // fp8: scales [T, H/128]
   const uint8_t* hq;             // fp8: quantised h
   const float* hs;               // fp8: scales of h
+  // MXFP4 weights (w_* / ws_* hold the packed E2M1 codes): E8M0 scale bytes, one
+  // per 32 contraction elements; x and h quantised to MXFP8 codes in xq / hq with
+  // E8M0 scales in xe8 [T, H/32] / he8 (one per 32 elements of h).
+  const uint8_t *e8_gate, *e8_up, *e8_down, *e8s_gate, *e8s_up, *e8s_down;
+  const uint8_t* xe8;
+  const uint8_t* he8;
   float* o;                      // [T*K, H] unweighted routed outputs, row = slot t*K+k
   float* y;                      // [T, H]
   void* y_act;                   // [T, H] act dtype or null: the cast of y
@@ -67,11 +73,13 @@ hipError_t launch_gate_up(const ExpertArgs& a, int weight_dtype, hipStream_t str
 hipError_t launch_down(const ExpertArgs& a, int weight_dtype, hipStream_t stream);
 hipError_t launch_gate_up_tiled(const ExpertArgs& a, bool fp8, bool tall, hipStream_t stream);
 hipError_t launch_down_tiled(const ExpertArgs& a, bool fp8, bool tall, hipStream_t stream);
-hipError_t launch_gate_up_stream(const ExpertArgs& a, bool fp8, int64_t rho, hipStream_t stream);
-hipError_t launch_down_stream(const ExpertArgs& a, bool fp8, int64_t rho, hipStream_t stream);
+hipError_t launch_gate_up_stream(const ExpertArgs& a, int weight_dtype, int64_t rho, hipStream_t stream);
+hipError_t launch_down_stream(const ExpertArgs& a, int weight_dtype, int64_t rho, hipStream_t stream);
 hipError_t launch_combine(const ExpertArgs& a, hipStream_t stream);
 hipError_t launch_router_stream(const ExpertArgs& a, hipStream_t stream);
 hipError_t launch_quant_x(const ExpertArgs& a, uint8_t* xq, float* xs, hipStream_t stream);
 hipError_t launch_quant_h(const ExpertArgs& a, uint8_t* hq, float* hs, hipStream_t stream);
+hipError_t launch_quant_x_mx(const ExpertArgs& a, uint8_t* xq, uint8_t* xe8, hipStream_t stream);
+hipError_t launch_quant_h_mx(const ExpertArgs& a, uint8_t* hq, uint8_t* he8, hipStream_t stream);
 
 }  // namespace moe

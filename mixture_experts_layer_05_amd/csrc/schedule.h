@@ -11,7 +11,7 @@
 namespace moe {
 namespace {
 
-constexpr int kDtypeF32 = 0, kDtypeBf16 = 1, kDtypeFp8 = 2;
+constexpr int kDtypeF32 = 0, kDtypeBf16 = 1, kDtypeFp8 = 2, kDtypeMxfp4 = 3;
 
 // The schedule lives in LDS: prefix[0..G] of per-group tile counts, then each
 // group's row count and first dispatch row, so that finding a tile's group reads no

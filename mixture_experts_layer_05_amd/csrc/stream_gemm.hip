@@ -51,25 +51,35 @@ constexpr uint32_t kDeadRow = 0xC0000000u;
 // router logits z = x [W_r; w_g]^T over all T tokens (one group of T rows).
 enum class SMode { GateUp, Down, Router };
 
-template <SMode MODE, int BM, int BN, int WM, bool FP8>
+// FMT is the weight dtype: kDtypeBf16; kDtypeFp8 (e4m3 codes, float32 scale per
+// row and 128-group, activations quantised the same way); kDtypeMxfp4 (E2M1 codes
+// two per byte, E8M0 scale per 32 elements, activations MXFP8).
+template <SMode MODE, int BM, int BN, int WM, int FMT>
 struct StreamCfg {
+  static constexpr bool kQ = FMT != kDtypeBf16;                // 8-bit activation codes + scales
+  static constexpr bool kMX = FMT == kDtypeMxfp4;
   static constexpr int kWM = WM;                               // compute waves along rows
   static constexpr int kWN = kComputeWaves / WM;               // compute waves along weight rows
-  static constexpr int kRowData = FP8 ? 128 : 256;            // bytes per row per stage
-  static constexpr int kRowStride = kRowData + 8;             // padded LDS row (8 mod 16)
-  static constexpr int kLanesPerRow = kRowData / 16;
-  static constexpr int kRowsPerPass = kLoadThreads / kLanesPerRow;
-  static constexpr int kAPasses = (BM + kRowsPerPass - 1) / kRowsPerPass;
-  static constexpr int kBPasses = BN / kRowsPerPass;
+  static constexpr int kRowDataA = kQ ? 128 : 256;             // A bytes per row per stage
+  static constexpr int kRowDataB = kMX ? 64 : kRowDataA;       // B bytes per row per stage
+  static constexpr int kRowStrideA = kRowDataA + 8;            // padded LDS rows (8 mod 16)
+  static constexpr int kRowStrideB = kRowDataB + 8;
+  static constexpr int kLanesPerRowA = kRowDataA / 16;
+  static constexpr int kLanesPerRowB = kRowDataB / 16;
+  static constexpr int kRowsPerPassA = kLoadThreads / kLanesPerRowA;
+  static constexpr int kRowsPerPassB = kLoadThreads / kLanesPerRowB;
+  static constexpr int kAPasses = (BM + kRowsPerPassA - 1) / kRowsPerPassA;
+  static constexpr int kBPasses = BN / kRowsPerPassB;
   static constexpr int kRM = BM / WM / 16;                     // row blocks per compute wave
   static constexpr int kCB = BN / kWN / 16;                    // column blocks per compute wave
   static constexpr int kElems = 128;                           // contraction elements per stage
-  static constexpr int kSlot = (BM + BN) * kRowStride;         // one LDS stage buffer
-  static constexpr int kScales = BM + BN;
-  static_assert(BN % kRowsPerPass == 0, "BN must be a multiple of the rows per pass");
+  static constexpr int kBOff = BM * kRowStrideA;               // B rows inside a stage buffer
+  static constexpr int kSlot = kBOff + BN * kRowStrideB;       // one LDS stage buffer
+  static constexpr int kScales = BM + BN;                      // one 32-bit scale word per row
+  static_assert(BN % kRowsPerPassB == 0, "BN must be a multiple of the rows per pass");
   static_assert(MODE == SMode::Down || kCB % 2 == 0, "gate/up needs gate and up blocks");
   static_assert(kRM >= 1 && BM % (16 * WM) == 0, "rows per wave must be a multiple of 16");
-  static_assert(!FP8 || BM + BN <= kLoadThreads, "one scale per loader thread");
+  static_assert(!kQ || BM + BN <= kLoadThreads, "one scale per loader thread");
 };
 
 // Register stages a loader keeps in flight: as many as fit ~160 VGPRs (more make
@@ -168,11 +178,15 @@ __device__ Walk balanced_walk(const int* sched, int* gcost, long long* cpre, int
               static_cast<int>(gridDim.x / 8)};
 }
 
-template <SMode MODE, int BM, int BN, int WM, bool FP8, int NS>
+template <SMode MODE, int BM, int BN, int WM, int FMT, int NS>
 __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(ExpertArgs a) {
-  using C = StreamCfg<MODE, BM, BN, WM, FP8>;
+  using C = StreamCfg<MODE, BM, BN, WM, FMT>;
+  constexpr bool FP8 = C::kQ;    // quantised: 8-bit activation codes with scales
+  constexpr bool MX = C::kMX;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::kSlot];
-  __shared__ __attribute__((aligned(16))) float sscale[FP8 ? 2 * C::kScales : 4];
+  // Per stage and row: the fp8 float32 scale (as bits), or the MX row's four E8M0
+  // bytes for the stage's four 32-element blocks.
+  __shared__ __attribute__((aligned(16))) uint32_t sscale[FP8 ? 2 * C::kScales : 4];
   __shared__ int sched[kSchedInts];
   __shared__ int gcost[kSchedStride];
   __shared__ long long cpre[kSchedStride];
@@ -182,7 +196,9 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
   const int G = a.E + (has_shared ? 1 : 0);
   const int H = a.H;
   const int bn_cols = (MODE == SMode::GateUp) ? BN / 2 : BN;
-  const size_t esz = FP8 ? 1 : 2;
+  const size_t esz = FP8 ? 1 : 2;   // bytes per A (activation) element
+  // Bytes of one weight row of `k` elements.
+  auto b_row_bytes = [&](int k) -> size_t { return MX ? static_cast<size_t>(k) / 2 : static_cast<size_t>(k) * esz; };
   Walk walk;
   if constexpr (MODE == SMode::Router) {
     // Equal tiles: an equal run per XCD, strided by its workgroups.
@@ -237,8 +253,10 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (wave < kLoadWaves) {
     // ================================================================ loaders
-    const int lrow = tid / C::kLanesPerRow;            // row inside a load pass
-    const int lcol = (tid % C::kLanesPerRow) * 16;     // byte offset inside the stage slice
+    const int lrow = tid / C::kLanesPerRowA;           // A row inside a load pass
+    const int lcol = (tid % C::kLanesPerRowA) * 16;    // byte offset inside the A stage slice
+    const int lrowb = tid / C::kLanesPerRowB;          // the same for B
+    const int lcolb = (tid % C::kLanesPerRowB) * 16;
     const uint8_t* abase;
     size_t aelems;
     if constexpr (MODE != SMode::Down) {
@@ -266,24 +284,25 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
         const int base = t.shared ? 0 : t.rowbase;
 #pragma unroll
         for (int q = 0; q < C::kAPasses; ++q) {
-          const int mc = min(t.m0 + lrow + q * C::kRowsPerPass, t.rows - 1);
+          const int mc = min(t.m0 + lrow + q * C::kRowsPerPassA, t.rows - 1);
           p.pv[q] = a.perm[base + mc];
         }
         if constexpr (FP8) p.ps = a.perm[base + min(t.m0 + min(tid, BM - 1), t.rows - 1)];
       }
       return p;
     };
-    // A row offsets and this thread's fp8 scale row of a tile.
+    // A row offsets and this thread's scale row of a tile (bytes; the stage's
+    // scale word is 4 bytes at 4 * stage).
     struct Src {
       uint32_t a[C::kAPasses];
-      const float* s;
+      const uint8_t* s;
     };
     auto resolve = [&](const Tile& d, const Pend& p) {
       Src S;
       const TileInfo& t = d.t;
 #pragma unroll
       for (int q = 0; q < C::kAPasses; ++q) {
-        const int row = lrow + q * C::kRowsPerPass;
+        const int row = lrow + q * C::kRowsPerPassA;
         const int m = t.m0 + row;
         const int mc = min(m, t.rows - 1);
         uint32_t off;
@@ -297,32 +316,41 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
       }
       S.s = nullptr;
       if constexpr (FP8) {
-        // Thread tid < BM stages the scale of tile row tid, BM <= tid < BM+BN that of
-        // B row tid-BM; the other threads re-read B row 0's scales (never stored).
+        // Thread tid < BM stages the scale word of tile row tid, BM <= tid < BM+BN
+        // that of B row tid-BM; the other threads re-read B row 0's (never stored).
+        // fp8: ng float32 scales per row (one per 128); MX: K/32 E8M0 bytes per row.
         const int ng = d.kdim / kGroup;
-        const float* sw0;
-        const float* sw1 = nullptr;
+        const size_t srow = MX ? static_cast<size_t>(d.kdim / kMxBlock) : static_cast<size_t>(ng) * 4;
+        const uint8_t* sw0;
+        const uint8_t* sw1 = nullptr;
+        auto wscale = [&](const float* fs, const uint8_t* ms) {
+          return MX ? ms : reinterpret_cast<const uint8_t*>(fs);
+        };
         if constexpr (MODE == SMode::GateUp) {
-          sw0 = t.shared ? a.ss_gate : a.s_gate + static_cast<size_t>(t.group) * a.I * ng;
-          sw1 = t.shared ? a.ss_up : a.s_up + static_cast<size_t>(t.group) * a.I * ng;
+          sw0 = t.shared ? wscale(a.ss_gate, a.e8s_gate)
+                         : wscale(a.s_gate, a.e8_gate) + static_cast<size_t>(t.group) * a.I * srow;
+          sw1 = t.shared ? wscale(a.ss_up, a.e8s_up)
+                         : wscale(a.s_up, a.e8_up) + static_cast<size_t>(t.group) * a.I * srow;
         } else {
-          sw0 = t.shared ? a.ss_down : a.s_down + static_cast<size_t>(t.group) * H * ng;
+          sw0 = t.shared ? wscale(a.ss_down, a.e8s_down)
+                         : wscale(a.s_down, a.e8_down) + static_cast<size_t>(t.group) * H * srow;
         }
         if (tid < BM) {
           const int mc = min(t.m0 + tid, t.rows - 1);
           if constexpr (MODE == SMode::GateUp) {
             const int tok = t.shared ? mc : p.ps / a.K;
-            S.s = a.xs + static_cast<size_t>(tok) * ng;
+            S.s = (MX ? a.xe8 : reinterpret_cast<const uint8_t*>(a.xs)) + static_cast<size_t>(tok) * srow;
           } else {
-            S.s = a.hs + hrow(d, mc) / kGroup;
+            // Element offset of the row in h, in scale units (one per 32 or per 128).
+            S.s = MX ? a.he8 + hrow(d, mc) / kMxBlock : reinterpret_cast<const uint8_t*>(a.hs + hrow(d, mc) / kGroup);
           }
         } else {
           const int br = (tid < BM + BN) ? tid - BM : 0;
           if constexpr (MODE == SMode::GateUp)
-            S.s = (br < BN / 2) ? sw0 + static_cast<size_t>(d.n0 + br) * ng
-                                : sw1 + static_cast<size_t>(d.n0 + br - BN / 2) * ng;
+            S.s = (br < BN / 2) ? sw0 + static_cast<size_t>(d.n0 + br) * srow
+                                : sw1 + static_cast<size_t>(d.n0 + br - BN / 2) * srow;
           else
-            S.s = sw0 + static_cast<size_t>(d.n0 + br) * ng;
+            S.s = sw0 + static_cast<size_t>(d.n0 + br) * srow;
         }
       }
       return S;
@@ -336,33 +364,33 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
       const TileInfo& t = d.t;
       const uint8_t* w0;
       const uint8_t* w1 = nullptr;
+      const size_t rb = b_row_bytes(d.kdim);
       if constexpr (MODE == SMode::GateUp) {
         w0 = static_cast<const uint8_t*>(t.shared ? a.ws_gate : a.w_gate);
         w1 = static_cast<const uint8_t*>(t.shared ? a.ws_up : a.w_up);
         if (!t.shared) {
-          w0 += static_cast<size_t>(t.group) * a.I * H * esz;
-          w1 += static_cast<size_t>(t.group) * a.I * H * esz;
+          w0 += static_cast<size_t>(t.group) * a.I * rb;
+          w1 += static_cast<size_t>(t.group) * a.I * rb;
         }
       } else if constexpr (MODE == SMode::Router) {
         w0 = static_cast<const uint8_t*>(a.w_router);
       } else {
         w0 = static_cast<const uint8_t*>(t.shared ? a.ws_down : a.w_down);
-        if (!t.shared) w0 += static_cast<size_t>(t.group) * H * a.I * esz;
+        if (!t.shared) w0 += static_cast<size_t>(t.group) * H * rb;
       }
 #pragma unroll
       for (int q = 0; q < C::kBPasses; ++q) {
-        const int br = lrow + q * C::kRowsPerPass;
+        const int br = lrowb + q * C::kRowsPerPassB;
         if constexpr (MODE == SMode::GateUp) {
-          P.b[q] = (br < BN / 2) ? w0 + static_cast<size_t>(d.n0 + br) * d.kdim * esz
-                                 : w1 + static_cast<size_t>(d.n0 + br - BN / 2) * d.kdim * esz;
+          P.b[q] = (br < BN / 2) ? w0 + static_cast<size_t>(d.n0 + br) * rb
+                                 : w1 + static_cast<size_t>(d.n0 + br - BN / 2) * rb;
         } else if constexpr (MODE == SMode::Router) {
           // Column c < E: router row c; c == E: the shared gate vector; columns past
           // the last one re-read a valid row and are never stored.
           const int c = min(d.n0 + br, a.ncols - 1);
-          P.b[q] = (c < a.E) ? w0 + static_cast<size_t>(c) * d.kdim * esz
-                             : static_cast<const uint8_t*>(a.w_gcol);
+          P.b[q] = (c < a.E) ? w0 + static_cast<size_t>(c) * rb : static_cast<const uint8_t*>(a.w_gcol);
         } else {
-          P.b[q] = w0 + static_cast<size_t>(d.n0 + br) * d.kdim * esz;
+          P.b[q] = w0 + static_cast<size_t>(d.n0 + br) * rb;
         }
       }
       return P;
@@ -370,25 +398,26 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
 
     struct Regs {
       uint4 a[C::kAPasses], b[C::kBPasses];
-      float s;
+      uint32_t s;
     };
     auto gload = [&](Regs& R, const BPtr& P, const Src& S, int ks) {
-      const uint32_t off = static_cast<uint32_t>(ks) * C::kRowData + lcol;
+      const uint32_t off = static_cast<uint32_t>(ks) * C::kRowDataA + lcol;
+      const uint32_t offb = static_cast<uint32_t>(ks) * C::kRowDataB + lcolb;
 #pragma unroll
-      for (int q = 0; q < C::kBPasses; ++q) R.b[q] = ld16_stream(P.b[q] + off);
+      for (int q = 0; q < C::kBPasses; ++q) R.b[q] = ld16_stream(P.b[q] + offb);
 #pragma unroll
       for (int q = 0; q < C::kAPasses; ++q) R.a[q] = buf_ld16(arsrc, S.a[q] + off, 0);
-      if constexpr (FP8) R.s = S.s[ks];
+      if constexpr (FP8) R.s = *reinterpret_cast<const uint32_t*>(S.s + 4 * ks);
     };
     auto lstore = [&](const Regs& R, int slot) {
       uint8_t* base = smem + slot * C::kSlot;
 #pragma unroll
       for (int q = 0; q < C::kAPasses; ++q)
-        if (lrow + q * C::kRowsPerPass < BM)
-          lds_st16(base + (lrow + q * C::kRowsPerPass) * C::kRowStride + lcol, R.a[q]);
+        if (lrow + q * C::kRowsPerPassA < BM)
+          lds_st16(base + (lrow + q * C::kRowsPerPassA) * C::kRowStrideA + lcol, R.a[q]);
 #pragma unroll
       for (int q = 0; q < C::kBPasses; ++q)
-        lds_st16(base + (BM + lrow + q * C::kRowsPerPass) * C::kRowStride + lcol, R.b[q]);
+        lds_st16(base + C::kBOff + (lrowb + q * C::kRowsPerPassB) * C::kRowStrideB + lcolb, R.b[q]);
       if constexpr (FP8) {
         if (tid < C::kScales) sscale[slot * C::kScales + tid] = R.s;
       }
@@ -453,32 +482,60 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
     };
 
     auto compute = [&](int slot) {
-      const uint8_t* As = smem + slot * C::kSlot + (wrow0 + r) * C::kRowStride;
-      const uint8_t* Bs = smem + slot * C::kSlot + BM * C::kRowStride;
+      const uint8_t* As = smem + slot * C::kSlot + (wrow0 + r) * C::kRowStrideA;
+      const uint8_t* Bs = smem + slot * C::kSlot + C::kBOff;
       if constexpr (!FP8) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           uint4 af[C::kRM], bf[C::kCB];
 #pragma unroll
-          for (int i = 0; i < C::kRM; ++i) af[i] = lds_ld16(As + 16 * i * C::kRowStride + 64 * s + 16 * g);
+          for (int i = 0; i < C::kRM; ++i) af[i] = lds_ld16(As + 16 * i * C::kRowStrideA + 64 * s + 16 * g);
 #pragma unroll
           for (int j = 0; j < C::kCB; ++j)
-            bf[j] = lds_ld16(Bs + stream_b_row<MODE, BN, C::kWN, C::kCB>(wn, j, r) * C::kRowStride + 64 * s +
+            bf[j] = lds_ld16(Bs + stream_b_row<MODE, BN, C::kWN, C::kCB>(wn, j, r) * C::kRowStrideB + 64 * s +
                              16 * g);
 #pragma unroll
           for (int i = 0; i < C::kRM; ++i)
 #pragma unroll
             for (int j = 0; j < C::kCB; ++j) acc[i][j] = mfma_bf16_16x16x32(af[i], bf[j], acc[i][j]);
         }
+      } else if constexpr (MX) {
+        // 16x16x128 with A = MXFP8 codes (8-bit layout: lane group g holds bytes
+        // [16g, +16) and [64+16g, +16) of the row's 128 codes) and B = MXFP4 codes
+        // (4-bit layout: lane group g holds the 32 codes [32g, +32), bytes [16g, +16)
+        // of the row's 64).  The E8M0 scale of K-block g (elements [32g, +32)) of the
+        // lane's row comes from lane group g, byte g of the row's scale word.
+        const uint32_t* sc = sscale + slot * C::kScales;
+        i32x8 af[C::kRM], bf[C::kCB];
+        int sa[C::kRM], sb[C::kCB];
+#pragma unroll
+        for (int i = 0; i < C::kRM; ++i) {
+          const uint8_t* p = As + 16 * i * C::kRowStrideA;
+          const uint4 lo = lds_ld16(p + 16 * g);
+          const uint4 hi = lds_ld16(p + 64 + 16 * g);
+          af[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          sa[i] = static_cast<int>((sc[wrow0 + 16 * i + r] >> (8 * g)) & 0xffu);
+        }
+#pragma unroll
+        for (int j = 0; j < C::kCB; ++j) {
+          const int br = stream_b_row<MODE, BN, C::kWN, C::kCB>(wn, j, r);
+          const uint4 v = lds_ld16(Bs + br * C::kRowStrideB + 16 * g);
+          bf[j] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+          sb[j] = static_cast<int>((sc[BM + br] >> (8 * g)) & 0xffu);
+        }
+#pragma unroll
+        for (int i = 0; i < C::kRM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::kCB; ++j) acc[i][j] = mfma_mxfp8_mxfp4_16x16x128(af[i], bf[j], acc[i][j], sa[i], sb[j]);
       } else {
         // Lane group g holds bytes [16g, +16) and [64+16g, +16) of its row's 128-byte group.
-        const float* sc = sscale + slot * C::kScales;
+        const float* sc = reinterpret_cast<const float*>(sscale + slot * C::kScales);
         i32x8 af[C::kRM], bf[C::kCB];
         f32x4 sa[C::kRM];
         float sb[C::kCB];
 #pragma unroll
         for (int i = 0; i < C::kRM; ++i) {
-          const uint8_t* p = As + 16 * i * C::kRowStride;
+          const uint8_t* p = As + 16 * i * C::kRowStrideA;
           const uint4 lo = lds_ld16(p + 16 * g);
           const uint4 hi = lds_ld16(p + 64 + 16 * g);
           af[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
@@ -487,7 +544,7 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
 #pragma unroll
         for (int j = 0; j < C::kCB; ++j) {
           const int br = stream_b_row<MODE, BN, C::kWN, C::kCB>(wn, j, r);
-          const uint8_t* p = Bs + br * C::kRowStride;
+          const uint8_t* p = Bs + br * C::kRowStrideB;
           const uint4 lo = lds_ld16(p + 16 * g);
           const uint4 hi = lds_ld16(p + 64 + 16 * g);
           bf[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
@@ -612,15 +669,15 @@ int stream_grid(int64_t tiles) {
   return static_cast<int>(std::max<int64_t>(kXcdCount, ceil_div(b, kXcdCount) * kXcdCount));
 }
 
-template <SMode MODE, int BM, int BN, int WM, bool FP8>
+template <SMode MODE, int BM, int BN, int WM, int FMT>
 hipError_t launch_stream(const ExpertArgs& a, hipStream_t stream) {
-  using C = StreamCfg<MODE, BM, BN, WM, FP8>;
+  using C = StreamCfg<MODE, BM, BN, WM, FMT>;
   constexpr int NS = stream_stages(C::kAPasses + C::kBPasses);
   const int bn_cols = (MODE == SMode::GateUp) ? BN / 2 : BN;
   const int nt_r = (MODE == SMode::GateUp) ? a.I / bn_cols : a.H / bn_cols;
   const int nt_s = (MODE == SMode::GateUp) ? a.S / bn_cols : a.H / bn_cols;
   const int grid = stream_grid(stream_tiles(a, BM, nt_r, nt_s));
-  stream_expert_kernel<MODE, BM, BN, WM, FP8, NS><<<grid, kStreamThreads, 0, stream>>>(a);
+  stream_expert_kernel<MODE, BM, BN, WM, FMT, NS><<<grid, kStreamThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -630,38 +687,40 @@ hipError_t launch_stream(const ExpertArgs& a, hipStream_t stream) {
 // tiles per CU: its tiles all have H/128 stages, so the count per workgroup sets
 // the balance.  Down tiles keep 128 weight rows: they are short (I/128 stages),
 // there are H/128 of them per row block, and wider tiles re-read fewer h rows.
-template <SMode MODE, bool FP8>
+template <SMode MODE, int FMT>
 hipError_t launch_stream_rho(const ExpertArgs& a, int64_t rho, hipStream_t stream) {
   const int64_t slots = static_cast<int64_t>(a.T) * a.K;
   const int64_t touched = std::min<int64_t>(a.E, slots);
   const int64_t n_out = (MODE == SMode::GateUp) ? a.I : a.H;
   const int64_t tiles128 = touched * (MODE == SMode::GateUp ? n_out / 64 : n_out / 128);
   const bool narrow = MODE == SMode::GateUp && tiles128 < 3 * 256;
-  if (rho <= 12) return launch_stream<MODE, 16, 128, 1, FP8>(a, stream);
-  if (rho <= 24) return narrow ? launch_stream<MODE, 32, 64, 2, FP8>(a, stream)
-                               : launch_stream<MODE, 32, 128, 1, FP8>(a, stream);
-  return narrow ? launch_stream<MODE, 64, 64, 2, FP8>(a, stream)
-                : launch_stream<MODE, 64, 128, 1, FP8>(a, stream);
+  if (rho <= 12) return launch_stream<MODE, 16, 128, 1, FMT>(a, stream);
+  if (rho <= 24) return narrow ? launch_stream<MODE, 32, 64, 2, FMT>(a, stream)
+                               : launch_stream<MODE, 32, 128, 1, FMT>(a, stream);
+  return narrow ? launch_stream<MODE, 64, 64, 2, FMT>(a, stream)
+                : launch_stream<MODE, 64, 128, 1, FMT>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_router_stream(const ExpertArgs& a, hipStream_t stream) {
   const int grid = stream_grid(ceil_div(a.T, 64) * ceil_div(a.ncols, 128));
-  using C = StreamCfg<SMode::Router, 64, 128, 1, false>;
+  using C = StreamCfg<SMode::Router, 64, 128, 1, kDtypeBf16>;
   constexpr int NS = stream_stages(C::kAPasses + C::kBPasses);
-  stream_expert_kernel<SMode::Router, 64, 128, 1, false, NS><<<grid, kStreamThreads, 0, stream>>>(a);
+  stream_expert_kernel<SMode::Router, 64, 128, 1, kDtypeBf16, NS><<<grid, kStreamThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
-hipError_t launch_gate_up_stream(const ExpertArgs& a, bool fp8, int64_t rho, hipStream_t stream) {
-  return fp8 ? launch_stream_rho<SMode::GateUp, true>(a, rho, stream)
-             : launch_stream_rho<SMode::GateUp, false>(a, rho, stream);
+hipError_t launch_gate_up_stream(const ExpertArgs& a, int weight_dtype, int64_t rho, hipStream_t stream) {
+  if (weight_dtype == kDtypeMxfp4) return launch_stream_rho<SMode::GateUp, kDtypeMxfp4>(a, rho, stream);
+  if (weight_dtype == kDtypeFp8) return launch_stream_rho<SMode::GateUp, kDtypeFp8>(a, rho, stream);
+  return launch_stream_rho<SMode::GateUp, kDtypeBf16>(a, rho, stream);
 }
 
-hipError_t launch_down_stream(const ExpertArgs& a, bool fp8, int64_t rho, hipStream_t stream) {
-  return fp8 ? launch_stream_rho<SMode::Down, true>(a, rho, stream)
-             : launch_stream_rho<SMode::Down, false>(a, rho, stream);
+hipError_t launch_down_stream(const ExpertArgs& a, int weight_dtype, int64_t rho, hipStream_t stream) {
+  if (weight_dtype == kDtypeMxfp4) return launch_stream_rho<SMode::Down, kDtypeMxfp4>(a, rho, stream);
+  if (weight_dtype == kDtypeFp8) return launch_stream_rho<SMode::Down, kDtypeFp8>(a, rho, stream);
+  return launch_stream_rho<SMode::Down, kDtypeBf16>(a, rho, stream);
 }
 
 }  // namespace moe

@@ -25,7 +25,7 @@ TOPP_MARGIN = 1e-3
 # Budget margin: the B-th and (B+1)-th aggregate weights differ by more than this.
 BUDGET_MARGIN = 1e-4
 
-TOL = {"f32": 1e-5, "bf16": 2e-3, "fp8_e4m3_g128": 1e-2}   # relative L2 of y
+TOL = {"f32": 1e-5, "bf16": 2e-3, "fp8_e4m3_g128": 1e-2, "mxfp4": 1e-2}   # relative L2 of y
 # Routing weights, absolute.  The pages fix no tolerance here; the bound comes from
 # the arithmetic: the logits are float32 sums of H <= 7168 bf16 products with
 # |z| = O(1), whose rounding (random-walk ~ sqrt(H) * 2^-24 * |partial sums|) is a

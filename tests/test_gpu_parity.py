@@ -58,6 +58,19 @@ def test_large_layer_8192_skewed_sampled():
     _run(W.LARGE, 8192, W.base_seed(3, 8192), 1.5, tokens=Hn.sample_tokens(8192, 16))
 
 
+# MXFP4 expert weights x MXFP8 activations (block-scaled fp8 x fp4 contraction).
+@pytest.mark.parametrize("shape,T,idx,alpha,tokens", [
+    (W.DRAFTER_MX4, 7, 1, None, None),
+    (W.DRAFTER_MX4, 56, 1, None, None),
+    (W.DRAFTER_MX4, 224, 1, None, 48),
+    (W.NARROW_MX4, 56, 2, None, None),
+    (W.LARGE_MX4, 512, 3, 1.5, 24),
+    (W.LARGE_MX4.with_(name="large_mxfp4_budget64", expert_budget=64), 512, 4, 1.5, 24),
+])
+def test_mxfp4_layer(shape, T, idx, alpha, tokens):
+    _run(shape, T, W.base_seed(idx, T), alpha, tokens=None if tokens is None else Hn.sample_tokens(T, tokens))
+
+
 # Top-p trim before the budget [colibri issue_budget.md, "Relationship to existing
 # features"]: the per-token trim alone, and composed with the budget.
 @pytest.mark.parametrize("shape,T,seed,top_p,tokens", [

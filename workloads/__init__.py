@@ -72,6 +72,11 @@ DRAFTER = LayerShape("drafter_16x1024_top2_shared2048", 5120, 16, 1024, 2, 2048,
 NARROW = LayerShape("narrow_512x512_top10_shared2048", 5120, 512, 512, 10, 2048, DT_BF16, DT_BF16)
 LARGE = LayerShape("large_256x2048_top8_h7168", 7168, 256, 2048, 8, 0, DT_BF16, DT_BF16)
 LARGE_FP8 = LARGE.with_(name="large_fp8_budget64", weight_dtype=DT_FP8, expert_budget=64)
+# 4-bit (MXFP4) expert weights on the decode-bound layers [the 4-bit group-scaled
+# weights the pages point to for decode]: same shapes, synthetic MXFP4 codes.
+DRAFTER_MX4 = DRAFTER.with_(name="drafter_mxfp4", weight_dtype=DT_MXFP4)
+NARROW_MX4 = NARROW.with_(name="narrow_mxfp4", weight_dtype=DT_MXFP4)
+LARGE_MX4 = LARGE.with_(name="large_mxfp4", weight_dtype=DT_MXFP4)
 
 # One GPU's share of the large layer sharded over 8 GPUs by experts: rank r
 # holds experts [32r, 32r + 32) of the 256 (H 7168, I 2048) and receives, for a

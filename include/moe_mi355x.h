@@ -32,10 +32,10 @@
  *     reading any pointer but cfg and enqueue nothing; moe_dispatch writes zero
  *     counts and offsets (topk_ids and perm may be NULL).
  *   - Supported dtype combinations (weight_dtype / act_dtype):
- *       F32 / F32, BF16 / BF16, FP8_E4M3_G128 / BF16.
+ *       F32 / F32, BF16 / BF16, FP8_E4M3_G128 / BF16, MXFP4 / BF16.
  *     With BF16 or FP8 weights, hidden_size, moe_intermediate_size and
- *     shared_expert_intermediate_size must be multiples of 128
- *     (MOE_ERR_UNSUPPORTED otherwise).  1 <= n_routed_experts <= 512,
+ *     shared_expert_intermediate_size must be multiples of 128, with MXFP4
+ *     weights multiples of 256 (MOE_ERR_UNSUPPORTED otherwise).  1 <= n_routed_experts <= 512,
  *     1 <= num_experts_per_tok <= min(n_routed_experts, 16).
  */
 #ifndef MOE_MI355X_H

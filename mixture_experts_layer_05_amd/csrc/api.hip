@@ -43,8 +43,9 @@ int check_config(const moe_config* c) {
   if (!(c->top_p >= 0.f && c->top_p <= 1.f)) return MOE_ERR_BAD_SHAPE;   // also rejects NaN
   if (c->n_routed_experts > kMaxExperts || c->num_experts_per_tok > kMaxTopK) return MOE_ERR_UNSUPPORTED;
   if (c->weight_dtype != MOE_DTYPE_F32) {
-    if (c->hidden_size % 128 || c->moe_intermediate_size % 128 ||
-        c->shared_expert_intermediate_size % 128)
+    // The expert kernels contract in whole stages: 128 elements, 256 with MXFP4.
+    const int q = c->weight_dtype == MOE_DTYPE_MXFP4 ? 256 : 128;
+    if (c->hidden_size % q || c->moe_intermediate_size % q || c->shared_expert_intermediate_size % q)
       return MOE_ERR_UNSUPPORTED;
   }
   // Index arithmetic is 32-bit inside the kernels for rows and slots.

@@ -67,6 +67,31 @@ struct TileInfo {
 // slabs x a few row blocks, so both operands are reused from that XCD's L2 instead
 // of one operand being re-fetched for every tile.  band >= m-tiles gives plain
 // m-fastest order.
+__device__ __forceinline__ TileInfo tile_in_group(const int* sched, int g, int tile, const ExpertArgs& a,
+                                                  int BM, int band = 1 << 30) {
+  const int* prefix = sched;
+  TileInfo t;
+  t.group = g;
+  t.shared = g == a.E;
+  t.rows = sched[kSchedStride + g];
+  t.rowbase = sched[2 * kSchedStride + g];
+  const int mt = static_cast<int>(ceil_div(t.rows, BM));
+  const int local = tile - prefix[g];
+  if (band >= mt) {
+    t.nt = local / mt;
+    t.m0 = (local % mt) * BM;
+    return t;
+  }
+  const int ntile = (prefix[g + 1] - prefix[g]) / mt;
+  const int per_band = band * ntile;
+  const int first_m = (local / per_band) * band;
+  const int bm = min(mt - first_m, band);
+  const int in_band = local - (first_m / band) * per_band;
+  t.nt = in_band / bm;
+  t.m0 = (first_m + in_band % bm) * BM;
+  return t;
+}
+
 __device__ __forceinline__ TileInfo find_tile(const int* sched, int G, int tile, const ExpertArgs& a,
                                               int BM, int band = 1 << 30) {
   const int* prefix = sched;
@@ -75,26 +100,23 @@ __device__ __forceinline__ TileInfo find_tile(const int* sched, int G, int tile,
     const int mid = (lo + hi) >> 1;
     if (prefix[mid] <= tile) lo = mid; else hi = mid;
   }
-  TileInfo t;
-  t.group = lo;
-  t.shared = lo == a.E;
-  t.rows = sched[kSchedStride + lo];
-  t.rowbase = sched[2 * kSchedStride + lo];
-  const int mt = static_cast<int>(ceil_div(t.rows, BM));
-  const int local = tile - prefix[lo];
-  if (band >= mt) {
-    t.nt = local / mt;
-    t.m0 = (local % mt) * BM;
-    return t;
+  return tile_in_group(sched, lo, tile, a, BM, band);
+}
+
+// Group of `tile` (the last g < G with prefix[g] <= tile), found by scanning forward
+// from group g, which must satisfy prefix[g] <= tile: a persistent walk only moves
+// forward.  Each lane of the (whole, converged) wave tests one later group, so one
+// LDS read covers 64 groups; prefix is non-decreasing, so the passed groups are the
+// first lanes of the ballot.
+__device__ __forceinline__ int advance_group(const int* prefix, int G, int tile, int g) {
+  const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+  for (;;) {
+    const int c = g + 1 + lane;
+    const bool passed = c < G && prefix[c] <= tile;
+    const int n = __popcll(__ballot(passed));
+    g += n;
+    if (n < kWave) return g;
   }
-  const int ntile = (prefix[lo + 1] - prefix[lo]) / mt;
-  const int per_band = band * ntile;
-  const int first_m = (local / per_band) * band;
-  const int bm = min(mt - first_m, band);
-  const int in_band = local - (first_m / band) * per_band;
-  t.nt = in_band / bm;
-  t.m0 = (first_m + in_band % bm) * BM;
-  return t;
 }
 
 // Persistent walk over [0, total): the tiles are cut into 8 contiguous ranges, one

@@ -6,9 +6,11 @@
 // The kernel is built around keeping enough of that stream in flight:
 //
 //   * a tile is BN weight rows of one group (routed expert or shared expert)
-//     against BM rows of tokens; the contraction runs in stages of 256 bytes per
-//     row (128 bf16, or one fp8 128-group of 128 bytes).  Global loads give each
-//     row 256 (bf16) or 128 (fp8) contiguous bytes per wave instruction;
+//     against BM rows of tokens; the contraction runs in stages of 128 elements
+//     (bf16: 256 bytes per row; fp8: one 128-group, 128 bytes) or 256 elements
+//     (MXFP4 weights: 128 bytes per weight row, 256 bytes per MXFP8 activation
+//     row).  Global loads give each row 128-256 contiguous bytes per wave
+//     instruction (64-byte row pieces load at well under half the rate);
 //   * a workgroup is 8 waves with two roles.  Four loader waves only load: they
 //     keep NS stages in flight in registers and write one stage per step into a
 //     double-buffered LDS stage.  Four compute waves read the other LDS buffer,
@@ -60,8 +62,11 @@ struct StreamCfg {
   static constexpr bool kMX = FMT == kDtypeMxfp4;
   static constexpr int kWM = WM;                               // compute waves along rows
   static constexpr int kWN = kComputeWaves / WM;               // compute waves along weight rows
-  static constexpr int kRowDataA = kQ ? 128 : 256;             // A bytes per row per stage
-  static constexpr int kRowDataB = kMX ? 64 : kRowDataA;       // B bytes per row per stage
+  // Contraction elements per stage: 128 (one bf16 row slice of 256 bytes, or one fp8
+  // 128-group), 256 for MX so that a weight row still gives 128 contiguous bytes.
+  static constexpr int kElems = kMX ? 256 : 128;
+  static constexpr int kRowDataA = kQ && !kMX ? 128 : 256;     // A bytes per row per stage
+  static constexpr int kRowDataB = kMX ? 128 : kRowDataA;      // B bytes per row per stage
   static constexpr int kRowStrideA = kRowDataA + 8;            // padded LDS rows (8 mod 16)
   static constexpr int kRowStrideB = kRowDataB + 8;
   static constexpr int kLanesPerRowA = kRowDataA / 16;
@@ -72,10 +77,12 @@ struct StreamCfg {
   static constexpr int kBPasses = BN / kRowsPerPassB;
   static constexpr int kRM = BM / WM / 16;                     // row blocks per compute wave
   static constexpr int kCB = BN / kWN / 16;                    // column blocks per compute wave
-  static constexpr int kElems = 128;                           // contraction elements per stage
   static constexpr int kBOff = BM * kRowStrideA;               // B rows inside a stage buffer
   static constexpr int kSlot = kBOff + BN * kRowStrideB;       // one LDS stage buffer
-  static constexpr int kScales = BM + BN;                      // one 32-bit scale word per row
+  static constexpr int kScales = BM + BN;                      // one scale word per row (below)
+  // Scale word of a row per stage: the fp8 float32 group scale, or the MX row's
+  // eight E8M0 bytes (one per 32 elements) as two 32-bit words.
+  using ScaleWord = std::conditional_t<kMX, uint2, uint32_t>;
   static_assert(BN % kRowsPerPassB == 0, "BN must be a multiple of the rows per pass");
   static_assert(MODE == SMode::Down || kCB % 2 == 0, "gate/up needs gate and up blocks");
   static_assert(kRM >= 1 && BM % (16 * WM) == 0, "rows per wave must be a multiple of 16");
@@ -184,9 +191,10 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
   constexpr bool FP8 = C::kQ;    // quantised: 8-bit activation codes with scales
   constexpr bool MX = C::kMX;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::kSlot];
-  // Per stage and row: the fp8 float32 scale (as bits), or the MX row's four E8M0
-  // bytes for the stage's four 32-element blocks.
-  __shared__ __attribute__((aligned(16))) uint32_t sscale[FP8 ? 2 * C::kScales : 4];
+  // Per stage and row: the fp8 float32 scale (as bits), or the MX row's eight E8M0
+  // bytes for the stage's eight 32-element blocks.
+  using SW = typename C::ScaleWord;
+  __shared__ __attribute__((aligned(16))) SW sscale[FP8 ? 2 * C::kScales : 1];
   __shared__ int sched[kSchedInts];
   __shared__ int gcost[kSchedStride];
   __shared__ long long cpre[kSchedStride];
@@ -221,7 +229,9 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
     TileInfo t;
     int kdim, nk, n0;
   };
-  auto make_tile = [&](int tile) {
+  // gc: the caller's group cursor (a group at or before the tile's; tiles only move
+  // forward, so each role keeps one and the lookup scans forward from it).
+  auto make_tile = [&](int tile, int& gc) {
     Tile d;
     if constexpr (MODE == SMode::Router) {
       // One group of T rows read straight from x (the shared-expert row rule).
@@ -233,7 +243,8 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
       d.t.m0 = (tile % mt) * BM;
       d.t.nt = tile / mt;
     } else {
-      d.t = find_tile(sched, G, tile, a, BM);
+      gc = advance_group(sched, G, tile, gc);
+      d.t = tile_in_group(sched, gc, tile, a, BM);
     }
     d.kdim = (MODE != SMode::Down) ? H : (d.t.shared ? a.S : a.I);
     d.nk = d.kdim / C::kElems;
@@ -245,10 +256,21 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
                       : static_cast<size_t>(d.t.rowbase + m) * d.kdim;
   };
 
-  // Both roles pass one barrier per stage of the workgroup's tiles.
+  // Both roles pass one barrier per stage of the workgroup's tiles.  Every routed
+  // tile has the same stage count, and so does every shared-expert tile (the tiles
+  // from prefix[E] on), so the total needs only the number of the walk's tiles in
+  // that tail.
   const int last = walk.tile + (walk.end - 1 - walk.tile) / walk.step * walk.step;
-  int nstages = 0;
-  for (int t = walk.tile; t <= last; t += walk.step) nstages += make_tile(t).nk;
+  const int ntiles = (last - walk.tile) / walk.step + 1;
+  int nstages = ntiles * (H / C::kElems);
+  if constexpr (MODE != SMode::Router) {
+    const int nk_r = ((MODE == SMode::GateUp) ? H : a.I) / C::kElems;
+    const int nk_s = ((MODE == SMode::GateUp) ? H : a.S) / C::kElems;
+    const int first_shared = has_shared ? sched[a.E] : walk.end;
+    const int skip = first_shared <= walk.tile ? 0 : (first_shared - walk.tile + walk.step - 1) / walk.step;
+    const int n_shared = max(0, ntiles - skip);
+    nstages = (ntiles - n_shared) * nk_r + n_shared * nk_s;
+  }
 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (wave < kLoadWaves) {
@@ -292,7 +314,7 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
       return p;
     };
     // A row offsets and this thread's scale row of a tile (bytes; the stage's
-    // scale word is 4 bytes at 4 * stage).
+    // scale word is at sizeof(SW) * stage).
     struct Src {
       uint32_t a[C::kAPasses];
       const uint8_t* s;
@@ -398,7 +420,7 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
 
     struct Regs {
       uint4 a[C::kAPasses], b[C::kBPasses];
-      uint32_t s;
+      SW s;
     };
     auto gload = [&](Regs& R, const BPtr& P, const Src& S, int ks) {
       const uint32_t off = static_cast<uint32_t>(ks) * C::kRowDataA + lcol;
@@ -407,7 +429,7 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
       for (int q = 0; q < C::kBPasses; ++q) R.b[q] = ld16_stream(P.b[q] + offb);
 #pragma unroll
       for (int q = 0; q < C::kAPasses; ++q) R.a[q] = buf_ld16(arsrc, S.a[q] + off, 0);
-      if constexpr (FP8) R.s = *reinterpret_cast<const uint32_t*>(S.s + 4 * ks);
+      if constexpr (FP8) R.s = *reinterpret_cast<const SW*>(S.s + sizeof(SW) * ks);
     };
     auto lstore = [&](const Regs& R, int slot) {
       uint8_t* base = smem + slot * C::kSlot;
@@ -425,11 +447,12 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
 
     // The load cursor: stage ld_ks of tile ld; the next tile's dispatch rows are
     // already being fetched (np).
-    Tile ld = make_tile(walk.tile);
+    int lg = 0;   // group cursor of the look-ahead tile nld
+    Tile ld = make_tile(walk.tile, lg);
     Src ls = resolve(ld, fetch(ld));
     BPtr lb = make_b(ld);
     int ld_tile = walk.tile, ld_ks = 0;
-    Tile nld = make_tile(min(walk.tile + walk.step, last));
+    Tile nld = make_tile(min(walk.tile + walk.step, last), lg);
     Pend np = fetch(nld);
     auto issue = [&](Regs& R) {
       gload(R, lb, ls, ld_ks);
@@ -441,7 +464,7 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
         ls = resolve(ld, np);
         lb = make_b(ld);
         ld_ks = 0;
-        nld = make_tile(min(ld_tile + walk.step, last));
+        nld = make_tile(min(ld_tile + walk.step, last), lg);
         np = fetch(nld);
       }
       // else: past the workgroup's last stage; that stage is loaded again, unused.
@@ -500,33 +523,40 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
             for (int j = 0; j < C::kCB; ++j) acc[i][j] = mfma_bf16_16x16x32(af[i], bf[j], acc[i][j]);
         }
       } else if constexpr (MX) {
-        // 16x16x128 with A = MXFP8 codes (8-bit layout: lane group g holds bytes
-        // [16g, +16) and [64+16g, +16) of the row's 128 codes) and B = MXFP4 codes
-        // (4-bit layout: lane group g holds the 32 codes [32g, +32), bytes [16g, +16)
-        // of the row's 64).  The E8M0 scale of K-block g (elements [32g, +32)) of the
-        // lane's row comes from lane group g, byte g of the row's scale word.
-        const uint32_t* sc = sscale + slot * C::kScales;
-        i32x8 af[C::kRM], bf[C::kCB];
-        int sa[C::kRM], sb[C::kCB];
+        // Two 16x16x128 steps per stage (s = 0, 1: elements [128s, +128)), A = MXFP8
+        // codes (8-bit layout: lane group g holds bytes [16g, +16) and [64+16g, +16)
+        // of the step's 128 codes) and B = MXFP4 codes (4-bit layout: lane group g
+        // holds the 32 codes [32g, +32), bytes [16g, +16) of the step's 64).  The E8M0
+        // scale of K-block g of a step (its elements [32g, +32)) for the lane's row
+        // comes from lane group g: byte g of the row's scale word s.
+        const SW* sc = sscale + slot * C::kScales;
 #pragma unroll
-        for (int i = 0; i < C::kRM; ++i) {
-          const uint8_t* p = As + 16 * i * C::kRowStrideA;
-          const uint4 lo = lds_ld16(p + 16 * g);
-          const uint4 hi = lds_ld16(p + 64 + 16 * g);
-          af[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-          sa[i] = static_cast<int>((sc[wrow0 + 16 * i + r] >> (8 * g)) & 0xffu);
+        for (int s = 0; s < 2; ++s) {
+          i32x8 af[C::kRM], bf[C::kCB];
+          int sa[C::kRM], sb[C::kCB];
+#pragma unroll
+          for (int i = 0; i < C::kRM; ++i) {
+            const uint8_t* p = As + 16 * i * C::kRowStrideA + 128 * s;
+            const uint4 lo = lds_ld16(p + 16 * g);
+            const uint4 hi = lds_ld16(p + 64 + 16 * g);
+            af[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            const SW w = sc[wrow0 + 16 * i + r];
+            sa[i] = static_cast<int>(((s ? w.y : w.x) >> (8 * g)) & 0xffu);
+          }
+#pragma unroll
+          for (int j = 0; j < C::kCB; ++j) {
+            const int br = stream_b_row<MODE, BN, C::kWN, C::kCB>(wn, j, r);
+            const uint4 v = lds_ld16(Bs + br * C::kRowStrideB + 64 * s + 16 * g);
+            bf[j] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+            const SW w = sc[BM + br];
+            sb[j] = static_cast<int>(((s ? w.y : w.x) >> (8 * g)) & 0xffu);
+          }
+#pragma unroll
+          for (int i = 0; i < C::kRM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::kCB; ++j)
+              acc[i][j] = mfma_mxfp8_mxfp4_16x16x128(af[i], bf[j], acc[i][j], sa[i], sb[j]);
         }
-#pragma unroll
-        for (int j = 0; j < C::kCB; ++j) {
-          const int br = stream_b_row<MODE, BN, C::kWN, C::kCB>(wn, j, r);
-          const uint4 v = lds_ld16(Bs + br * C::kRowStrideB + 16 * g);
-          bf[j] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-          sb[j] = static_cast<int>((sc[BM + br] >> (8 * g)) & 0xffu);
-        }
-#pragma unroll
-        for (int i = 0; i < C::kRM; ++i)
-#pragma unroll
-          for (int j = 0; j < C::kCB; ++j) acc[i][j] = mfma_mxfp8_mxfp4_16x16x128(af[i], bf[j], acc[i][j], sa[i], sb[j]);
       } else {
         // Lane group g holds bytes [16g, +16) and [64+16g, +16) of its row's 128-byte group.
         const float* sc = reinterpret_cast<const float*>(sscale + slot * C::kScales);
@@ -633,7 +663,8 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
       }
     };
 
-    Tile cp = make_tile(walk.tile);
+    int cg = 0;   // group cursor of the computed tile
+    Tile cp = make_tile(walk.tile, cg);
     int cp_tile = walk.tile, cp_ks = 0;
     fetch_dst(cp);
     clear_acc();
@@ -646,7 +677,7 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
         cp_ks = 0;
         cp_tile += walk.step;
         if (cp_tile <= last) {
-          cp = make_tile(cp_tile);
+          cp = make_tile(cp_tile, cg);
           fetch_dst(cp);
         }
       }

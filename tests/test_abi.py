@@ -53,6 +53,10 @@ def _ws(cfg, T=4):
     (dict(hidden_size=5000), UNSUPPORTED),
     (dict(weight_dtype="fp8_e4m3_g128", moe_intermediate_size=1000), UNSUPPORTED),
     (dict(shared_expert_intermediate_size=100), UNSUPPORTED),
+    (dict(weight_dtype="mxfp4"), OK),
+    (dict(weight_dtype="mxfp4", moe_intermediate_size=384), UNSUPPORTED),
+    (dict(weight_dtype="mxfp4", shared_expert_intermediate_size=128), UNSUPPORTED),
+    (dict(weight_dtype="mxfp4", act_dtype="f32"), BAD_DTYPE),
     (dict(weight_dtype="f32"), BAD_DTYPE),
     (dict(act_dtype="f32", weight_dtype="fp8_e4m3_g128"), BAD_DTYPE),
     (dict(act_dtype="fp8_e4m3_g128", weight_dtype="fp8_e4m3_g128"), BAD_DTYPE),

@@ -71,6 +71,16 @@ def test_mxfp4_layer(shape, T, idx, alpha, tokens):
     _run(shape, T, W.base_seed(idx, T), alpha, tokens=None if tokens is None else Hn.sample_tokens(T, tokens))
 
 
+# A small MXFP4 layer (contraction of 2 stages) with ragged row tiles: one token,
+# 13 tokens and 64 tokens (~16 rows per expert).
+_SMALL_MX4 = W.LayerShape("small_mxfp4", 512, 8, 256, 2, 256, W.DT_MXFP4, W.DT_BF16)
+
+
+@pytest.mark.parametrize("T", [1, 13, 64])
+def test_mxfp4_small_ragged(T):
+    _run(_SMALL_MX4, T, W.base_seed(0, T) + 7)
+
+
 # Top-p trim before the budget [colibri issue_budget.md, "Relationship to existing
 # features"]: the per-token trim alone, and composed with the budget.
 @pytest.mark.parametrize("shape,T,seed,top_p,tokens", [

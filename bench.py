@@ -38,7 +38,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="drafter",
                    choices=["drafter", "narrow", "large", "large_fp8", "tiny", "ep_rank",
-                            "drafter_mxfp4", "narrow_mxfp4", "large_mxfp4"])
+                            "drafter_mxfp4", "narrow_mxfp4", "large_mxfp4", "drafter_fp8", "narrow_fp8"])
     p.add_argument("--tokens", type=int, default=None, help="T (default: the workload's bench size)")
     p.add_argument("--alpha", type=float, default=None, help="Zipf router skew for the large layers")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -60,6 +60,8 @@ def workload(args):
         "drafter_mxfp4": (W.DRAFTER_MX4, 1, 224, None),
         "narrow_mxfp4": (W.NARROW_MX4, 2, 224, None),
         "large_mxfp4": (W.LARGE_MX4, 3, 512, 0.0),
+        "drafter_fp8": (W.DRAFTER_FP8, 1, 224, None),
+        "narrow_fp8": (W.NARROW_FP8, 2, 224, None),
     }
     shape, idx, T, alpha = table[args.workload]
     if args.tokens is not None:

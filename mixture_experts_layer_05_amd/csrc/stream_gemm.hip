@@ -7,10 +7,11 @@
 //
 //   * a tile is BN weight rows of one group (routed expert or shared expert)
 //     against BM rows of tokens; the contraction runs in stages of 128 elements
-//     (bf16: 256 bytes per row; fp8: one 128-group, 128 bytes) or 256 elements
-//     (MXFP4 weights: 128 bytes per weight row, 256 bytes per MXFP8 activation
+//     (bf16: 256 bytes per row; fp8 when a contraction is not a multiple of 256:
+//     one 128-group, 128 bytes) or 256 elements (fp8: two groups, 256 bytes;
+//     MXFP4 weights: 128 bytes per weight row, 256 bytes per MXFP8 activation
 //     row).  Global loads give each row 128-256 contiguous bytes per wave
-//     instruction (64-byte row pieces load at well under half the rate);
+//     instruction (smaller row pieces load at a lower rate per byte);
 //   * a workgroup is 8 waves with two roles.  Four loader waves only load: they
 //     keep NS stages in flight in registers and write one stage per step into a
 //     double-buffered LDS stage.  Four compute waves read the other LDS buffer,
@@ -53,19 +54,25 @@ constexpr uint32_t kDeadRow = 0xC0000000u;
 // router logits z = x [W_r; w_g]^T over all T tokens (one group of T rows).
 enum class SMode { GateUp, Down, Router };
 
-// FMT is the weight dtype: kDtypeBf16; kDtypeFp8 (e4m3 codes, float32 scale per
-// row and 128-group, activations quantised the same way); kDtypeMxfp4 (E2M1 codes
-// two per byte, E8M0 scale per 32 elements, activations MXFP8).
+// FMT is the weight format: kDtypeBf16; kDtypeFp8 (e4m3 codes, float32 scale per
+// row and 128-group, activations quantised the same way) in stages of one group,
+// or kFp8Wide, the same in stages of two groups (contractions that are multiples
+// of 256); kDtypeMxfp4 (E2M1 codes two per byte, E8M0 scale per 32 elements,
+// activations MXFP8).
+constexpr int kFp8Wide = 0x12;
+
 template <SMode MODE, int BM, int BN, int WM, int FMT>
 struct StreamCfg {
   static constexpr bool kQ = FMT != kDtypeBf16;                // 8-bit activation codes + scales
   static constexpr bool kMX = FMT == kDtypeMxfp4;
+  static constexpr bool kWide = kMX || FMT == kFp8Wide;        // 256-element stages of 8-bit A
   static constexpr int kWM = WM;                               // compute waves along rows
   static constexpr int kWN = kComputeWaves / WM;               // compute waves along weight rows
   // Contraction elements per stage: 128 (one bf16 row slice of 256 bytes, or one fp8
-  // 128-group), 256 for MX so that a weight row still gives 128 contiguous bytes.
-  static constexpr int kElems = kMX ? 256 : 128;
-  static constexpr int kRowDataA = kQ && !kMX ? 128 : 256;     // A bytes per row per stage
+  // 128-group), 256 for wide fp8 and for MX (a weight row gives 128 contiguous
+  // bytes): 256-byte pieces load faster per byte than 128-byte ones.
+  static constexpr int kElems = kWide ? 256 : 128;
+  static constexpr int kRowDataA = kQ && !kWide ? 128 : 256;   // A bytes per row per stage
   static constexpr int kRowDataB = kMX ? 128 : kRowDataA;      // B bytes per row per stage
   static constexpr int kRowStrideA = kRowDataA + 8;            // padded LDS rows (8 mod 16)
   static constexpr int kRowStrideB = kRowDataB + 8;
@@ -80,9 +87,9 @@ struct StreamCfg {
   static constexpr int kBOff = BM * kRowStrideA;               // B rows inside a stage buffer
   static constexpr int kSlot = kBOff + BN * kRowStrideB;       // one LDS stage buffer
   static constexpr int kScales = BM + BN;                      // one scale word per row (below)
-  // Scale word of a row per stage: the fp8 float32 group scale, or the MX row's
-  // eight E8M0 bytes (one per 32 elements) as two 32-bit words.
-  using ScaleWord = std::conditional_t<kMX, uint2, uint32_t>;
+  // Scale word of a row per stage: the fp8 float32 group scale (two of them for
+  // wide fp8), or the MX row's eight E8M0 bytes (one per 32 elements).
+  using ScaleWord = std::conditional_t<kWide, uint2, uint32_t>;
   static_assert(BN % kRowsPerPassB == 0, "BN must be a multiple of the rows per pass");
   static_assert(MODE == SMode::Down || kCB % 2 == 0, "gate/up needs gate and up blocks");
   static_assert(kRM >= 1 && BM % (16 * WM) == 0, "rows per wave must be a multiple of 16");
@@ -558,37 +565,52 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
               acc[i][j] = mfma_mxfp8_mxfp4_16x16x128(af[i], bf[j], acc[i][j], sa[i], sb[j]);
         }
       } else {
-        // Lane group g holds bytes [16g, +16) and [64+16g, +16) of its row's 128-byte group.
-        const float* sc = reinterpret_cast<const float*>(sscale + slot * C::kScales);
-        i32x8 af[C::kRM], bf[C::kCB];
-        f32x4 sa[C::kRM];
-        float sb[C::kCB];
+        // One 16x16x128 step per 128-group of the stage (two for wide fp8).  Lane
+        // group g holds bytes [16g, +16) and [64+16g, +16) of its row's group.  The
+        // row scales of the accumulator rows 4g..4g+3 are rescaled in float32 per
+        // group.
+        constexpr int kSub = C::kWide ? 2 : 1;
+        const float* scf = reinterpret_cast<const float*>(sscale + slot * C::kScales);
 #pragma unroll
-        for (int i = 0; i < C::kRM; ++i) {
-          const uint8_t* p = As + 16 * i * C::kRowStrideA;
-          const uint4 lo = lds_ld16(p + 16 * g);
-          const uint4 hi = lds_ld16(p + 64 + 16 * g);
-          af[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-          sa[i] = *reinterpret_cast<const f32x4*>(&sc[wrow0 + 16 * i + 4 * g]);
-        }
+        for (int s = 0; s < kSub; ++s) {
+          i32x8 af[C::kRM], bf[C::kCB];
+          f32x4 sa[C::kRM];
+          float sb[C::kCB];
 #pragma unroll
-        for (int j = 0; j < C::kCB; ++j) {
-          const int br = stream_b_row<MODE, BN, C::kWN, C::kCB>(wn, j, r);
-          const uint8_t* p = Bs + br * C::kRowStrideB;
-          const uint4 lo = lds_ld16(p + 16 * g);
-          const uint4 hi = lds_ld16(p + 64 + 16 * g);
-          bf[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-          sb[j] = sc[BM + br];
-        }
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < C::kRM; ++i)
+          for (int i = 0; i < C::kRM; ++i) {
+            const uint8_t* p = As + 16 * i * C::kRowStrideA + 128 * s;
+            const uint4 lo = lds_ld16(p + 16 * g);
+            const uint4 hi = lds_ld16(p + 64 + 16 * g);
+            af[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            const int row = wrow0 + 16 * i + 4 * g;
+            if constexpr (C::kWide) {
+              // Two floats per row (groups 0 and 1 of the stage).
+              const f32x4 r01 = *reinterpret_cast<const f32x4*>(&scf[2 * row]);
+              const f32x4 r23 = *reinterpret_cast<const f32x4*>(&scf[2 * row + 4]);
+              sa[i] = s ? f32x4{r01[1], r01[3], r23[1], r23[3]} : f32x4{r01[0], r01[2], r23[0], r23[2]};
+            } else {
+              sa[i] = *reinterpret_cast<const f32x4*>(&scf[row]);
+            }
+          }
 #pragma unroll
           for (int j = 0; j < C::kCB; ++j) {
-            const f32x4 p = mfma_fp8_16x16x128(af[i], bf[j], zero);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(p[e], sa[i][e] * sb[j], acc[i][j][e]);
+            const int br = stream_b_row<MODE, BN, C::kWN, C::kCB>(wn, j, r);
+            const uint8_t* p = Bs + br * C::kRowStrideB + 128 * s;
+            const uint4 lo = lds_ld16(p + 16 * g);
+            const uint4 hi = lds_ld16(p + 64 + 16 * g);
+            bf[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            sb[j] = C::kWide ? scf[2 * (BM + br) + s] : scf[BM + br];
           }
+          const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int i = 0; i < C::kRM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::kCB; ++j) {
+              const f32x4 p = mfma_fp8_16x16x128(af[i], bf[j], zero);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(p[e], sa[i][e] * sb[j], acc[i][j][e]);
+            }
+        }
       }
     };
 
@@ -742,15 +764,22 @@ hipError_t launch_router_stream(const ExpertArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// fp8 runs in two-group stages when every contraction (H, I, S) is a multiple of 256.
+static bool fp8_wide(const ExpertArgs& a) { return a.H % 256 == 0 && a.I % 256 == 0 && a.S % 256 == 0; }
+
 hipError_t launch_gate_up_stream(const ExpertArgs& a, int weight_dtype, int64_t rho, hipStream_t stream) {
   if (weight_dtype == kDtypeMxfp4) return launch_stream_rho<SMode::GateUp, kDtypeMxfp4>(a, rho, stream);
-  if (weight_dtype == kDtypeFp8) return launch_stream_rho<SMode::GateUp, kDtypeFp8>(a, rho, stream);
+  if (weight_dtype == kDtypeFp8)
+    return fp8_wide(a) ? launch_stream_rho<SMode::GateUp, kFp8Wide>(a, rho, stream)
+                       : launch_stream_rho<SMode::GateUp, kDtypeFp8>(a, rho, stream);
   return launch_stream_rho<SMode::GateUp, kDtypeBf16>(a, rho, stream);
 }
 
 hipError_t launch_down_stream(const ExpertArgs& a, int weight_dtype, int64_t rho, hipStream_t stream) {
   if (weight_dtype == kDtypeMxfp4) return launch_stream_rho<SMode::Down, kDtypeMxfp4>(a, rho, stream);
-  if (weight_dtype == kDtypeFp8) return launch_stream_rho<SMode::Down, kDtypeFp8>(a, rho, stream);
+  if (weight_dtype == kDtypeFp8)
+    return fp8_wide(a) ? launch_stream_rho<SMode::Down, kFp8Wide>(a, rho, stream)
+                       : launch_stream_rho<SMode::Down, kDtypeFp8>(a, rho, stream);
   return launch_stream_rho<SMode::Down, kDtypeBf16>(a, rho, stream);
 }
 

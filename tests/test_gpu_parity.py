@@ -71,6 +71,16 @@ def test_mxfp4_layer(shape, T, idx, alpha, tokens):
     _run(shape, T, W.base_seed(idx, T), alpha, tokens=None if tokens is None else Hn.sample_tokens(T, tokens))
 
 
+# fp8 e4m3 group-128 weights on the decode layers (two-group streaming stages).
+@pytest.mark.parametrize("shape,T,idx,tokens", [
+    (W.DRAFTER_FP8, 7, 1, None),
+    (W.DRAFTER_FP8, 224, 1, 48),
+    (W.NARROW_FP8, 56, 2, None),
+])
+def test_fp8_decode_layer(shape, T, idx, tokens):
+    _run(shape, T, W.base_seed(idx, T), tokens=None if tokens is None else Hn.sample_tokens(T, tokens))
+
+
 # A small MXFP4 layer (contraction of 2 stages) with ragged row tiles: one token,
 # 13 tokens and 64 tokens (~16 rows per expert).
 _SMALL_MX4 = W.LayerShape("small_mxfp4", 512, 8, 256, 2, 256, W.DT_MXFP4, W.DT_BF16)

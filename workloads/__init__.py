@@ -75,6 +75,9 @@ LARGE_FP8 = LARGE.with_(name="large_fp8_budget64", weight_dtype=DT_FP8, expert_b
 # 4-bit (MXFP4) expert weights on the decode-bound layers [the 4-bit group-scaled
 # weights the pages point to for decode]: same shapes, synthetic MXFP4 codes.
 DRAFTER_MX4 = DRAFTER.with_(name="drafter_mxfp4", weight_dtype=DT_MXFP4)
+# The decode layers with fp8 e4m3 group-128 weights (no budget).
+DRAFTER_FP8 = DRAFTER.with_(name="drafter_fp8", weight_dtype=DT_FP8)
+NARROW_FP8 = NARROW.with_(name="narrow_fp8", weight_dtype=DT_FP8)
 NARROW_MX4 = NARROW.with_(name="narrow_mxfp4", weight_dtype=DT_MXFP4)
 LARGE_MX4 = LARGE.with_(name="large_mxfp4", weight_dtype=DT_MXFP4)
 

@@ -28,6 +28,9 @@ What it computes, step by step, each from the page that defines it:
    activations that enter an fp8 contraction (x before gate/up, h before down)
    are quantised per row per 128-group exactly as the kernels do, in float32
    (see oracle.e4m3.quantise_group128).
+7b. MXFP4 weights (E2M1 codes, one E8M0 scale per 32 elements) are used as
+   decoded code * 2^(e - 127); the activations entering their contractions are
+   quantised per row and 32-block to MXFP8 (see oracle.mx.quantise_mxfp8).
 
 Readings where the pages are silent (all listed in the design notes):
   * top-k selection is decided on float32 logits, ties to the lower expert id;

@@ -145,18 +145,24 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 
 // Per row and per 128-element group: amax, s = amax / 448 (1 if amax = 0),
 // q = e4m3(RNE(clamp(v / s, +-448))).  32 lanes (half a wave) per group, four
-// elements per lane.  Rows [0, rows_host) of src, or [0, *rows_dev) if rows_dev.
+// elements per lane.  Rows [0, rows_host) of src, or [0, *rows_dev) if rows_dev,
+// then, if seg1_items > 0, seg1_items more groups starting at element seg1 (the
+// shared expert's rows of h, in the same launch).
 template <bool SRC_BF16>
 __global__ void __launch_bounds__(256) quant_g128_kernel(const void* __restrict__ src, int rows_host,
                                                          const int32_t* __restrict__ rows_dev, int cols,
+                                                         size_t seg1, size_t seg1_items,
                                                          uint8_t* __restrict__ q, float* __restrict__ s) {
   const int rows = rows_dev ? *rows_dev : rows_host;
   const int ng = cols / kGroup;
-  const size_t items = static_cast<size_t>(rows) * ng;
+  const size_t items0 = static_cast<size_t>(rows) * ng;
+  const size_t items = items0 + seg1_items;
   const int half = threadIdx.x >> 5, hl = threadIdx.x & 31;
   for (size_t it = static_cast<size_t>(blockIdx.x) * 8 + half; it < items;
        it += static_cast<size_t>(gridDim.x) * 8) {
-    const size_t base = it * kGroup + 4 * hl;  // rows are contiguous: (row, group) -> it*128
+    // Rows are contiguous: (row, group) -> element it*128 of its segment.
+    const size_t g0 = it < items0 ? it * kGroup : seg1 + (it - items0) * kGroup;
+    const size_t base = g0 + 4 * hl;
     float v[4];
     if constexpr (SRC_BF16) {
       const uint2 p = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(src) + base);
@@ -178,7 +184,7 @@ __global__ void __launch_bounds__(256) quant_g128_kernel(const void* __restrict_
     int packed = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
     packed = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], packed, true);
     *reinterpret_cast<int*>(q + base) = packed;
-    if (hl == 0) s[it] = sc;
+    if (hl == 0) s[g0 / kGroup] = sc;
   }
 }
 
@@ -187,17 +193,22 @@ __global__ void __launch_bounds__(256) quant_g128_kernel(const void* __restrict_
 // >= -127 (0 for an all-zero block), scale byte s + 127, element = e4m3 RNE of
 // clamp(v * 2^-s, +-448).  2^-s is built from its exponent bits, so the product is
 // exact.  Eight lanes per block, four elements per lane.  Rows [0, rows_host) of
-// src, or [0, *rows_dev) if rows_dev.
+// src, or [0, *rows_dev) if rows_dev, then seg1_items more blocks from element
+// seg1 (as quant_g128_kernel).
 template <bool SRC_BF16>
 __global__ void __launch_bounds__(256) quant_mx8_kernel(const void* __restrict__ src, int rows_host,
                                                         const int32_t* __restrict__ rows_dev, int cols,
+                                                        size_t seg1, size_t seg1_items,
                                                         uint8_t* __restrict__ q, uint8_t* __restrict__ e8) {
   const int rows = rows_dev ? *rows_dev : rows_host;
-  const size_t items = static_cast<size_t>(rows) * (cols / kMxBlock);
+  const size_t items0 = static_cast<size_t>(rows) * (cols / kMxBlock);
+  const size_t items = items0 + seg1_items;
   const int blk = threadIdx.x >> 3, bl = threadIdx.x & 7;
   for (size_t it = static_cast<size_t>(blockIdx.x) * 32 + blk; it < items;
        it += static_cast<size_t>(gridDim.x) * 32) {
-    const size_t base = it * kMxBlock + 4 * bl;   // rows are contiguous: (row, block) -> it*32
+    // Rows are contiguous: (row, block) -> element it*32 of its segment.
+    const size_t b0 = it < items0 ? it * kMxBlock : seg1 + (it - items0) * kMxBlock;
+    const size_t base = b0 + 4 * bl;
     float v[4];
     if constexpr (SRC_BF16) {
       const uint2 p = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(src) + base);
@@ -222,7 +233,7 @@ __global__ void __launch_bounds__(256) quant_mx8_kernel(const void* __restrict__
     int packed = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
     packed = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], packed, true);
     *reinterpret_cast<int*>(q + base) = packed;
-    if (bl == 0) e8[it] = static_cast<uint8_t>(s + 127);
+    if (bl == 0) e8[b0 / kMxBlock] = static_cast<uint8_t>(s + 127);
   }
 }
 
@@ -286,43 +297,34 @@ hipError_t launch_combine(const ExpertArgs& a, hipStream_t stream) {
 hipError_t launch_quant_x(const ExpertArgs& a, uint8_t* xq, float* xs, hipStream_t stream) {
   const int64_t items = static_cast<int64_t>(a.T) * (a.H / kGroup);
   const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(ceil_div(items, 8), 4096)));
-  quant_g128_kernel<true><<<grid, 256, 0, stream>>>(a.x, a.T, nullptr, a.H, xq, xs);
+  quant_g128_kernel<true><<<grid, 256, 0, stream>>>(a.x, a.T, nullptr, a.H, 0, 0, xq, xs);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_x_mx(const ExpertArgs& a, uint8_t* xq, uint8_t* xe8, hipStream_t stream) {
   const int64_t items = static_cast<int64_t>(a.T) * (a.H / kMxBlock);
   const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(ceil_div(items, 32), 4096)));
-  quant_mx8_kernel<true><<<grid, 256, 0, stream>>>(a.x, a.T, nullptr, a.H, xq, xe8);
+  quant_mx8_kernel<true><<<grid, 256, 0, stream>>>(a.x, a.T, nullptr, a.H, 0, 0, xq, xe8);
   return hipGetLastError();
 }
 
+// One launch over h: the routed rows the dispatch kept (their count read on the
+// device from offsets[E]), then the shared expert's T rows at h_shared.
 hipError_t launch_quant_h_mx(const ExpertArgs& a, uint8_t* hq, uint8_t* he8, hipStream_t stream) {
-  // Routed rows: as many as the dispatch kept (read on the device from offsets[E]).
-  const int64_t items = static_cast<int64_t>(a.T) * a.K * (a.I / kMxBlock);
-  int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(ceil_div(items, 32), 4096)));
-  quant_mx8_kernel<false><<<grid, 256, 0, stream>>>(a.h, 0, a.offsets + a.E, a.I, hq, he8);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || a.S == 0) return err;
-  const int64_t items_s = static_cast<int64_t>(a.T) * (a.S / kMxBlock);
-  grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(ceil_div(items_s, 32), 4096)));
-  quant_mx8_kernel<false><<<grid, 256, 0, stream>>>(static_cast<const float*>(a.h) + a.h_shared, a.T,
-                                                    nullptr, a.S, hq + a.h_shared, he8 + a.h_shared / kMxBlock);
+  const int64_t items_s = a.S > 0 ? static_cast<int64_t>(a.T) * (a.S / kMxBlock) : 0;
+  const int64_t items = static_cast<int64_t>(a.T) * a.K * (a.I / kMxBlock) + items_s;
+  const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(ceil_div(items, 32), 4096)));
+  quant_mx8_kernel<false><<<grid, 256, 0, stream>>>(a.h, 0, a.offsets + a.E, a.I, a.h_shared,
+                                                    static_cast<size_t>(items_s), hq, he8);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_h(const ExpertArgs& a, uint8_t* hq, float* hs, hipStream_t stream) {
-  // Routed rows: as many as the dispatch kept (read on the device from offsets[E]).
-  const int64_t items = static_cast<int64_t>(a.T) * a.K * (a.I / kGroup);
-  int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(ceil_div(items, 8), 4096)));
-  quant_g128_kernel<false><<<grid, 256, 0, stream>>>(a.h, 0, a.offsets + a.E, a.I, hq, hs);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || a.S == 0) return err;
-  const int64_t items_s = static_cast<int64_t>(a.T) * (a.S / kGroup);
-  grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(ceil_div(items_s, 8), 4096)));
-  quant_g128_kernel<false><<<grid, 256, 0, stream>>>(static_cast<const float*>(a.h) + a.h_shared, a.T,
-                                                     nullptr, a.S, hq + a.h_shared,
-                                                     hs + a.h_shared / kGroup);
+  const int64_t items_s = a.S > 0 ? static_cast<int64_t>(a.T) * (a.S / kGroup) : 0;
+  const int64_t items = static_cast<int64_t>(a.T) * a.K * (a.I / kGroup) + items_s;
+  const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(ceil_div(items, 8), 4096)));
+  quant_g128_kernel<false><<<grid, 256, 0, stream>>>(a.h, 0, a.offsets + a.E, a.I, a.h_shared,
+                                                     static_cast<size_t>(items_s), hq, hs);
   return hipGetLastError();
 }
 

@@ -58,22 +58,25 @@ enum class SMode { GateUp, Down, Router };
 // row and 128-group, activations quantised the same way) in stages of one group,
 // or kFp8Wide, the same in stages of two groups (contractions that are multiples
 // of 256); kDtypeMxfp4 (E2M1 codes two per byte, E8M0 scale per 32 elements,
-// activations MXFP8).
+// activations MXFP8) in stages of 256 elements, or kMxWide, the same in stages of
+// 512 (contractions that are multiples of 512).
 constexpr int kFp8Wide = 0x12;
+constexpr int kMxWide = 0x13;
 
 template <SMode MODE, int BM, int BN, int WM, int FMT>
 struct StreamCfg {
   static constexpr bool kQ = FMT != kDtypeBf16;                // 8-bit activation codes + scales
-  static constexpr bool kMX = FMT == kDtypeMxfp4;
-  static constexpr bool kWide = kMX || FMT == kFp8Wide;        // 256-element stages of 8-bit A
+  static constexpr bool kMX = FMT == kDtypeMxfp4 || FMT == kMxWide;
+  static constexpr bool kWide = kMX || FMT == kFp8Wide;        // 8-bit A in stages of >= 256
   static constexpr int kWM = WM;                               // compute waves along rows
   static constexpr int kWN = kComputeWaves / WM;               // compute waves along weight rows
   // Contraction elements per stage: 128 (one bf16 row slice of 256 bytes, or one fp8
   // 128-group), 256 for wide fp8 and for MX (a weight row gives 128 contiguous
   // bytes): 256-byte pieces load faster per byte than 128-byte ones.
-  static constexpr int kElems = kWide ? 256 : 128;
-  static constexpr int kRowDataA = kQ && !kWide ? 128 : 256;   // A bytes per row per stage
-  static constexpr int kRowDataB = kMX ? 128 : kRowDataA;      // B bytes per row per stage
+  static constexpr int kElems = FMT == kMxWide ? 512 : kWide ? 256 : 128;
+  static constexpr int kRowDataA = kQ ? kElems : 256;          // A bytes per row per stage
+  static constexpr int kRowDataB = kMX ? kElems / 2 : kRowDataA;   // B bytes per row per stage
+  static constexpr int kSub = kQ ? kElems / 128 : 4;           // MFMA k-steps per stage
   static constexpr int kRowStrideA = kRowDataA + 8;            // padded LDS rows (8 mod 16)
   static constexpr int kRowStrideB = kRowDataB + 8;
   static constexpr int kLanesPerRowA = kRowDataA / 16;
@@ -88,8 +91,8 @@ struct StreamCfg {
   static constexpr int kSlot = kBOff + BN * kRowStrideB;       // one LDS stage buffer
   static constexpr int kScales = BM + BN;                      // one scale word per row (below)
   // Scale word of a row per stage: the fp8 float32 group scale (two of them for
-  // wide fp8), or the MX row's eight E8M0 bytes (one per 32 elements).
-  using ScaleWord = std::conditional_t<kWide, uint2, uint32_t>;
+  // wide fp8), or the MX row's E8M0 bytes (one per 32 elements: 8 or 16).
+  using ScaleWord = std::conditional_t<FMT == kMxWide, uint4, std::conditional_t<kWide, uint2, uint32_t>>;
   static_assert(BN % kRowsPerPassB == 0, "BN must be a multiple of the rows per pass");
   static_assert(MODE == SMode::Down || kCB % 2 == 0, "gate/up needs gate and up blocks");
   static_assert(kRM >= 1 && BM % (16 * WM) == 0, "rows per wave must be a multiple of 16");
@@ -538,7 +541,7 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
         // comes from lane group g: byte g of the row's scale word s.
         const SW* sc = sscale + slot * C::kScales;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
+        for (int s = 0; s < C::kSub; ++s) {
           i32x8 af[C::kRM], bf[C::kCB];
           int sa[C::kRM], sb[C::kCB];
 #pragma unroll
@@ -547,16 +550,16 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
             const uint4 lo = lds_ld16(p + 16 * g);
             const uint4 hi = lds_ld16(p + 64 + 16 * g);
             af[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            const SW w = sc[wrow0 + 16 * i + r];
-            sa[i] = static_cast<int>(((s ? w.y : w.x) >> (8 * g)) & 0xffu);
+            const uint32_t w = reinterpret_cast<const uint32_t*>(&sc[wrow0 + 16 * i + r])[s];
+            sa[i] = static_cast<int>((w >> (8 * g)) & 0xffu);
           }
 #pragma unroll
           for (int j = 0; j < C::kCB; ++j) {
             const int br = stream_b_row<MODE, BN, C::kWN, C::kCB>(wn, j, r);
             const uint4 v = lds_ld16(Bs + br * C::kRowStrideB + 64 * s + 16 * g);
             bf[j] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-            const SW w = sc[BM + br];
-            sb[j] = static_cast<int>(((s ? w.y : w.x) >> (8 * g)) & 0xffu);
+            const uint32_t w = reinterpret_cast<const uint32_t*>(&sc[BM + br])[s];
+            sb[j] = static_cast<int>((w >> (8 * g)) & 0xffu);
           }
 #pragma unroll
           for (int i = 0; i < C::kRM; ++i)
@@ -569,7 +572,7 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
         // group g holds bytes [16g, +16) and [64+16g, +16) of its row's group.  The
         // row scales of the accumulator rows 4g..4g+3 are rescaled in float32 per
         // group.
-        constexpr int kSub = C::kWide ? 2 : 1;
+        constexpr int kSub = C::kSub;
         const float* scf = reinterpret_cast<const float*>(sscale + slot * C::kScales);
 #pragma unroll
         for (int s = 0; s < kSub; ++s) {
@@ -767,8 +770,15 @@ hipError_t launch_router_stream(const ExpertArgs& a, hipStream_t stream) {
 // fp8 runs in two-group stages when every contraction (H, I, S) is a multiple of 256.
 static bool fp8_wide(const ExpertArgs& a) { return a.H % 256 == 0 && a.I % 256 == 0 && a.S % 256 == 0; }
 
+// MXFP4 runs in 512-element stages (256-byte weight row pieces) when the
+// projection's contractions are multiples of 512.
+static bool mx_wide_gate_up(const ExpertArgs& a) { return a.H % 512 == 0; }
+static bool mx_wide_down(const ExpertArgs& a) { return a.I % 512 == 0 && a.S % 512 == 0; }
+
 hipError_t launch_gate_up_stream(const ExpertArgs& a, int weight_dtype, int64_t rho, hipStream_t stream) {
-  if (weight_dtype == kDtypeMxfp4) return launch_stream_rho<SMode::GateUp, kDtypeMxfp4>(a, rho, stream);
+  if (weight_dtype == kDtypeMxfp4)
+    return mx_wide_gate_up(a) ? launch_stream_rho<SMode::GateUp, kMxWide>(a, rho, stream)
+                              : launch_stream_rho<SMode::GateUp, kDtypeMxfp4>(a, rho, stream);
   if (weight_dtype == kDtypeFp8)
     return fp8_wide(a) ? launch_stream_rho<SMode::GateUp, kFp8Wide>(a, rho, stream)
                        : launch_stream_rho<SMode::GateUp, kDtypeFp8>(a, rho, stream);
@@ -776,7 +786,9 @@ hipError_t launch_gate_up_stream(const ExpertArgs& a, int weight_dtype, int64_t 
 }
 
 hipError_t launch_down_stream(const ExpertArgs& a, int weight_dtype, int64_t rho, hipStream_t stream) {
-  if (weight_dtype == kDtypeMxfp4) return launch_stream_rho<SMode::Down, kDtypeMxfp4>(a, rho, stream);
+  if (weight_dtype == kDtypeMxfp4)
+    return mx_wide_down(a) ? launch_stream_rho<SMode::Down, kMxWide>(a, rho, stream)
+                           : launch_stream_rho<SMode::Down, kDtypeMxfp4>(a, rho, stream);
   if (weight_dtype == kDtypeFp8)
     return fp8_wide(a) ? launch_stream_rho<SMode::Down, kFp8Wide>(a, rho, stream)
                        : launch_stream_rho<SMode::Down, kDtypeFp8>(a, rho, stream);

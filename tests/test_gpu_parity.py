@@ -81,6 +81,16 @@ def test_fp8_decode_layer(shape, T, idx, tokens):
     _run(shape, T, W.base_seed(idx, T), tokens=None if tokens is None else Hn.sample_tokens(T, tokens))
 
 
+# A small fp8 layer on the two-group stages (H, I, S multiples of 256; the down
+# projection is one stage long) with ragged row tiles.
+_SMALL_FP8 = W.LayerShape("small_fp8_wide", 512, 8, 256, 2, 256, W.DT_FP8, W.DT_BF16)
+
+
+@pytest.mark.parametrize("T", [1, 13, 64])
+def test_fp8_small_ragged(T):
+    _run(_SMALL_FP8, T, W.base_seed(0, T) + 11)
+
+
 # A small MXFP4 layer (contraction of 2 stages) with ragged row tiles: one token,
 # 13 tokens and 64 tokens (~16 rows per expert).
 _SMALL_MX4 = W.LayerShape("small_mxfp4", 512, 8, 256, 2, 256, W.DT_MXFP4, W.DT_BF16)

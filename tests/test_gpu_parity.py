@@ -327,3 +327,33 @@ def test_activation_dtype_output(shape, T):
         assert err <= Hn.TOL["bf16"] + 2.0 ** -9, err
     else:
         assert torch.equal(y_act, y_host)
+
+
+# ----------------------------------------------------------------------------- seeded shape sweep
+
+def _sweep_shapes(n=40, seed=7):
+    """Small random layers over every dtype, with and without shared expert, budget
+    and top-p, sized so that some calls take the decode streaming kernels and some
+    the LDS-tiled ones."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dt = (W.DT_BF16, W.DT_FP8, W.DT_MXFP4, W.DT_F32)[i % 4]
+        q = 256 if dt == W.DT_MXFP4 else 128
+        H = int(rng.integers(1, 4)) * q if dt != W.DT_MXFP4 else int(rng.integers(1, 3)) * q
+        E = int(rng.integers(1, 41))
+        K = int(rng.integers(1, min(E, 8) + 1))
+        I = min(int(rng.choice([1, 2, 4])) * q, 512)
+        S = int(rng.choice([0, 1, 2])) * q
+        T = int(rng.choice([1, 5, 37, 100, 300, 640]))
+        budget = int(rng.integers(1, E + 1)) if rng.random() < 0.3 else 0
+        top_p = float(np.round(rng.uniform(0.3, 0.9), 2)) if rng.random() < 0.3 else 0.0
+        act = W.DT_F32 if dt == W.DT_F32 else W.DT_BF16
+        shape = W.LayerShape(f"sweep{i}_{dt}", H, E, I, K, S, dt, act, expert_budget=budget, top_p=top_p)
+        out.append((shape, T, 500 + i))
+    return out
+
+
+@pytest.mark.parametrize("shape,T,seed", _sweep_shapes(), ids=lambda v: getattr(v, "name", str(v)))
+def test_seeded_shape_sweep(shape, T, seed):
+    _run(shape, T, seed)

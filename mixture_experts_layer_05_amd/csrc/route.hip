@@ -120,6 +120,8 @@ __global__ void __launch_bounds__(256) topk_kernel(
     for (int p = 1; p < parts; ++p) s += zr[static_cast<size_t>(p) * plane + c];
     return s;
   };
+  // The shared-expert gate logit is read up front, next to the expert logits.
+  const float gate_logit = (has_shared && lane == 0) ? logit(E) : 0.f;
   float v[kMaxExperts / kWave];
 #pragma unroll
   for (int j = 0; j < kMaxExperts / kWave; ++j) {
@@ -186,7 +188,7 @@ __global__ void __launch_bounds__(256) topk_kernel(
     topk_ids[static_cast<size_t>(t) * K + lane] = kept ? my_id : -1;
     topk_w[static_cast<size_t>(t) * K + lane] = pk / denom;
   }
-  if (has_shared && lane == 0) shared_gate[t] = 1.0f / (1.0f + expf(-logit(E)));
+  if (has_shared && lane == 0) shared_gate[t] = 1.0f / (1.0f + expf(-gate_logit));
 }
 
 // ------------------------------------------------------------------ expert budget

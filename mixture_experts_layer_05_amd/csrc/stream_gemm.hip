@@ -6,18 +6,21 @@
 // The kernel is built around keeping enough of that stream in flight:
 //
 //   * a tile is BN weight rows of one group (routed expert or shared expert)
-//     against BM rows of tokens; the contraction runs in stages of 128 elements
-//     (bf16: 256 bytes per row; fp8 when a contraction is not a multiple of 256:
-//     one 128-group, 128 bytes) or 256 elements (fp8: two groups, 256 bytes;
-//     MXFP4 weights: 128 bytes per weight row, 256 bytes per MXFP8 activation
-//     row).  Global loads give each row 128-256 contiguous bytes per wave
-//     instruction (smaller row pieces load at a lower rate per byte);
+//     against BM rows of tokens; the contraction runs in stages that give every
+//     row 256 contiguous bytes where the contraction allows: 128 elements of
+//     bf16, 256 of fp8 (two 128-groups; one group, 128 bytes, when a contraction
+//     is not a multiple of 256), 512 of MXFP4 weights (256 bytes of codes per
+//     weight row, 512 per MXFP8 activation row; 256 elements when a contraction
+//     is not a multiple of 512).  Per workgroup, 256-byte row pieces load ~40 %
+//     more bytes per clock than 128-byte ones (measured); larger ones gain
+//     nothing;
 //   * a workgroup is 8 waves with two roles.  Four loader waves only load: they
 //     keep NS stages in flight in registers and write one stage per step into a
 //     double-buffered LDS stage.  Four compute waves read the other LDS buffer,
-//     run the MFMAs (16x16x32 bf16 or 16x16x128 fp8, fp8 partial sums rescaled by
-//     the row and column group scales in float32) and write the results.  One
-//     barrier per stage hands the buffers over;
+//     run the MFMAs (16x16x32 bf16; 16x16x128 fp8 with the row and column group
+//     scales applied to each group's partial sum in float32; the block-scaled
+//     16x16x128 fp8 x fp4 MFMA for MXFP4, which applies the E8M0 scales itself)
+//     and write the results.  One barrier per stage hands the buffers over;
 //   * the split keeps the loaders' wait counts exact: a wave's vector-memory
 //     counter covers its loads and its stores alike, and the compiler waits for
 //     everything once a store is pending, so a wave that also wrote results would
@@ -26,10 +29,11 @@
 //     group are read through a buffer descriptor at an offset past its end (zeros),
 //     the stages past the workgroup's last one re-read that stage, and the dispatch
 //     rows of a tile are fetched a whole tile before their first use;
-//   * one workgroup per CU, 256 VGPRs per lane: the loaders hold NS = 3..6 stages
-//     (~100-150 KB per CU in flight); measured, deeper staging no longer moves
-//     the rate, which sits near 14 bytes per clock per CU of loads (HBM and L2
-//     alike), so the remaining lever is fewer bytes per tile;
+//   * one workgroup per CU, 256 VGPRs per lane: the loaders hold NS = 2..6
+//     stages (~100-150 KB per CU in flight); measured, deeper staging no longer
+//     moves the rate: a CU keeps ~11 KB of loads outstanding, so its rate is
+//     that over the latency (~10 B/clk from HBM, more from L2), and the
+//     remaining lever is fewer bytes per tile;
 //   * tiles are spread by their cost in stages (see balanced_walk);
 //   * gate/up tiles fuse SwiGLU and write h; down tiles write each routed slot's
 //     output row (unweighted) and the shared expert's rows (weighted by sigmoid(g)).

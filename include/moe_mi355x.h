@@ -171,8 +171,9 @@ int moe_dispatch(const moe_config* cfg, int32_t num_tokens, const int32_t* topk_
  *          + shared_gate[t] * down_s(silu(gate_s x_t) * up_s x_t)
  * with e = topk_ids[t,k], taken through the dispatch outputs.  y (device) out
  * [T, H] float32, 16-byte aligned, overwritten.  The intermediate activations
- * are stored in the workspace as bf16 (BF16 weights), float32 (F32) or e4m3 +
- * group-128 scales (FP8).  Accumulation is float32.  Each routed slot's
+ * are stored in the workspace as bf16 (BF16 weights), float32 (F32), e4m3 +
+ * group-128 scales (FP8) or MXFP8 codes + E8M0 block-32 scales (MXFP4; x is
+ * quantised the same way).  Accumulation is float32.  Each routed slot's
  * down-projection row is kept in the workspace and the slots of a token are
  * added to y in slot order after the shared term, so y is bit-reproducible
  * (no atomics).  Slots with weight 0 (dropped by the budget) are skipped.

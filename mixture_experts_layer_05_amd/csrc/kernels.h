@@ -14,8 +14,9 @@ namespace moe {
 //
 // Intermediate activations h: routed rows first, in dispatch (perm) order,
 // [T*K, I]; then the shared expert's rows [T, S] starting at element h_shared.
-// With fp8 weights h is kept in float32 and then quantised to hq / hs with the
-// same layout (hs has one float per 128 elements).
+// With fp8 or MXFP4 weights h is kept in float32 and then quantised to hq with
+// the same layout, its scales in hs (fp8: one float per 128 elements) or he8
+// (MXFP8: one E8M0 byte per 32 elements).
 struct ExpertArgs {
   const void* x;                 // [T, H] act dtype
   const int32_t* counts;         // [E]

@@ -58,6 +58,13 @@ def test_large_layer_8192_skewed_sampled():
     _run(W.LARGE, 8192, W.base_seed(3, 8192), 1.5, tokens=Hn.sample_tokens(8192, 16))
 
 
+# The rest of the large layer's (T, alpha) grid, on sampled tokens: the middle
+# skew at every size, the skewed middle size and the uniform full size.
+@pytest.mark.parametrize("T,alpha", [(512, 1.0), (2048, 1.0), (2048, 1.5), (8192, 0.0), (8192, 1.0)])
+def test_large_layer_grid_sampled(T, alpha):
+    _run(W.LARGE, T, W.base_seed(3, T), alpha, tokens=Hn.sample_tokens(T, 16))
+
+
 # MXFP4 expert weights x MXFP8 activations (block-scaled fp8 x fp4 contraction).
 @pytest.mark.parametrize("shape,T,idx,alpha,tokens", [
     (W.DRAFTER_MX4, 7, 1, None, None),

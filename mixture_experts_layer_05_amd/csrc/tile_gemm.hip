@@ -11,8 +11,8 @@
 // same XCD, so those operands are fetched from HBM once per XCD and hit that
 // XCD's L2 afterwards.  Three kernels:
 //
-//   * tiled4_expert_kernel (bf16, 256-row tiles): 4 waves of 128 x 128 with
-//     32x32x16 MFMAs; see its own description below.
+//   * tiledpp_expert_kernel (bf16, 256-row tiles): 8 waves (two per SIMD) of
+//     128 x 64 with 32x32x16 MFMAs; see its own description below.
 //   * tiled8_expert_kernel (fp8, 256-row tiles): 4 waves of 128 x 64 with
 //     16x16x128 fp8 MFMAs and all operands loaded by LDS DMA; see below.
 //   * tiled_expert_kernel (128-row tiles, bf16 and fp8): 8 waves of 64 x 64.
@@ -286,23 +286,16 @@ __global__ void __launch_bounds__(kTileThreads) tiled_expert_kernel(ExpertArgs a
   }
 }
 
-// ---------------------------------------------------------------- 256 x 256, 4 waves (bf16)
+// ---------------------------------------------------------------- 256-row tiles: shared pieces
 //
-// The bf16 prefill tile: 256 x 256 outputs per workgroup of 4 waves, each wave a
-// 128 x 128 sub-tile held as 4 x 4 blocks of 32x32 (the 256 accumulator
-// registers; one wave per SIMD).  With one wave per SIMD the 32x32x16 bf16 MFMA
-// sustains close to the chip's peak, the 16x16x32 one about half of it
-// (measured), and a 128 x 128 wave tile needs half the LDS fragment bytes per
-// flop of a 64 x 64 one.
-//
-// A stage is 64 contraction elements: 128 bytes of each of the 256 A rows and 256
-// B rows (64 KiB), double-buffered in LDS.  Full 128-byte row pieces matter: from
-// L2, a CU receives about 2.5x the bytes per clock with 128-byte pieces than with
-// 64-byte ones (measured).
+// A stage of the 256-row kernels is 64 contraction elements of bf16 (or one
+// 128-element fp8 group): 128 bytes of each A row and B row, double-buffered in
+// LDS.  Full 128-byte row pieces matter: from L2, a CU receives about 2.5x the
+// bytes per clock with 128-byte pieces than with 64-byte ones (measured).
 //   * A (gathered activation rows, mostly L2 hits) goes memory -> LDS directly,
 //     one stage ahead, with buffer loads carrying the LDS flag (each wave
 //     instruction writes 64 lanes x 16 bytes = 1 KiB of consecutive LDS);
-//   * B (weight rows, streamed from HBM) is loaded into registers two stages
+//   * bf16 B (weight rows, streamed from HBM) is loaded into registers two stages
 //     ahead and written to LDS one stage ahead, which keeps two stages of the
 //     HBM stream in flight per CU within the LDS budget.
 // Rows are stored unpadded with their eight 16-byte pieces permuted by
@@ -311,7 +304,6 @@ __global__ void __launch_bounds__(kTileThreads) tiled_expert_kernel(ExpertArgs a
 constexpr int kT4Threads = 256;
 constexpr int kT4RowBytes = 128;                        // 64 bf16 per row per stage
 constexpr int kT4Stage = (256 + 256) * kT4RowBytes;     // 64 KiB
-constexpr int kT4Insts = 256 * kT4RowBytes / 1024 / 4;  // DMA instructions per wave per operand (8)
 
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)p));
@@ -350,6 +342,18 @@ __device__ __forceinline__ void dma8_rows(i32x4_t rsrc, const uint32_t (&voff)[8
                :
                : [v0] "v"(voff[0]), [v1] "v"(voff[1]), [v2] "v"(voff[2]), [v3] "v"(voff[3]),
                  [v4] "v"(voff[4]), [v5] "v"(voff[5]), [v6] "v"(voff[6]), [v7] "v"(voff[7]),
+                 [rs] "s"(rsrc), [so] "s"(__builtin_amdgcn_readfirstlane(soff)),
+                 [lds] "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "scc");
+}
+
+// The same, four instructions (voff[0..3]).
+__device__ __forceinline__ void dma4_rows(i32x4_t rsrc, const uint32_t (&voff)[4], uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %[lds]\n\t"
+               MOE_DMA_LINE("%[v0]", "%[so]") MOE_DMA_NEXT MOE_DMA_LINE("%[v1]", "%[so]") MOE_DMA_NEXT
+               MOE_DMA_LINE("%[v2]", "%[so]") MOE_DMA_NEXT MOE_DMA_LINE("%[v3]", "%[so]")
+               :
+               : [v0] "v"(voff[0]), [v1] "v"(voff[1]), [v2] "v"(voff[2]), [v3] "v"(voff[3]),
                  [rs] "s"(rsrc), [so] "s"(__builtin_amdgcn_readfirstlane(soff)),
                  [lds] "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "scc");
@@ -397,15 +401,28 @@ __device__ __forceinline__ f32x16 mfma_bf16_32x32x16(uint4 a, uint4 b, f32x16 c)
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// ---------------------------------------------------------------- 256 x 256, 8 waves (bf16)
+//
+// The bf16 prefill tile: 256 x 256 outputs per workgroup of 8 waves, two per
+// SIMD.  Wave w computes rows [128 (w / 4), +128) x one quarter of the tile's
+// columns as 4 x 2 blocks of 32x32 (32x32x16 MFMAs, 128 accumulator registers),
+// so that one wave's fragment reads and waits overlap the other's MFMAs.  With
+// one wave per SIMD (4 waves of 128 x 128, 256 accumulators each) the same tile
+// ran 9.5 % slower on the large layer's gate/up (measured); the 32x32x16 MFMA
+// sustains close to the chip's peak where the 16x16x32 one reaches about half.
+// Per stage each wave issues 4 DMA instructions of activation rows, then 4
+// register loads of weight rows.
+constexpr int kPPThreads = 512;
+
 template <Mode MODE>
-__global__ void __launch_bounds__(kT4Threads) tiled4_expert_kernel(ExpertArgs a) {
+__global__ void __launch_bounds__(kPPThreads) tiledpp_expert_kernel(ExpertArgs a) {
   constexpr int BM = 256, BN = 256;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kT4Stage];
   __shared__ int prefix[kSchedInts];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
 
   const bool has_shared = a.S > 0;
   const int G = a.E + (has_shared ? 1 : 0);
@@ -416,18 +433,16 @@ __global__ void __launch_bounds__(kT4Threads) tiled4_expert_kernel(ExpertArgs a)
   const int total = build_tile_prefix(prefix, a.counts, a.offsets, a.E, a.T, has_shared, BM, nt_r, nt_s);
 
   // DMA lane mapping: instruction q of this wave covers tile rows
-  // 8 (kT4Insts wave + q) + lane / 8; LDS piece lane % 8 holds global piece
-  // (lane % 8) ^ ((row / 2) mod 8), which depends only on q's parity here.
+  // 8 (4 wave + q) + lane / 8; LDS piece lane % 8 holds global piece
+  // (lane % 8) ^ ((row / 2) mod 8), which depends only on q's parity.
   const int drow = lane >> 3;
   uint32_t dpiece[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) dpiece[h] = static_cast<uint32_t>(((lane & 7) ^ ((4 * h + (drow >> 1)) & 7)) * 16);
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(smem));
-  // Fragment reads (32x32x16): lane row r32 = lane % 32 of a 32-row block, piece
-  // 2 kk + lane / 32 for contraction step kk of the stage.
   const int r32 = lane & 31, hi = lane >> 5;
   const uint32_t fswz = static_cast<uint32_t>(hi ^ ((r32 >> 1) & 7));
-  // B register rows t / 8 + 32 q: the piece permutation depends on t / 8 only.
+  // B register rows t / 8 + 64 q: the piece permutation depends on t / 8 only.
   const uint32_t bldsoff = static_cast<uint32_t>((tid >> 3) * kT4RowBytes + (((tid & 7) ^ ((tid >> 4) & 7)) * 16));
 
   const XcdWalk walk(total);
@@ -447,10 +462,10 @@ __global__ void __launch_bounds__(kT4Threads) tiled4_expert_kernel(ExpertArgs a)
     i32x4_t ra;
     const uint8_t* b0p;   // B rows [0, 128) of the tile
     const uint8_t* b1p;   // B rows [128, 256)
-    uint32_t aoff[kT4Insts];
+    uint32_t aoff[4];
 #pragma unroll
-    for (int q = 0; q < kT4Insts; ++q) {
-      const int m = min(t.m0 + 8 * (kT4Insts * wave + q) + drow, t.rows - 1);
+    for (int q = 0; q < 4; ++q) {
+      const int m = min(t.m0 + 8 * (4 * wave + q) + drow, t.rows - 1);
       if constexpr (MODE == Mode::GateUp)
         aoff[q] = static_cast<uint32_t>(row_token(a, t, m)) * krow + dpiece[q & 1];
       else
@@ -477,38 +492,35 @@ __global__ void __launch_bounds__(kT4Threads) tiled4_expert_kernel(ExpertArgs a)
     const __amdgpu_buffer_rsrc_t rb1v = buf_rsrc(b1p, 128 * krow);
     const uint32_t bvoff = static_cast<uint32_t>(tid >> 3) * krow + (tid & 7) * 16;
 
-    // A (activation rows, mostly L2 hits) goes memory -> LDS by DMA one stage
-    // ahead.  B (weight rows, streamed from HBM) is loaded into registers two
-    // stages ahead and written to LDS one stage ahead: thread t holds rows
-    // t / 8 + 32 q (q < 8; q < 4 from rb0, the rest from rb1), piece t % 8.
     auto issue_a = [&](int ks) {
-      const uint32_t buf = lds0 + static_cast<uint32_t>(ks & 1) * kT4Stage + kT4Insts * wave * 1024;
-      dma8_rows(ra, aoff, static_cast<uint32_t>(ks) * kT4RowBytes, buf);
+      const uint32_t buf = lds0 + static_cast<uint32_t>(ks & 1) * kT4Stage + 4 * wave * 1024;
+      dma4_rows(ra, aoff, static_cast<uint32_t>(ks) * kT4RowBytes, buf);
     };
     struct BRegs {
-      uint4 v[8];
+      uint4 v[4];
     };
+    // Thread t holds B rows t / 8 + 64 q (q < 2 from rb0, the rest from rb1), piece t % 8.
     auto load_b = [&](BRegs& R, int ks) {
       const uint32_t kb = static_cast<uint32_t>(ks) * kT4RowBytes;
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        R.v[q] = buf_ld16(q < 4 ? rb0v : rb1v, bvoff, kb + 32 * (q & 3) * krow);
+      for (int q = 0; q < 4; ++q)
+        R.v[q] = buf_ld16(q < 2 ? rb0v : rb1v, bvoff, kb + 64 * (q & 1) * krow);
     };
     auto store_b = [&](const BRegs& R, int ks) {
       uint8_t* dst = smem + (ks & 1) * kT4Stage + BM * kT4RowBytes + bldsoff;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) *reinterpret_cast<uint4*>(dst + 32 * q * kT4RowBytes) = R.v[q];
+      for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(dst + 64 * q * kT4RowBytes) = R.v[q];
     };
 
     constexpr int NI = 4;                      // 32-row blocks per wave
-    constexpr int NJ = 4;                      // 32-column blocks per wave
+    constexpr int NJ = 2;                      // 32-column blocks per wave
     const int arow0 = wm * 128;
 
-    // LDS row of B feeding 32-column block j.  Gate/up: the first half of the
-    // blocks are gate rows, the second half the up rows of the same columns.
+    // LDS row of B feeding 32-column block j.  Gate/up: block 0 is the gate rows,
+    // block 1 the up rows of the wave's 32 intermediate columns.
     auto brow = [&](int j) -> int {
-      if constexpr (MODE == Mode::GateUp) return ((j < 2) ? 0 : BN / 2) + wn * 64 + 32 * (j & 1) + r32;
-      else return wn * 128 + 32 * j + r32;
+      if constexpr (MODE == Mode::GateUp) return (j == 0 ? 0 : BN / 2) + wn * 32 + r32;
+      else return wn * 64 + 32 * j + r32;
     };
 
     f32x16 acc[NI][NJ];
@@ -541,27 +553,25 @@ __global__ void __launch_bounds__(kT4Threads) tiled4_expert_kernel(ExpertArgs a)
     // nk is even (contractions are multiples of 128).  Iteration ks: wait for
     // A(ks); barrier; write B(ks + 1) from registers and start A(ks + 1) into
     // the other buffer; refill those registers with B(ks + 3); multiply stage
-    // ks.  The register loads are issued unconditionally (past the end they
-    // re-read the last stage, an L2 hit), so every iteration has the same
-    // number of loads in flight and the compiler's waits for the registers stay
-    // exact.
+    // ks.  Each wait leaves only the newest 4 register loads in flight.  The
+    // register loads are issued unconditionally (past the end they re-read the
+    // last stage, an L2 hit), so every iteration has the same number of loads
+    // in flight and the compiler's waits for the registers stay exact.
     BRegs R0, R1;
     load_b(R0, 0);
     load_b(R1, 1);
     __syncthreads();                 // the previous tile is done with both buffers
-    store_b(R0, 0);                  // (the compiler waits for R0's loads)
+    store_b(R0, 0);
     issue_a(0);
     load_b(R0, min(2, nk - 1));
     for (int ks = 0; ks < nk; ks += 2) {
-      // Even stage ks: after A(ks) come B(ks + 2)'s 8 register loads.
-      wait_vm<8>();
+      wait_vm<4>();
       __syncthreads();
       store_b(R1, ks + 1);
       issue_a(ks + 1);
       load_b(R1, min(ks + 3, nk - 1));
       compute(ks);
-      // Odd stage ks + 1: after A(ks + 1) come B(ks + 3)'s 8 register loads.
-      wait_vm<8>();
+      wait_vm<4>();
       __syncthreads();
       if (ks + 2 < nk) {
         store_b(R0, ks + 2);
@@ -578,22 +588,17 @@ __global__ void __launch_bounds__(kT4Threads) tiled4_expert_kernel(ExpertArgs a)
       const int width = t.shared ? a.S : a.I;
       uint16_t* hbase = static_cast<uint16_t*>(a.h) +
                         (t.shared ? static_cast<size_t>(a.h_shared) : static_cast<size_t>(t.rowbase) * width);
-      const int col0 = n0 + wn * 64 + r32;
-      constexpr int NH = NJ / 2;             // gate blocks (each paired with an up block)
+      const int col = n0 + wn * 32 + r32;
 #pragma unroll
       for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int m = t.m0 + arow0 + 32 * i + 8 * (v >> 2) + 4 * hi + (v & 3);
-          if (m < t.rows) {
-            uint16_t* hr = hbase + static_cast<size_t>(m) * width + col0;
-#pragma unroll
-            for (int jh = 0; jh < NH; ++jh)
-              hr[32 * jh] = f32_to_bf16_bits(silu_f32(acc[i][jh][v]) * acc[i][jh + NH][v]);
-          }
+          if (m < t.rows)
+            hbase[static_cast<size_t>(m) * width + col] = f32_to_bf16_bits(silu_f32(acc[i][0][v]) * acc[i][1][v]);
         }
     } else {
-      const int col0 = n0 + wn * 128 + r32;
+      const int col0 = n0 + wn * 64 + r32;
 #pragma unroll
       for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -875,7 +880,7 @@ hipError_t launch_gate_up_tiled(const ExpertArgs& a, bool fp8, bool tall, hipStr
   const int grid = tiled_grid(a, BM, a.I / hcols, a.S / hcols);
   if (tall) {
     if (fp8) tiled8_expert_kernel<Mode::GateUp><<<grid, kT4Threads, 0, stream>>>(a);
-    else tiled4_expert_kernel<Mode::GateUp><<<grid, kT4Threads, 0, stream>>>(a);
+    else tiledpp_expert_kernel<Mode::GateUp><<<grid, kPPThreads, 0, stream>>>(a);
   } else {
     if (fp8) tiled_expert_kernel<Mode::GateUp, 128, 256, true><<<grid, kTileThreads, 0, stream>>>(a);
     else tiled_expert_kernel<Mode::GateUp, 128, 256, false><<<grid, kTileThreads, 0, stream>>>(a);
@@ -890,7 +895,7 @@ hipError_t launch_down_tiled(const ExpertArgs& a, bool fp8, bool tall, hipStream
   const int grid = tiled_grid(a, BM, a.H / ycols, a.H / ycols);
   if (tall) {
     if (fp8) tiled8_expert_kernel<Mode::Down><<<grid, kT4Threads, 0, stream>>>(a);
-    else tiled4_expert_kernel<Mode::Down><<<grid, kT4Threads, 0, stream>>>(a);
+    else tiledpp_expert_kernel<Mode::Down><<<grid, kPPThreads, 0, stream>>>(a);
   } else {
     if (fp8) tiled_expert_kernel<Mode::Down, 128, 256, true><<<grid, kTileThreads, 0, stream>>>(a);
     else tiled_expert_kernel<Mode::Down, 128, 256, false><<<grid, kTileThreads, 0, stream>>>(a);

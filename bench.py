@@ -319,23 +319,22 @@ def main():
     acc = [accounting(shape, T, L.counts.cpu().numpy(), router=not ep_rank) for L in layers]
     a = {k: float(np.mean([d[k] for d in acc])) for k in acc[0]}
     tokens_per_s = T / (ms_per_step * 1e-3)
-    # Dominant kernel: gate/up + SwiGLU.  Below 48 rows per expert it runs on the
-    # weight-streaming kernel (HBM-bound: weights + x in, h out); above, on the
-    # LDS-tiled MFMA kernel (bound by the MFMA rate of the weight dtype).
-    rho = T * shape.num_experts_per_tok / shape.n_routed_experts
-    if rho >= 48 and shape.weight_dtype != "f32":
+    # Dominant kernel: gate/up + SwiGLU, against the roofline that binds it: its
+    # algorithmic bytes at the HBM peak or its algorithmic FLOPs at the weight
+    # dtype's dense MFMA peak, whichever takes longer.
+    peak_tf = MFMA_PEAK_TFLOPS[shape.weight_dtype]
+    t_hbm = a["gate_up_bytes"] / (HBM_PEAK_GBPS * 1e9)
+    t_mfma = a["gate_up_flops"] / (peak_tf * 1e12)
+    kernel = gate_up_kernel(shape, T)
+    traffic = stored_traffic("gate_up", f"{args.workload}_T{T}", kernel_source_file(kernel))
+    if t_mfma > t_hbm and shape.weight_dtype != "f32":
         achieved = a["gate_up_flops"] / (gate_up_ms * 1e-3) / 1e12
-        peak = MFMA_PEAK_TFLOPS[shape.weight_dtype]
-        roof = {"bound": "mfma", "kernel": gate_up_kernel(shape, T), "achieved": round(achieved, 1),
-                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": stored_traffic("gate_up", f"{args.workload}_T{T}",
-                                          kernel_source_file(gate_up_kernel(shape, T)))}
+        roof = {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 1), "peak": peak_tf,
+                "unit": "TFLOP/s", "frac": round(achieved / peak_tf, 4), "traffic": traffic}
     else:
         achieved = a["gate_up_bytes"] / (gate_up_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": gate_up_kernel(shape, T), "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": stored_traffic("gate_up", f"{args.workload}_T{T}",
-                                          kernel_source_file(gate_up_kernel(shape, T)))}
+        roof = {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic}
     line = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),

@@ -126,7 +126,7 @@ def gate_up_kernel(shape, T: int) -> str:
     if rho >= 48 and dt != "mxfp4":   # MXFP4 runs on the streaming kernel at every size
         tall = rho >= 160 and T * max(H, I, S) * 2 < (1 << 32)
         if tall:
-            return "tiled8_expert_kernel<GateUp> (fp8, 256x128)" if fp8 else "tiledpp_expert_kernel<GateUp> (bf16, 256x256)"
+            return "tiled8pp_expert_kernel<GateUp> (fp8, 256x128)" if fp8 else "tiledpp_expert_kernel<GateUp> (bf16, 256x256)"
         return f"tiled_expert_kernel<GateUp, 128, 256, {'fp8' if fp8 else 'bf16'}>"
     narrow = min(E, T * K) * (I // 64) < 3 * 256
     if rho <= 12:

@@ -13,8 +13,9 @@
 //
 //   * tiledpp_expert_kernel (bf16, 256-row tiles): 8 waves (two per SIMD) of
 //     128 x 64 with 32x32x16 MFMAs; see its own description below.
-//   * tiled8_expert_kernel (fp8, 256-row tiles): 4 waves of 128 x 64 with
-//     16x16x128 fp8 MFMAs and all operands loaded by LDS DMA; see below.
+//   * tiled8pp_expert_kernel (fp8, 256-row tiles): 8 waves (two per SIMD) of
+//     64 x 64 with 16x16x128 fp8 MFMAs and all operands loaded by LDS DMA; see
+//     below.
 //   * tiled_expert_kernel (128-row tiles, bf16 and fp8): 8 waves of 64 x 64.
 //     Each stage of A (token rows, gathered through the dispatch permutation)
 //     and B (weight rows) is loaded with 16-byte coalesced loads into registers
@@ -301,7 +302,6 @@ __global__ void __launch_bounds__(kTileThreads) tiled_expert_kernel(ExpertArgs a
 // Rows are stored unpadded with their eight 16-byte pieces permuted by
 // (row / 2) mod 8; a fragment read (32 rows x one piece) then touches each
 // 16-byte bank group of the 256-byte bank width once per 16 rows.
-constexpr int kT4Threads = 256;
 constexpr int kT4RowBytes = 128;                        // 64 bf16 per row per stage
 constexpr int kT4Stage = (256 + 256) * kT4RowBytes;     // 64 KiB
 
@@ -323,31 +323,17 @@ __device__ __forceinline__ i32x4_t dma_rsrc(const void* base, uint32_t bytes) {
   return r;
 }
 
-// Eight wave instructions of buffer loads with the LDS flag.  Instruction q: lane l
+// Wave instructions of buffer loads with the LDS flag.  Instruction q: lane l
 // loads 16 bytes at resource offset voff[q] + soff and writes them to LDS at
 // lds + 1024 q + 16 l (M0 holds the LDS address; a write of M0 needs one wait
-// state before the load that uses it).  Completion is
-// counted by vmcnt like any load; the caller waits for it explicitly.  The
-// compiler does not see these accesses: it neither waits for them nor moves LDS
-// accesses across them ("memory" clobber).
+// state before the load that uses it).  Completion is counted by vmcnt like any
+// load; the caller waits for it explicitly.  The compiler does not see these
+// accesses: it neither waits for them nor moves LDS accesses across them
+// ("memory" clobber).
 #define MOE_DMA_LINE(V, S) "s_nop 0\n\tbuffer_load_dwordx4 " V ", %[rs], " S " offen lds\n\t"
 #define MOE_DMA_NEXT "s_add_u32 m0, m0, 0x400\n\t"
 
-__device__ __forceinline__ void dma8_rows(i32x4_t rsrc, const uint32_t (&voff)[8], uint32_t soff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %[lds]\n\t"
-               MOE_DMA_LINE("%[v0]", "%[so]") MOE_DMA_NEXT MOE_DMA_LINE("%[v1]", "%[so]") MOE_DMA_NEXT
-               MOE_DMA_LINE("%[v2]", "%[so]") MOE_DMA_NEXT MOE_DMA_LINE("%[v3]", "%[so]") MOE_DMA_NEXT
-               MOE_DMA_LINE("%[v4]", "%[so]") MOE_DMA_NEXT MOE_DMA_LINE("%[v5]", "%[so]") MOE_DMA_NEXT
-               MOE_DMA_LINE("%[v6]", "%[so]") MOE_DMA_NEXT MOE_DMA_LINE("%[v7]", "%[so]")
-               :
-               : [v0] "v"(voff[0]), [v1] "v"(voff[1]), [v2] "v"(voff[2]), [v3] "v"(voff[3]),
-                 [v4] "v"(voff[4]), [v5] "v"(voff[5]), [v6] "v"(voff[6]), [v7] "v"(voff[7]),
-                 [rs] "s"(rsrc), [so] "s"(__builtin_amdgcn_readfirstlane(soff)),
-                 [lds] "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory", "scc");
-}
-
-// The same, four instructions (voff[0..3]).
+// Four instructions (voff[0..3]).
 __device__ __forceinline__ void dma4_rows(i32x4_t rsrc, const uint32_t (&voff)[4], uint32_t soff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %[lds]\n\t"
                MOE_DMA_LINE("%[v0]", "%[so]") MOE_DMA_NEXT MOE_DMA_LINE("%[v1]", "%[so]") MOE_DMA_NEXT
@@ -359,14 +345,12 @@ __device__ __forceinline__ void dma4_rows(i32x4_t rsrc, const uint32_t (&voff)[4
                : "memory", "scc");
 }
 
-// Four 16-byte instructions over rows `step` bytes apart: instruction q uses
-// voff[q & 1] and soff + q * step, and writes LDS at lds + 1024 q.
-__device__ __forceinline__ void dma4_step(i32x4_t rsrc, const uint32_t (&voff)[2], uint32_t soff, uint32_t step,
+// Two 16-byte instructions over rows `step` bytes apart (voff[0], then voff[1] at
+// soff + step), writing LDS at lds and lds + 1024.
+__device__ __forceinline__ void dma2_step(i32x4_t rsrc, const uint32_t (&voff)[2], uint32_t soff, uint32_t step,
                                           uint32_t lds) {
   uint32_t so;
   asm volatile("s_mov_b32 m0, %[lds]\n\ts_mov_b32 %[so], %[s0]\n\t"
-               MOE_DMA_LINE("%[va]", "%[so]") MOE_DMA_NEXT "s_add_u32 %[so], %[so], %[st]\n\t"
-               MOE_DMA_LINE("%[vb]", "%[so]") MOE_DMA_NEXT "s_add_u32 %[so], %[so], %[st]\n\t"
                MOE_DMA_LINE("%[va]", "%[so]") MOE_DMA_NEXT "s_add_u32 %[so], %[so], %[st]\n\t"
                MOE_DMA_LINE("%[vb]", "%[so]")
                : [so] "=&s"(so)
@@ -615,26 +599,38 @@ __global__ void __launch_bounds__(kPPThreads) tiledpp_expert_kernel(ExpertArgs a
   }
 }
 
-// ---------------------------------------------------------------- 256 x 128, 4 waves (fp8)
+// ---------------------------------------------------------------- 256 x 128 (fp8): shared pieces
 //
-// The fp8 prefill tile: 256 x 128 outputs per workgroup of 4 waves, each wave
-// 128 x 64 as 8 x 4 blocks of 16x16 from 16x16x128 fp8 MFMAs.  A stage is one
-// 128-element scale group (128 bytes per row).  Every product is rescaled by its
-// row and column group scales on the VALU, which cannot reach the accumulation
-// registers; the 128 accumulators therefore live in ordinary registers.
+// The fp8 prefill tile: 256 x 128 outputs per workgroup, from 16x16x128 fp8
+// MFMAs.  A stage is one 128-element scale group (128 bytes per row).  Every
+// product is rescaled by its row and column group scales on the VALU, which
+// cannot reach the accumulation registers; the accumulators therefore live in
+// ordinary registers.
 //
 // Everything a stage needs goes memory -> LDS by DMA: the 256 activation rows,
 // the 128 weight rows and both sets of group scales (48 KiB + 1.5 KiB).  Three
 // stage buffers keep two stages in flight while one is multiplied out; the
-// waits are explicit (every wave issues the same 14 instructions per stage and
-// they complete in order), so nothing else shortens the prefetch distance.
-// Same unpadded, piece-permuted row layout as the bf16 tile.
+// waits are explicit (every wave issues the same instructions per stage and they
+// complete in order), so nothing else shortens the prefetch distance.  Same
+// unpadded, piece-permuted row layout as the bf16 tile.
 constexpr int kF8Bufs = 3;
 constexpr int kF8Stage = (256 + 128) * kT4RowBytes;   // 48 KiB
-constexpr int kF8DmaPerStage = 8 + 4 + 1 + 1;        // per wave: A rows, B rows, A scales, B scales
+
+// ---------------------------------------------------------------- 256 x 128, 8 waves (fp8)
+//
+// 8 waves, two per SIMD: wave w computes rows [64 (w / 2), +64) x the column
+// half w % 2 as 4 x 4 blocks of 16x16 (64 accumulator registers), so that one
+// wave's VALU rescale, fragment reads and waits overlap the other's MFMAs (4
+// waves of 128 x 64, one per SIMD, ran the fp8 layer 9 % slower, measured).
+// Per stage every wave issues the same 7 DMA instructions: 4 of activation rows
+// (32 rows), 2 of weight rows (16 rows of its half), and 1 of scales (waves 0-3:
+// 64 activation rows each; waves 4-7: one weight half each, issued twice with
+// identical values).
+constexpr int kF8PPThreads = 512;
+constexpr int kF8PPDmaPerStage = 4 + 2 + 1;
 
 template <Mode MODE>
-__global__ void __launch_bounds__(kT4Threads) tiled8_expert_kernel(ExpertArgs a) {
+__global__ void __launch_bounds__(kF8PPThreads) tiled8pp_expert_kernel(ExpertArgs a) {
   constexpr int BM = 256, BN = 128;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kF8Bufs * kF8Stage];
   __shared__ __attribute__((aligned(16))) float sscale[kF8Bufs][BM + BN];
@@ -652,16 +648,15 @@ __global__ void __launch_bounds__(kT4Threads) tiled8_expert_kernel(ExpertArgs a)
   const int nt_s = has_shared ? ((MODE == Mode::GateUp) ? a.S / bn_cols : H / bn_cols) : 0;
   const int total = build_tile_prefix(prefix, a.counts, a.offsets, a.E, a.T, has_shared, BM, nt_r, nt_s);
 
-  // DMA lane mapping (16-byte pieces): instruction q of a wave covers 8 rows,
-  // row 8 q' + lane / 8 with LDS piece lane % 8 holding global piece
-  // (lane % 8) ^ ((row / 2) mod 8); the permutation depends on q's parity only.
+  // DMA lane mapping: instruction q covers 8 rows (row 8 q' + lane / 8); LDS piece
+  // lane % 8 holds global piece (lane % 8) ^ ((row / 2) mod 8), which depends on
+  // q's parity only.
   const int drow = lane >> 3;
   uint32_t dpiece[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) dpiece[h] = static_cast<uint32_t>(((lane & 7) ^ ((4 * h + (drow >> 1)) & 7)) * 16);
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(smem));
   const uint32_t sc0 = __builtin_amdgcn_readfirstlane(lds_address(&sscale[0][0]));
-  // Fragment reads: lane row r16 = lane % 16, pieces g and 4 + g (g = lane / 16).
   const int r16 = lane & 15, g = lane >> 4;
   const uint32_t fsw = static_cast<uint32_t>((r16 >> 1) & 7);
   const uint32_t pc0 = (static_cast<uint32_t>(g) ^ fsw) * 16, pc1 = (static_cast<uint32_t>(4 + g) ^ fsw) * 16;
@@ -682,37 +677,29 @@ __global__ void __launch_bounds__(kT4Threads) tiled8_expert_kernel(ExpertArgs a)
     const uint32_t krow = static_cast<uint32_t>(kdim);          // bytes per fp8 row
     const size_t hrow0 = t.shared ? static_cast<size_t>(a.h_shared) : static_cast<size_t>(t.rowbase) * kdim;
 
-    // A rows of this wave: 64 wave + 8 q + lane / 8 (q < 8); its scale row: 64 wave + lane.
-    i32x4_t ra, rsa, rb, rsb;
-    uint32_t aoff[8];
-    uint32_t saoff;
-    {
-      const int ms = min(t.m0 + 64 * wave + lane, t.rows - 1);
-      if constexpr (MODE == Mode::GateUp) {
-        ra = dma_rsrc(a.xq, static_cast<uint32_t>(a.T) * krow);
-        rsa = dma_rsrc(a.xs, static_cast<uint32_t>(a.T) * ng * 4);
-        saoff = static_cast<uint32_t>(row_token(a, t, ms)) * ng * 4;
-      } else {
-        ra = dma_rsrc(a.hq + hrow0, static_cast<uint32_t>(t.rows) * krow);
-        rsa = dma_rsrc(a.hs + hrow0 / kGroup, static_cast<uint32_t>(t.rows) * ng * 4);
-        saoff = static_cast<uint32_t>(ms) * ng * 4;
-      }
+    // A rows of this wave: 32 wave + 8 q + lane / 8 (q < 4).
+    i32x4_t ra, rsa;
+    uint32_t aoff[4];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int m = min(t.m0 + 64 * wave + 8 * q + drow, t.rows - 1);
-        if constexpr (MODE == Mode::GateUp)
-          aoff[q] = static_cast<uint32_t>(row_token(a, t, m)) * krow + dpiece[q & 1];
-        else
-          aoff[q] = static_cast<uint32_t>(m) * krow + dpiece[q & 1];
-      }
+    for (int q = 0; q < 4; ++q) {
+      const int m = min(t.m0 + 32 * wave + 8 * q + drow, t.rows - 1);
+      if constexpr (MODE == Mode::GateUp)
+        aoff[q] = static_cast<uint32_t>(row_token(a, t, m)) * krow + dpiece[q & 1];
+      else
+        aoff[q] = static_cast<uint32_t>(m) * krow + dpiece[q & 1];
     }
-    // B rows: waves w and w + 2 cover the same 64-row half (w & 1) of the tile:
-    // gate / up rows (gate/up) or output rows n0 + 64 (w & 1) ... (down).  Each
-    // wave loads 32 of the half's rows; the scale DMA of the half is issued by
-    // both waves (identical values to the same place).
+    if constexpr (MODE == Mode::GateUp) {
+      ra = dma_rsrc(a.xq, static_cast<uint32_t>(a.T) * krow);
+      rsa = dma_rsrc(a.xs, static_cast<uint32_t>(a.T) * ng * 4);
+    } else {
+      ra = dma_rsrc(a.hq + hrow0, static_cast<uint32_t>(t.rows) * krow);
+      rsa = dma_rsrc(a.hs + hrow0 / kGroup, static_cast<uint32_t>(t.rows) * ng * 4);
+    }
+    // B rows: the 64-row half (wave & 1) of the tile, gate / up rows (gate/up) or
+    // output rows n0 + 64 (wave & 1) ... (down); wave loads rows 16 (wave >> 1) + ...
     const int half = wave & 1;
+    i32x4_t rb, rsb;
     uint32_t boff[2];
-    uint32_t sboff;
     {
       const uint8_t* wb;
       const float* sbp;
@@ -733,7 +720,22 @@ __global__ void __launch_bounds__(kT4Threads) tiled8_expert_kernel(ExpertArgs a)
       rsb = dma_rsrc(sbp, 64 * ng * 4);
 #pragma unroll
       for (int h = 0; h < 2; ++h) boff[h] = static_cast<uint32_t>(drow) * krow + dpiece[h];
-      sboff = static_cast<uint32_t>(lane) * ng * 4;
+    }
+    // The scale vector this wave stages: waves 0-3 the activation rows
+    // [64 wave, +64); waves 4-7 the weight half (wave & 1).
+    const bool a_scales = wave < 4;
+    i32x4_t rss;
+    uint32_t ssoff, ssdst;
+    if (a_scales) {
+      const int ms = min(t.m0 + 64 * wave + lane, t.rows - 1);
+      rss = rsa;
+      if constexpr (MODE == Mode::GateUp) ssoff = static_cast<uint32_t>(row_token(a, t, ms)) * ng * 4;
+      else ssoff = static_cast<uint32_t>(ms) * ng * 4;
+      ssdst = 64 * wave * 4;
+    } else {
+      rss = rsb;
+      ssoff = static_cast<uint32_t>(lane) * ng * 4;
+      ssdst = (BM + 64 * half) * 4;
     }
 
     // Stage ks -> buffer ks % 3: A rows at [0, 32 KiB), B rows after; scales in sscale.
@@ -741,16 +743,13 @@ __global__ void __launch_bounds__(kT4Threads) tiled8_expert_kernel(ExpertArgs a)
       const int b = ks % kF8Bufs;
       const uint32_t buf = lds0 + static_cast<uint32_t>(b) * kF8Stage;
       const uint32_t kb = static_cast<uint32_t>(ks) * kT4RowBytes;
-      dma8_rows(ra, aoff, kb, buf + 8 * wave * 1024);
-      dma4_step(rb, boff, kb + 8 * 4 * (wave >> 1) * krow, 8 * krow,
-                buf + BM * kT4RowBytes + (64 * half + 32 * (wave >> 1)) * kT4RowBytes);
+      dma4_rows(ra, aoff, kb, buf + 4 * wave * 1024);
+      dma2_step(rb, boff, kb + 16 * (wave >> 1) * krow, 8 * krow,
+                buf + BM * kT4RowBytes + (64 * half + 16 * (wave >> 1)) * kT4RowBytes);
       const uint32_t sbuf = sc0 + static_cast<uint32_t>(b) * (BM + BN) * 4;
-      dma1_dword(rsa, saoff, static_cast<uint32_t>(ks) * 4, sbuf + 64 * wave * 4);
-      dma1_dword(rsb, sboff, static_cast<uint32_t>(ks) * 4, sbuf + (BM + 64 * half) * 4);
+      dma1_dword(rss, ssoff, static_cast<uint32_t>(ks) * 4, sbuf + ssdst);
     };
 
-    // LDS row of B feeding 16-column block j.  Gate/up: blocks 0, 1 are gate
-    // rows, 2, 3 the up rows of the same columns.
     auto brow = [&](int j) -> int {
       if constexpr (MODE == Mode::GateUp) return ((j < 2) ? 0 : BN / 2) + wn * 32 + 16 * (j & 1) + r16;
       else return wn * 64 + 16 * j + r16;
@@ -760,17 +759,18 @@ __global__ void __launch_bounds__(kT4Threads) tiled8_expert_kernel(ExpertArgs a)
       const uint4 hi = *reinterpret_cast<const uint4*>(row + pc1);
       return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     };
-    f32x4 acc[8][4];
+    constexpr int NI = 4;
+    f32x4 acc[NI][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto compute = [&](int ks) {
       const int b = ks % kF8Bufs;
       const uint8_t* base = smem + b * kF8Stage;
-      const uint8_t* As = base + (wm * 128 + r16) * kT4RowBytes;
+      const uint8_t* As = base + (wm * 64 + r16) * kT4RowBytes;
       const uint8_t* Bs = base + BM * kT4RowBytes;
-      const float* sA = &sscale[b][wm * 128 + 4 * g];
+      const float* sA = &sscale[b][wm * 64 + 4 * g];
       const float* sB = &sscale[b][BM];
       const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
       i32x8 bf[4];
@@ -780,8 +780,8 @@ __global__ void __launch_bounds__(kT4Threads) tiled8_expert_kernel(ExpertArgs a)
         bf[j] = frag(Bs + brow(j) * kT4RowBytes);
         sb[j] = sB[brow(j)];
       }
-      // Products are formed one row block ahead of their rescale, so the matrix
-      // pipe always has independent work while the VALU waits for results.
+      // Products one row block ahead of their rescale (independent MFMA work
+      // while the VALU waits for results).
       f32x4 pc[4], pn[4];
       {
         const i32x8 af = frag(As);
@@ -789,8 +789,8 @@ __global__ void __launch_bounds__(kT4Threads) tiled8_expert_kernel(ExpertArgs a)
         for (int j = 0; j < 4; ++j) pc[j] = mfma_fp8_16x16x128(af, bf[j], zero);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (i + 1 < 8) {
+      for (int i = 0; i < NI; ++i) {
+        if (i + 1 < NI) {
           const i32x8 af = frag(As + (i + 1) * 16 * kT4RowBytes);
 #pragma unroll
           for (int j = 0; j < 4; ++j) pn[j] = mfma_fp8_16x16x128(af, bf[j], zero);
@@ -805,15 +805,14 @@ __global__ void __launch_bounds__(kT4Threads) tiled8_expert_kernel(ExpertArgs a)
       }
     };
 
-    // Stage ks: wait for this wave's part of it (only stage ks + 1's 14
-    // instructions may still be pending); barrier (every wave's part has landed,
-    // and stage ks - 1's buffer is no longer read); start stage ks + 2 into that
-    // buffer; multiply stage ks.
+    // Stage ks: wait for this wave's part of it (only stage ks + 1's 7
+    // instructions may still be pending); barrier; start stage ks + 2 into the
+    // buffer stage ks - 1 used; multiply stage ks.
     __syncthreads();                   // the previous tile is done with every buffer
     issue(0);
     if (nk > 1) issue(1);
     for (int ks = 0; ks < nk; ++ks) {
-      if (ks + 1 < nk) wait_vm<kF8DmaPerStage>();
+      if (ks + 1 < nk) wait_vm<kF8PPDmaPerStage>();
       else wait_vm<0>();
       __syncthreads();
       if (ks + 2 < nk) issue(ks + 2);
@@ -827,10 +826,10 @@ __global__ void __launch_bounds__(kT4Threads) tiled8_expert_kernel(ExpertArgs a)
                      (t.shared ? static_cast<size_t>(a.h_shared) : static_cast<size_t>(t.rowbase) * width);
       const int col0 = n0 + wn * 32 + r16;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int m = t.m0 + wm * 128 + 16 * i + 4 * g + e;
+          const int m = t.m0 + wm * 64 + 16 * i + 4 * g + e;
           if (m < t.rows) {
             float* hr = hbase + static_cast<size_t>(m) * width + col0;
 #pragma unroll
@@ -840,10 +839,10 @@ __global__ void __launch_bounds__(kT4Threads) tiled8_expert_kernel(ExpertArgs a)
     } else {
       const int col0 = n0 + wn * 64 + r16;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int m = t.m0 + wm * 128 + 16 * i + 4 * g + e;
+          const int m = t.m0 + wm * 64 + 16 * i + 4 * g + e;
           if (m < t.rows) {
             const DownDst dst = down_row(a, t, m);
             float* yr = dst.row + col0;
@@ -879,7 +878,7 @@ hipError_t launch_gate_up_tiled(const ExpertArgs& a, bool fp8, bool tall, hipStr
   const int hcols = (tall && fp8) ? 64 : 128;   // h columns per tile
   const int grid = tiled_grid(a, BM, a.I / hcols, a.S / hcols);
   if (tall) {
-    if (fp8) tiled8_expert_kernel<Mode::GateUp><<<grid, kT4Threads, 0, stream>>>(a);
+    if (fp8) tiled8pp_expert_kernel<Mode::GateUp><<<grid, kF8PPThreads, 0, stream>>>(a);
     else tiledpp_expert_kernel<Mode::GateUp><<<grid, kPPThreads, 0, stream>>>(a);
   } else {
     if (fp8) tiled_expert_kernel<Mode::GateUp, 128, 256, true><<<grid, kTileThreads, 0, stream>>>(a);
@@ -894,7 +893,7 @@ hipError_t launch_down_tiled(const ExpertArgs& a, bool fp8, bool tall, hipStream
   const int ycols = (tall && fp8) ? 128 : 256;  // output columns per tile
   const int grid = tiled_grid(a, BM, a.H / ycols, a.H / ycols);
   if (tall) {
-    if (fp8) tiled8_expert_kernel<Mode::Down><<<grid, kT4Threads, 0, stream>>>(a);
+    if (fp8) tiled8pp_expert_kernel<Mode::Down><<<grid, kF8PPThreads, 0, stream>>>(a);
     else tiledpp_expert_kernel<Mode::Down><<<grid, kPPThreads, 0, stream>>>(a);
   } else {
     if (fp8) tiled_expert_kernel<Mode::Down, 128, 256, true><<<grid, kTileThreads, 0, stream>>>(a);

@@ -169,3 +169,23 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(moe, "_lib", None)
     with pytest.raises(ImportError):
         moe.lib()
+
+
+@pytest.mark.parametrize("kw", [
+    {},
+    dict(weight_dtype="fp8_e4m3_g128"),
+    dict(weight_dtype="mxfp4"),
+    dict(n_routed_experts=256, moe_intermediate_size=2048, num_experts_per_tok=8, hidden_size=7168,
+         shared_expert_intermediate_size=0),
+    dict(weight_dtype="f32", act_dtype="f32", hidden_size=256, n_routed_experts=8, moe_intermediate_size=512,
+         shared_expert_intermediate_size=0),
+])
+def test_workspace_size_is_monotone_in_tokens(kw):
+    # A workspace sized for max_tokens must serve every smaller call.
+    cfg = _cfg(**kw)
+    sizes = []
+    for T in (1, 2, 7, 56, 224, 255, 256, 257, 1000, 1024, 1025, 4096, 8192):
+        st, n = _ws(cfg, T)
+        assert st == OK
+        sizes.append(n)
+    assert all(b >= a for a, b in zip(sizes, sizes[1:])), sizes

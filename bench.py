@@ -129,6 +129,8 @@ def gate_up_kernel(shape, T: int) -> str:
             return "tiled8pp_expert_kernel<GateUp> (fp8, 256x128)" if fp8 else "tiledpp_expert_kernel<GateUp> (bf16, 256x256)"
         return f"tiled_expert_kernel<GateUp, 128, 256, {'fp8' if fp8 else 'bf16'}>"
     narrow = min(E, T * K) * (I // 64) < 3 * 256
+    if dt == "mxfp4" and rho >= 48:
+        return "stream_expert_kernel<GateUp, 128, 128, 2, mxfp4>"
     if rho <= 12:
         cfg = "16, 128, 1"
     elif rho <= 24:

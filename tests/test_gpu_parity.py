@@ -98,6 +98,16 @@ def test_fp8_small_ragged(T):
     _run(_SMALL_FP8, T, W.base_seed(0, T) + 11)
 
 
+# MXFP4 at prefill sizes (128 x 128 streaming tiles): few experts with many rows
+# (partial row tiles), and the large layer at T = 8192 on sampled tokens.
+@pytest.mark.parametrize("shape,T,seed,alpha,tokens", [
+    (W.LayerShape("mx_tall", 512, 4, 512, 2, 512, W.DT_MXFP4, W.DT_BF16), 700, 731, None, None),
+    (W.LARGE_MX4, 8192, W.base_seed(3, 8192), 1.5, 16),
+])
+def test_mxfp4_prefill(shape, T, seed, alpha, tokens):
+    _run(shape, T, seed, alpha, tokens=None if tokens is None else Hn.sample_tokens(T, tokens))
+
+
 # A small MXFP4 layer (contraction of 2 stages) with ragged row tiles: one token,
 # 13 tokens and 64 tokens (~16 rows per expert).
 _SMALL_MX4 = W.LayerShape("small_mxfp4", 512, 8, 256, 2, 256, W.DT_MXFP4, W.DT_BF16)

@@ -123,14 +123,11 @@ def gate_up_kernel(shape, T: int) -> str:
     H, E, I, K, S = (shape.hidden_size, shape.n_routed_experts, shape.moe_intermediate_size,
                      shape.num_experts_per_tok, shape.shared_expert_intermediate_size)
     rho = T * K // E
-    if rho >= 48 and dt != "mxfp4":   # MXFP4 runs on the streaming kernel at every size
-        tall = rho >= 160 and T * max(H, I, S) * 2 < (1 << 32)
-        if tall:
-            return "tiled8pp_expert_kernel<GateUp> (fp8, 256x128)" if fp8 else "tiledpp_expert_kernel<GateUp> (bf16, 256x256)"
-        return f"tiled_expert_kernel<GateUp, 128, 256, {'fp8' if fp8 else 'bf16'}>"
+    if rho >= 160 and dt != "mxfp4":   # MXFP4 runs on the streaming kernel at every size
+        return "tiled8pp_expert_kernel<GateUp> (fp8, 256x128)" if fp8 else "tiledpp_expert_kernel<GateUp> (bf16, 256x256)"
     narrow = min(E, T * K) * (I // 64) < 3 * 256
-    if dt == "mxfp4" and rho >= 48:
-        return "stream_expert_kernel<GateUp, 128, 128, 2, mxfp4>"
+    if rho >= 48:
+        return f"stream_expert_kernel<GateUp, 128, 128, 2, {dt}>"
     if rho <= 12:
         cfg = "16, 128, 1"
     elif rho <= 24:

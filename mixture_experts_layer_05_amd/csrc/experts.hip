@@ -251,10 +251,11 @@ int tile_bound(const ExpertArgs& a, int BM, int nt_routed, int nt_shared) {
 
 // Rows per expert decide the kernel: the average expert sees rho = T*K/E rows
 // (the same load measure as the small-M / large-M family choice of
-// [DeepGEMM fork PR #5, "Dynamic family selection"]).  Below kTiledRows the
-// weight-streaming kernels (stream_gemm.hip); from there the LDS-tiled MFMA
-// kernels (tile_gemm.hip), 128-row tiles, and 256-row tiles from kTallRows.
-constexpr int64_t kTiledRows = 48, kTallRows = 160;
+// [DeepGEMM fork PR #5, "Dynamic family selection"]).  Below kTallRows the
+// weight-streaming kernels (stream_gemm.hip, which pick their tile height from
+// rho); from there the 256-row LDS-tiled MFMA kernels (tile_gemm.hip), for bf16
+// and fp8 weights.
+constexpr int64_t kTallRows = 160;
 
 int64_t rows_per_expert(const ExpertArgs& a) { return static_cast<int64_t>(a.T) * a.K / a.E; }
 
@@ -268,9 +269,8 @@ hipError_t launch_gate_up(const ExpertArgs& a, int weight_dtype, hipStream_t str
   }
   const int64_t rho = rows_per_expert(a);
   // MXFP4 weights run on the streaming kernel at every size (no LDS-tiled form).
-  if (weight_dtype == kDtypeMxfp4) return launch_gate_up_stream(a, kDtypeMxfp4, rho, stream);
-  const bool fp8 = weight_dtype == kDtypeFp8;
-  if (rho >= kTiledRows) return launch_gate_up_tiled(a, fp8, rho >= kTallRows, stream);
+  if (weight_dtype != kDtypeMxfp4 && rho >= kTallRows && tall_tiles_fit(a))
+    return launch_gate_up_tall(a, weight_dtype == kDtypeFp8, stream);
   return launch_gate_up_stream(a, weight_dtype, rho, stream);
 }
 
@@ -281,9 +281,8 @@ hipError_t launch_down(const ExpertArgs& a, int weight_dtype, hipStream_t stream
     return hipGetLastError();
   }
   const int64_t rho = rows_per_expert(a);
-  if (weight_dtype == kDtypeMxfp4) return launch_down_stream(a, kDtypeMxfp4, rho, stream);
-  const bool fp8 = weight_dtype == kDtypeFp8;
-  if (rho >= kTiledRows && a.H % 256 == 0) return launch_down_tiled(a, fp8, rho >= kTallRows, stream);
+  if (weight_dtype != kDtypeMxfp4 && rho >= kTallRows && a.H % 256 == 0 && tall_tiles_fit(a))
+    return launch_down_tall(a, weight_dtype == kDtypeFp8, stream);
   return launch_down_stream(a, weight_dtype, rho, stream);
 }
 

@@ -72,8 +72,11 @@ __global__ void dispatch_scatter_kernel(const int32_t*, int, int, int, const int
 // experts.hip: host-side launchers (they pick tile shapes and grid sizes).
 hipError_t launch_gate_up(const ExpertArgs& a, int weight_dtype, hipStream_t stream);
 hipError_t launch_down(const ExpertArgs& a, int weight_dtype, hipStream_t stream);
-hipError_t launch_gate_up_tiled(const ExpertArgs& a, bool fp8, bool tall, hipStream_t stream);
-hipError_t launch_down_tiled(const ExpertArgs& a, bool fp8, bool tall, hipStream_t stream);
+// 256-row LDS-tiled kernels (tile_gemm.hip); tall_tiles_fit: their 32-bit
+// operand offsets cover the call's activation matrices.
+bool tall_tiles_fit(const ExpertArgs& a);
+hipError_t launch_gate_up_tall(const ExpertArgs& a, bool fp8, hipStream_t stream);
+hipError_t launch_down_tall(const ExpertArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_gate_up_stream(const ExpertArgs& a, int weight_dtype, int64_t rho, hipStream_t stream);
 hipError_t launch_down_stream(const ExpertArgs& a, int weight_dtype, int64_t rho, hipStream_t stream);
 hipError_t launch_combine(const ExpertArgs& a, hipStream_t stream);

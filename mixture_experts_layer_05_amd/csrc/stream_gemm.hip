@@ -1,4 +1,5 @@
-// Weight-streaming grouped expert GEMMs for decode-sized M (few rows per expert).
+// Weight-streaming grouped expert GEMMs: decode-sized M (few rows per expert) and,
+// with 128-row tiles, the middle range up to the 256-row LDS-tiled kernels.
 //
 // At decode sizes every routed expert sees a handful of tokens, so the layer is
 // bound by reading each touched expert's weights once from HBM [SpecForge PR
@@ -741,10 +742,11 @@ hipError_t launch_stream(const ExpertArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-constexpr int64_t kMxTallRows = 48;   // rows per expert from which MXFP4 takes 128-row tiles
+constexpr int64_t kStreamTallRows = 48;   // rows per expert from which the tiles are 128 rows tall
 
 // Tile shape from the average rows per expert rho = T*K/E: 16-row tiles up to 12
-// rows, 32 up to 24, 64 above.  Gate/up tiles of 32 or 64 rows use 64 weight rows
+// rows, 32 up to 24, 64 up to 48, then 128 x 128 (below the 256-row LDS-tiled
+// kernels' range, and for MXFP4 at every size).  Gate/up tiles of 32 or 64 rows use 64 weight rows
 // (the compute waves split 2 x 2) when 128-row tiles would leave fewer than ~3
 // tiles per CU: its tiles all have H/128 stages, so the count per workgroup sets
 // the balance.  Down tiles keep 128 weight rows: they are short (I/128 stages),
@@ -756,13 +758,13 @@ hipError_t launch_stream_rho(const ExpertArgs& a, int64_t rho, hipStream_t strea
   const int64_t n_out = (MODE == SMode::GateUp) ? a.I : a.H;
   const int64_t tiles128 = touched * (MODE == SMode::GateUp ? n_out / 64 : n_out / 128);
   const bool narrow = MODE == SMode::GateUp && tiles128 < 3 * 256;
-  // MXFP4 at prefill sizes (there is no LDS-tiled MXFP4 kernel): 128 x 128 tiles
-  // in 256-element stages give 33 % more flops per loaded byte than 64 x 128 in
-  // 512-element stages (the 512-element form of the taller tile does not fit
-  // LDS); measured 16 % faster on the large layer at T = 8192.
-  if constexpr (FMT == kDtypeMxfp4 || FMT == kMxWide) {
-    if (rho >= kMxTallRows) return launch_stream<MODE, 128, 128, 2, kDtypeMxfp4>(a, stream);
-  }
+  // From kStreamTallRows rows per expert: 128 x 128 tiles (MXFP4 in 256-element
+  // stages: the 512-element form of this tile does not fit LDS).  For MXFP4 they
+  // give 33 % more flops per loaded byte than 64 x 128 in 512-element stages and
+  // ran the large layer 16 % faster at T = 8192; for bf16 and fp8 they ran 3-7 %
+  // faster than 128-row LDS-tiled kernels between 48 and 160 rows per expert.
+  if (rho >= kStreamTallRows)
+    return launch_stream<MODE, 128, 128, 2, (FMT == kMxWide ? kDtypeMxfp4 : FMT)>(a, stream);
   if (rho <= 12) return launch_stream<MODE, 16, 128, 1, FMT>(a, stream);
   if (rho <= 24) return narrow ? launch_stream<MODE, 32, 64, 2, FMT>(a, stream)
                                : launch_stream<MODE, 32, 128, 1, FMT>(a, stream);

@@ -249,13 +249,17 @@ int tile_bound(const ExpertArgs& a, int BM, int nt_routed, int nt_shared) {
   return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(b, kMaxGrid)));
 }
 
-// Rows per expert decide the kernel: the average expert sees rho = T*K/E rows
-// (the same load measure as the small-M / large-M family choice of
-// [DeepGEMM fork PR #5, "Dynamic family selection"]).  Below kTallRows the
-// weight-streaming kernels (stream_gemm.hip, which pick their tile height from
-// rho); from there the 256-row LDS-tiled MFMA kernels (tile_gemm.hip), for bf16
-// and fp8 weights.
-constexpr int64_t kTallRows = 160;
+// Rows per expert decide the kernels.  The average expert sees rho = T*K/E rows
+// (the load measure of the small-M / large-M family choice of [DeepGEMM fork
+// PR #5, "Dynamic family selection"]).  Below kMixRows, the weight-streaming
+// kernels alone (stream_gemm.hip, which pick their tile height from rho).  From
+// there, with bf16 or fp8 weights, the call's groups are split by their realised
+// row counts, read on the device: groups of at least kTallGroupRows rows go to
+// the 256-row LDS-tiled MFMA kernels (tile_gemm.hip, where such a tile is at
+// least half full), the others to the streaming kernel's 128-row tiles.  Two
+// launches, disjoint groups.
+constexpr int64_t kMixRows = 48;
+constexpr int kTallGroupRows = 128;
 
 int64_t rows_per_expert(const ExpertArgs& a) { return static_cast<int64_t>(a.T) * a.K / a.E; }
 
@@ -269,8 +273,14 @@ hipError_t launch_gate_up(const ExpertArgs& a, int weight_dtype, hipStream_t str
   }
   const int64_t rho = rows_per_expert(a);
   // MXFP4 weights run on the streaming kernel at every size (no LDS-tiled form).
-  if (weight_dtype != kDtypeMxfp4 && rho >= kTallRows && tall_tiles_fit(a))
-    return launch_gate_up_tall(a, weight_dtype == kDtypeFp8, stream);
+  if (weight_dtype != kDtypeMxfp4 && rho >= kMixRows && tall_tiles_fit(a)) {
+    ExpertArgs tall = a, rest = a;
+    tall.rows_lo = kTallGroupRows;
+    rest.rows_hi = kTallGroupRows;
+    const hipError_t e = launch_gate_up_tall(tall, weight_dtype == kDtypeFp8, stream);
+    if (e != hipSuccess) return e;
+    return launch_gate_up_stream(rest, weight_dtype, rho, stream);
+  }
   return launch_gate_up_stream(a, weight_dtype, rho, stream);
 }
 
@@ -281,8 +291,14 @@ hipError_t launch_down(const ExpertArgs& a, int weight_dtype, hipStream_t stream
     return hipGetLastError();
   }
   const int64_t rho = rows_per_expert(a);
-  if (weight_dtype != kDtypeMxfp4 && rho >= kTallRows && a.H % 256 == 0 && tall_tiles_fit(a))
-    return launch_down_tall(a, weight_dtype == kDtypeFp8, stream);
+  if (weight_dtype != kDtypeMxfp4 && rho >= kMixRows && a.H % 256 == 0 && tall_tiles_fit(a)) {
+    ExpertArgs tall = a, rest = a;
+    tall.rows_lo = kTallGroupRows;
+    rest.rows_hi = kTallGroupRows;
+    const hipError_t e = launch_down_tall(tall, weight_dtype == kDtypeFp8, stream);
+    if (e != hipSuccess) return e;
+    return launch_down_stream(rest, weight_dtype, rho, stream);
+  }
   return launch_down_stream(a, weight_dtype, rho, stream);
 }
 

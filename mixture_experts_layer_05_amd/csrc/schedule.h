@@ -16,12 +16,16 @@ constexpr int kDtypeF32 = 0, kDtypeBf16 = 1, kDtypeFp8 = 2, kDtypeMxfp4 = 3;
 // The schedule lives in LDS: prefix[0..G] of per-group tile counts, then each
 // group's row count and first dispatch row, so that finding a tile's group reads no
 // global memory.  prefix[g+1] - prefix[g] = ceil(rows_g / BM) * ntiles_g for g in
-// [0, G), where group E (if has_shared) is the shared expert with T rows.
+// [0, G), where group E (if has_shared) is the shared expert with T rows.  A group
+// whose row count lies outside [rows_lo, rows_hi) gets no tiles: launches that
+// split the groups between two kernels by their realised row counts each take a
+// window.
 constexpr int kSchedStride = kMaxExperts + 2;
 constexpr int kSchedInts = 3 * kSchedStride;
 
 __device__ int build_tile_prefix(int* sched, const int32_t* counts, const int32_t* offsets, int E, int T,
-                                 bool has_shared, int BM, int nt_routed, int nt_shared) {
+                                 bool has_shared, int BM, int nt_routed, int nt_shared, int rows_lo = 0,
+                                 int rows_hi = 0x7fffffff) {
   const int G = E + (has_shared ? 1 : 0);
   int* prefix = sched;
   int* rows_of = sched + kSchedStride;
@@ -33,7 +37,8 @@ __device__ int build_tile_prefix(int* sched, const int32_t* counts, const int32_
       const int g = base + lane;
       int v = 0;
       if (g < G) {
-        const int rows = (g < E) ? counts[g] : T;
+        int rows = (g < E) ? counts[g] : T;
+        if (rows < rows_lo || rows >= rows_hi) rows = 0;
         rows_of[g] = rows;
         base_of[g] = (g < E) ? offsets[g] : 0;
         v = static_cast<int>(ceil_div(rows, BM)) * ((g < E) ? nt_routed : nt_shared);

@@ -232,6 +232,20 @@ def test_tiled_fp8_kernels_with_partial_tiles(T):
     _run(TILED.with_(name="tiled_rows_fp8", weight_dtype=W.DT_FP8), T, 30 + T)
 
 
+# Groups on both sides of the 128-row split between the 256-row LDS-tiled kernel
+# and the streaming kernel's 128-row tiles (Zipf-skewed counts), checked on
+# every token; the shared expert (600 rows) runs on the tiled kernel.
+MIXED = W.LayerShape("mixed_groups", 512, 8, 256, 2, 256, W.DT_BF16, W.DT_BF16)
+
+
+@pytest.mark.parametrize("dt", [W.DT_BF16, W.DT_FP8])
+def test_groups_split_between_kernels_by_rows(dt):
+    shape = MIXED.with_(name=f"mixed_groups_{dt}", weight_dtype=dt)
+    case, gpu, ora, _ = _run(shape, 600, 61, 1.5)
+    counts = gpu["counts"]
+    assert (counts >= 128).any() and ((counts > 0) & (counts < 128)).any(), counts
+
+
 # 256-row tiles with the shortest contractions the kernels accept (128 elements)
 # and a single n-tile per group.
 SHORT_K = W.LayerShape("tiled_short_k", 256, 2, 128, 1, 128, W.DT_BF16, W.DT_BF16)

@@ -123,8 +123,9 @@ def gate_up_kernel(shape, T: int) -> str:
     H, E, I, K, S = (shape.hidden_size, shape.n_routed_experts, shape.moe_intermediate_size,
                      shape.num_experts_per_tok, shape.shared_expert_intermediate_size)
     rho = T * K // E
-    if rho >= 160 and dt != "mxfp4":   # MXFP4 runs on the streaming kernel at every size
-        return "tiled8pp_expert_kernel<GateUp> (fp8, 256x128)" if fp8 else "tiledpp_expert_kernel<GateUp> (bf16, 256x256)"
+    if rho >= 48 and dt != "mxfp4":   # MXFP4 runs on the streaming kernel at every size
+        tall = "tiled8pp_expert_kernel<GateUp> (fp8, 256x128)" if fp8 else "tiledpp_expert_kernel<GateUp> (bf16, 256x256)"
+        return f"{tall} for groups of >= 128 rows + stream_expert_kernel<GateUp, 128, 128, 2, {dt}> for the rest"
     narrow = min(E, T * K) * (I // 64) < 3 * 256
     if rho >= 48:
         return f"stream_expert_kernel<GateUp, 128, 128, 2, {dt}>"
@@ -138,12 +139,9 @@ def gate_up_kernel(shape, T: int) -> str:
 
 
 def kernel_source_file(kernel_label: str) -> str:
-    """HIP source file that holds the kernel named by a roofline label."""
-    if kernel_label.startswith("stream"):
-        return "stream_gemm.hip"
-    if kernel_label.startswith("tiled"):
-        return "tile_gemm.hip"
-    return "experts.hip"
+    """HIP source files ('+'-joined) that hold the kernels named by a roofline label."""
+    files = [f for key, f in (("tiled", "tile_gemm.hip"), ("stream", "stream_gemm.hip")) if key in kernel_label]
+    return "+".join(files) if files else "experts.hip"
 
 
 def library_source_hash(kernel_file: str = None) -> str:
@@ -155,7 +153,7 @@ def library_source_hash(kernel_file: str = None) -> str:
     csrc = os.path.join(ROOT, "mixture_experts_layer_05_amd", "csrc")
     files = sorted(glob.glob(os.path.join(csrc, "*")))
     if kernel_file is not None:
-        keep = {kernel_file, "experts.hip", "api.hip"}
+        keep = set(kernel_file.split("+")) | {"experts.hip", "api.hip"}
         files = [f for f in files if f.endswith(".h") or os.path.basename(f) in keep]
     h = hashlib.sha256()
     for f in files:

@@ -192,8 +192,7 @@ ExpertArgs expert_args(const moe_config& c, int32_t T, const void* x, const floa
     a.he8 = at<uint8_t>(ws, L.hs);
   }
   a.o = at<float>(ws, L.o);
-  a.rows_lo = 0;
-  a.rows_hi = 0x7fffffff;
+  a.split = 0;
   a.y = y;
   a.T = T;
   a.H = c.hidden_size;

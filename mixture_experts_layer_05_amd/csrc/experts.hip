@@ -253,13 +253,12 @@ int tile_bound(const ExpertArgs& a, int BM, int nt_routed, int nt_shared) {
 // (the load measure of the small-M / large-M family choice of [DeepGEMM fork
 // PR #5, "Dynamic family selection"]).  Below kMixRows, the weight-streaming
 // kernels alone (stream_gemm.hip, which pick their tile height from rho).  From
-// there, with bf16 or fp8 weights, the call's groups are split by their realised
-// row counts, read on the device: groups of at least kTallGroupRows rows go to
-// the 256-row LDS-tiled MFMA kernels (tile_gemm.hip, where such a tile is at
-// least half full), the others to the streaming kernel's 128-row tiles.  Two
-// launches, disjoint groups.
+// there, with bf16 or fp8 weights, the call's rows are divided by the realised
+// counts, read on the device (schedule.h, build_tile_prefix): rows that fill a
+// 256-row tile at least half go to the LDS-tiled MFMA kernels (tile_gemm.hip),
+// short groups and the short tails of long ones to the streaming kernel's
+// 128-row tiles.  Two launches, disjoint rows.
 constexpr int64_t kMixRows = 48;
-constexpr int kTallGroupRows = 128;
 
 int64_t rows_per_expert(const ExpertArgs& a) { return static_cast<int64_t>(a.T) * a.K / a.E; }
 
@@ -275,8 +274,8 @@ hipError_t launch_gate_up(const ExpertArgs& a, int weight_dtype, hipStream_t str
   // MXFP4 weights run on the streaming kernel at every size (no LDS-tiled form).
   if (weight_dtype != kDtypeMxfp4 && rho >= kMixRows && tall_tiles_fit(a)) {
     ExpertArgs tall = a, rest = a;
-    tall.rows_lo = kTallGroupRows;
-    rest.rows_hi = kTallGroupRows;
+    tall.split = 1;
+    rest.split = 2;
     const hipError_t e = launch_gate_up_tall(tall, weight_dtype == kDtypeFp8, stream);
     if (e != hipSuccess) return e;
     return launch_gate_up_stream(rest, weight_dtype, rho, stream);
@@ -293,8 +292,8 @@ hipError_t launch_down(const ExpertArgs& a, int weight_dtype, hipStream_t stream
   const int64_t rho = rows_per_expert(a);
   if (weight_dtype != kDtypeMxfp4 && rho >= kMixRows && a.H % 256 == 0 && tall_tiles_fit(a)) {
     ExpertArgs tall = a, rest = a;
-    tall.rows_lo = kTallGroupRows;
-    rest.rows_hi = kTallGroupRows;
+    tall.split = 1;
+    rest.split = 2;
     const hipError_t e = launch_down_tall(tall, weight_dtype == kDtypeFp8, stream);
     if (e != hipSuccess) return e;
     return launch_down_stream(rest, weight_dtype, rho, stream);

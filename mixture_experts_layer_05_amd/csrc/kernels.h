@@ -42,9 +42,9 @@ struct ExpertArgs {
   const uint8_t* he8;
   float* o;                      // [T*K, H] unweighted routed outputs, row = slot t*K+k
   float* y;                      // [T, H]
-  // Row-count window of the groups this launch serves (all: [0, INT_MAX)); the
-  // expert launchers split a call's groups between two kernels with it.
-  int rows_lo, rows_hi;
+  // Which of a call's rows this launch serves when the expert launchers divide
+  // them between two kernels by the realised counts (0: all; see schedule.h).
+  int split;
   void* y_act;                   // [T, H] act dtype or null: the cast of y
   int act_bf16;                  // y_act is bf16 (else float32)
   // Router logits (router mode of the streaming kernel): z[t, c] = x_t . col_c with

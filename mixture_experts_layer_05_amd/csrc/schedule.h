@@ -16,16 +16,23 @@ constexpr int kDtypeF32 = 0, kDtypeBf16 = 1, kDtypeFp8 = 2, kDtypeMxfp4 = 3;
 // The schedule lives in LDS: prefix[0..G] of per-group tile counts, then each
 // group's row count and first dispatch row, so that finding a tile's group reads no
 // global memory.  prefix[g+1] - prefix[g] = ceil(rows_g / BM) * ntiles_g for g in
-// [0, G), where group E (if has_shared) is the shared expert with T rows.  A group
-// whose row count lies outside [rows_lo, rows_hi) gets no tiles: launches that
-// split the groups between two kernels by their realised row counts each take a
-// window.
+// [0, G), where group E (if has_shared) is the shared expert with T rows.
+//
+// split divides a call's rows between two kernels by the realised counts (0: all
+// rows here).  A group of r rows is "tall" when r >= kSplitRows; its first
+// r_t = r rows, or r - r % kTallTile when that tail is shorter than kSplitRows,
+// go to the 256-row kernel (split 1; every one of its tiles is then at least half
+// full), and the other rows (short groups whole, tall groups' short tails from row
+// r_t on) to the streaming kernel (split 2).  The shared expert is never cut: its
+// rows are token indices.
 constexpr int kSchedStride = kMaxExperts + 2;
 constexpr int kSchedInts = 3 * kSchedStride;
 
+constexpr int kSplitRows = 128;
+constexpr int kTallTile = 256;
+
 __device__ int build_tile_prefix(int* sched, const int32_t* counts, const int32_t* offsets, int E, int T,
-                                 bool has_shared, int BM, int nt_routed, int nt_shared, int rows_lo = 0,
-                                 int rows_hi = 0x7fffffff) {
+                                 bool has_shared, int BM, int nt_routed, int nt_shared, int split = 0) {
   const int G = E + (has_shared ? 1 : 0);
   int* prefix = sched;
   int* rows_of = sched + kSchedStride;
@@ -37,10 +44,16 @@ __device__ int build_tile_prefix(int* sched, const int32_t* counts, const int32_
       const int g = base + lane;
       int v = 0;
       if (g < G) {
-        int rows = (g < E) ? counts[g] : T;
-        if (rows < rows_lo || rows >= rows_hi) rows = 0;
+        const int r = (g < E) ? counts[g] : T;
+        int rows = r, first = 0;
+        if (split != 0) {
+          const int tail = r % kTallTile;
+          const int rt = r < kSplitRows ? 0 : ((g < E && r >= kTallTile && tail < kSplitRows) ? r - tail : r);
+          if (split == 1) rows = rt;
+          else { rows = r - rt; first = rt; }
+        }
         rows_of[g] = rows;
-        base_of[g] = (g < E) ? offsets[g] : 0;
+        base_of[g] = (g < E) ? offsets[g] + first : 0;
         v = static_cast<int>(ceil_div(rows, BM)) * ((g < E) ? nt_routed : nt_shared);
       }
 #pragma unroll

@@ -232,8 +232,7 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
   } else {
     const int nt_r = (MODE == SMode::GateUp) ? a.I / bn_cols : H / bn_cols;
     const int nt_s = has_shared ? ((MODE == SMode::GateUp) ? a.S / bn_cols : H / bn_cols) : 0;
-    build_tile_prefix(sched, a.counts, a.offsets, a.E, a.T, has_shared, BM, nt_r, nt_s, a.rows_lo,
-                      a.rows_hi);
+    build_tile_prefix(sched, a.counts, a.offsets, a.E, a.T, has_shared, BM, nt_r, nt_s, a.split);
     const int nk_r = ((MODE == SMode::GateUp) ? H : a.I) / C::kElems;
     const int nk_s = ((MODE == SMode::GateUp) ? H : a.S) / C::kElems;
     walk = balanced_walk(sched, gcost, cpre, G, a.E, nk_r, nk_s);

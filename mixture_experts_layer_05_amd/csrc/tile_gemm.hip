@@ -159,7 +159,7 @@ __global__ void __launch_bounds__(kPPThreads) tiledpp_expert_kernel(ExpertArgs a
   const int nt_r = (MODE == Mode::GateUp) ? a.I / bn_cols : H / bn_cols;
   const int nt_s = has_shared ? ((MODE == Mode::GateUp) ? a.S / bn_cols : H / bn_cols) : 0;
   const int total = build_tile_prefix(prefix, a.counts, a.offsets, a.E, a.T, has_shared, BM, nt_r, nt_s,
-                                      a.rows_lo, a.rows_hi);
+                                      a.split);
 
   // DMA lane mapping: instruction q of this wave covers tile rows
   // 8 (4 wave + q) + lane / 8; LDS piece lane % 8 holds global piece
@@ -392,7 +392,7 @@ __global__ void __launch_bounds__(kF8PPThreads) tiled8pp_expert_kernel(ExpertArg
   const int nt_r = (MODE == Mode::GateUp) ? a.I / bn_cols : H / bn_cols;
   const int nt_s = has_shared ? ((MODE == Mode::GateUp) ? a.S / bn_cols : H / bn_cols) : 0;
   const int total = build_tile_prefix(prefix, a.counts, a.offsets, a.E, a.T, has_shared, BM, nt_r, nt_s,
-                                      a.rows_lo, a.rows_hi);
+                                      a.split);
 
   // DMA lane mapping: instruction q covers 8 rows (row 8 q' + lane / 8); LDS piece
   // lane % 8 holds global piece (lane % 8) ^ ((row / 2) mod 8), which depends on

@@ -232,9 +232,10 @@ def test_tiled_fp8_kernels_with_partial_tiles(T):
     _run(TILED.with_(name="tiled_rows_fp8", weight_dtype=W.DT_FP8), T, 30 + T)
 
 
-# Groups on both sides of the 128-row split between the 256-row LDS-tiled kernel
-# and the streaming kernel's 128-row tiles (Zipf-skewed counts), checked on
-# every token; the shared expert (600 rows) runs on the tiled kernel.
+# Rows on both sides of the split between the 256-row LDS-tiled kernel and the
+# streaming kernel's 128-row tiles (Zipf-skewed counts: short groups, and long
+# groups whose short tails go to the streaming kernel), checked on every token;
+# the shared expert (600 rows) runs whole on the tiled kernel.
 MIXED = W.LayerShape("mixed_groups", 512, 8, 256, 2, 256, W.DT_BF16, W.DT_BF16)
 
 
@@ -243,7 +244,9 @@ def test_groups_split_between_kernels_by_rows(dt):
     shape = MIXED.with_(name=f"mixed_groups_{dt}", weight_dtype=dt)
     case, gpu, ora, _ = _run(shape, 600, 61, 1.5)
     counts = gpu["counts"]
-    assert (counts >= 128).any() and ((counts > 0) & (counts < 128)).any(), counts
+    tail = counts % 256
+    assert ((counts >= 256) & (tail > 0) & (tail < 128)).any(), counts   # a long group's short tail
+    assert ((counts > 0) & (counts < 128)).any(), counts                  # a short group
 
 
 # 256-row tiles with the shortest contractions the kernels accept (128 elements)

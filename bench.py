@@ -125,7 +125,8 @@ def gate_up_kernel(shape, T: int) -> str:
     rho = T * K // E
     if rho >= 48 and dt != "mxfp4":   # MXFP4 runs on the streaming kernel at every size
         tall = "tiled8pp_expert_kernel<GateUp> (fp8, 256x128)" if fp8 else "tiledpp_expert_kernel<GateUp> (bf16, 256x256)"
-        return f"{tall} for groups of >= 128 rows + stream_expert_kernel<GateUp, 128, 128, 2, {dt}> for the rest"
+        rest = "64, 128, 1" if rho >= 192 else "128, 128, 2"
+        return f"{tall} for groups of >= 128 rows + stream_expert_kernel<GateUp, {rest}, {dt}> for the rest"
     narrow = min(E, T * K) * (I // 64) < 3 * 256
     if rho >= 48:
         return f"stream_expert_kernel<GateUp, 128, 128, 2, {dt}>"

@@ -114,8 +114,8 @@ def layer_roofline(shape, a, ms_per_step):
 
 
 def gate_up_kernel(shape, T: int) -> str:
-    """Name of the gate/up kernel the library launches for this layer and T (the
-    same rows-per-expert rule as its launchers; used to label the roofline)."""
+    """Name of the gate/up kernel(s) the library launches for this layer and T (the
+    same rules as its launchers; used to label the roofline)."""
     if shape.weight_dtype == "f32":
         return "gate_up_f32_kernel"
     fp8 = shape.weight_dtype != "bf16"
@@ -123,20 +123,24 @@ def gate_up_kernel(shape, T: int) -> str:
     H, E, I, K, S = (shape.hidden_size, shape.n_routed_experts, shape.moe_intermediate_size,
                      shape.num_experts_per_tok, shape.shared_expert_intermediate_size)
     rho = T * K // E
-    if rho >= 48 and dt != "mxfp4":   # MXFP4 runs on the streaming kernel at every size
+
+    def stream(r):
+        narrow = min(E, T * K) * (I // 64) < 3 * 256
+        if r >= 48:
+            cfg = "128, 128, 2"
+        elif r <= 12:
+            cfg = "16, 128, 1"
+        elif r <= 24:
+            cfg = "32, 64, 2" if narrow else "32, 128, 1"
+        else:
+            cfg = "64, 64, 2" if narrow else "64, 128, 1"
+        return f"stream_expert_kernel<GateUp, {cfg}, {dt}>"
+
+    # Rows divided between the 256-row LDS-tiled kernel and the streaming kernel.
+    if dt != "mxfp4" and rho >= 16 and T * K * I >= 256 * 256 * 128:
         tall = "tiled8pp_expert_kernel<GateUp> (fp8, 256x128)" if fp8 else "tiledpp_expert_kernel<GateUp> (bf16, 256x256)"
-        rest = "64, 128, 1" if rho >= 192 else "128, 128, 2"
-        return f"{tall} for groups of >= 128 rows + stream_expert_kernel<GateUp, {rest}, {dt}> for the rest"
-    narrow = min(E, T * K) * (I // 64) < 3 * 256
-    if rho >= 48:
-        return f"stream_expert_kernel<GateUp, 128, 128, 2, {dt}>"
-    if rho <= 12:
-        cfg = "16, 128, 1"
-    elif rho <= 24:
-        cfg = "32, 64, 2" if narrow else "32, 128, 1"
-    else:
-        cfg = "64, 64, 2" if narrow else "64, 128, 1"
-    return f"stream_expert_kernel<GateUp, {cfg}, {dt}>"
+        return f"{tall} for groups of >= 128 rows + {stream(47 if rho >= 192 else rho)} for the rest"
+    return stream(rho)
 
 
 def kernel_source_file(kernel_label: str) -> str:

@@ -251,14 +251,24 @@ int tile_bound(const ExpertArgs& a, int BM, int nt_routed, int nt_shared) {
 
 // Rows per expert decide the kernels.  The average expert sees rho = T*K/E rows
 // (the load measure of the small-M / large-M family choice of [DeepGEMM fork
-// PR #5, "Dynamic family selection"]).  Below kMixRows, the weight-streaming
-// kernels alone (stream_gemm.hip, which pick their tile height from rho).  From
-// there, with bf16 or fp8 weights, the call's rows are divided by the realised
-// counts, read on the device (schedule.h, build_tile_prefix): rows that fill a
-// 256-row tile at least half go to the LDS-tiled MFMA kernels (tile_gemm.hip),
-// short groups and the short tails of long ones to the streaming kernel's
-// 128-row tiles.  Two launches, disjoint rows.
-constexpr int64_t kMixRows = 48;
+// PR #5, "Dynamic family selection"]).  By default the weight-streaming kernels
+// alone (stream_gemm.hip, which pick their tile height from rho).  A call whose
+// rows could fill the GPU with 256-row tiles (T*K*I >= 256 CUs x 256 rows x 128
+// columns) and whose experts see at least kMixRows rows on average is instead
+// divided by its realised counts, read on the device (schedule.h,
+// build_tile_prefix), when its weights are bf16 or fp8: rows that fill a 256-row
+// tile at least half go to the LDS-tiled MFMA kernels (tile_gemm.hip), short
+// groups and the short tails of long ones to the streaming kernel.  Two launches,
+// disjoint rows.  Measured: the large layer at T = 512-1024 with Zipf skew
+// alpha >= 1 runs 22-30 % faster split; a call too small to fill the GPU with
+// 256-row tiles runs them nearly alone (the drafter at T = 224, whose shared
+// expert would be one 224-row group: 1.7x slower).
+constexpr int64_t kMixRows = 16;
+
+bool split_call(const ExpertArgs& a, int weight_dtype, int64_t rho) {
+  return weight_dtype != kDtypeMxfp4 && rho >= kMixRows &&
+         static_cast<int64_t>(a.T) * a.K * a.I >= int64_t{256} * 256 * 128 && tall_tiles_fit(a);
+}
 
 // Tile height for the streaming kernel's share of a split call, through the rows
 // per expert it is given: from 192 rows per expert on average that share is mostly
@@ -279,7 +289,7 @@ hipError_t launch_gate_up(const ExpertArgs& a, int weight_dtype, hipStream_t str
   }
   const int64_t rho = rows_per_expert(a);
   // MXFP4 weights run on the streaming kernel at every size (no LDS-tiled form).
-  if (weight_dtype != kDtypeMxfp4 && rho >= kMixRows && tall_tiles_fit(a)) {
+  if (split_call(a, weight_dtype, rho)) {
     ExpertArgs tall = a, rest = a;
     tall.split = 1;
     rest.split = 2;
@@ -297,7 +307,7 @@ hipError_t launch_down(const ExpertArgs& a, int weight_dtype, hipStream_t stream
     return hipGetLastError();
   }
   const int64_t rho = rows_per_expert(a);
-  if (weight_dtype != kDtypeMxfp4 && rho >= kMixRows && a.H % 256 == 0 && tall_tiles_fit(a)) {
+  if (split_call(a, weight_dtype, rho) && a.H % 256 == 0) {
     ExpertArgs tall = a, rest = a;
     tall.split = 1;
     rest.split = 2;

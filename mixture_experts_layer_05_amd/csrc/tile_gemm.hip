@@ -16,8 +16,10 @@
 //   * tiled8pp_expert_kernel (fp8): 256 x 128 tiles, 8 waves of 64 x 64 with
 //     16x16x128 fp8 MFMAs and all operands loaded by LDS DMA; see below.
 //
-// Below 160 rows per expert the streaming kernels serve every size (their
-// 128 x 128 tiles ran 3-7 % faster than 128-row LDS tiles here, measured).
+// The expert launchers (experts.hip) give these kernels the rows that fill a
+// 256-row tile at least half, in calls large enough to fill the GPU with such
+// tiles; the streaming kernels serve the rest (their 128 x 128 tiles ran 3-7 %
+// faster than 128-row LDS tiles for those, measured).
 #include "kernels.h"
 #include "schedule.h"
 

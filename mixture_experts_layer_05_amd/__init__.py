@@ -234,12 +234,13 @@ def forward_down(cfg, x, topk_weights, shared_gate, counts, offsets, perm, weigh
 
 class MoELayer:
     """Owns the outputs and the workspace for up to `max_tokens` tokens and runs
-    route -> dispatch -> forward on the current stream."""
+    route -> dispatch -> forward on the current stream.  With `stats=True` each
+    route also fills `route_stats` (int32[4], as moe_route documents it)."""
 
     def __init__(self, cfg: MoEConfig, weights: Dict[str, torch.Tensor], w_router: torch.Tensor,
                  w_shared_gate: Optional[torch.Tensor] = None,
                  shared: Optional[Dict[str, torch.Tensor]] = None, max_tokens: int = 1,
-                 device: str = "cuda", act_output: bool = False):
+                 device: str = "cuda", act_output: bool = False, stats: bool = False):
         self.cfg = cfg
         self.weights_dict, self.shared_dict = weights, shared
         self.weights = expert_weights_struct(cfg, weights, shared)
@@ -251,7 +252,9 @@ class MoELayer:
         self.topk_ids = torch.empty(max_tokens, K, dtype=torch.int32, device=dev)
         self.topk_weights = torch.empty(max_tokens, K, dtype=torch.float32, device=dev)
         self.shared_gate = torch.empty(max_tokens, dtype=torch.float32, device=dev)
-        self.route_stats = torch.zeros(4, dtype=torch.int32, device=dev)
+        # Routing statistics cost one extra single-block pass when there is no
+        # expert budget, so they are kept only on request.
+        self.route_stats = torch.zeros(4, dtype=torch.int32, device=dev) if stats else None
         self.counts = torch.empty(E, dtype=torch.int32, device=dev)
         self.offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
         self.perm = torch.empty(max_tokens * K, dtype=torch.int32, device=dev)

@@ -127,7 +127,7 @@ def run_gpu(case: Case, layer=None) -> Dict[str, np.ndarray]:
     if layer is None:
         layer = moe.MoELayer(config(shape), case.weights, case.inp.w_router.cuda(),
                              None if case.inp.w_shared_gate is None else case.inp.w_shared_gate.cuda(),
-                             case.shared, max_tokens=max(T, 1))
+                             case.shared, max_tokens=max(T, 1), stats=True)
     x = case.inp.x.cuda()
     bias = None if case.inp.logit_bias is None else case.inp.logit_bias.cuda()
     layer.route_stats.fill_(-7)

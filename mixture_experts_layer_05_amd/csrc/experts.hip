@@ -89,52 +89,68 @@ __global__ void __launch_bounds__(256) down_f32_kernel(ExpertArgs a) {
 // y[t,:] (+)= sum over k of w[t,k] * o[t*K+k,:], k ascending, skipping dropped
 // slots (weight 0, row never written).  `accumulate` adds onto the shared
 // expert's term already stored in y.  If y_act is not null the same values also
-// go there in the activation dtype.  One workgroup per token.
+// go there in the activation dtype.  A workgroup item is one token's run of
+// 1024 columns (256 float4), so small T still spreads over every CU and each
+// thread's K + 1 loads are independent.
+constexpr int kCombineCols = 1024;
+
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ o,
                                                       const float* __restrict__ topk_w,
                                                       float* __restrict__ y, void* __restrict__ y_act,
                                                       int act_bf16, int T, int H, int K, int accumulate) {
-  // The optional activation-dtype copy of an output element: bf16 rounded to
-  // nearest (ties to even), or float32 as is.
-  auto put_act = [&](size_t i, float v) {
-    if (act_bf16) static_cast<uint16_t*>(y_act)[i] = f32_to_bf16_bits(v);
-    else static_cast<float*>(y_act)[i] = v;
-  };
-  for (int t = blockIdx.x; t < T; t += gridDim.x) {
+  const int nchunk = (H + kCombineCols - 1) / kCombineCols;
+  const bool act_vec = reinterpret_cast<uintptr_t>(y_act) % (act_bf16 ? 8 : 16) == 0;
+  const int64_t items = static_cast<int64_t>(T) * nchunk;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int t = static_cast<int>(it / nchunk);
+    const int c0 = static_cast<int>(it - static_cast<int64_t>(t) * nchunk) * kCombineCols;
     const float* wr = topk_w + static_cast<size_t>(t) * K;
     const float* orow = o + static_cast<size_t>(t) * K * H;
     float* yr = y + static_cast<size_t>(t) * H;
     const size_t row = static_cast<size_t>(t) * H;
     if ((H & 3) == 0) {
-      const int h4 = H / 4;
-      for (int c = threadIdx.x; c < h4; c += blockDim.x) {
-        float4 s = accumulate ? reinterpret_cast<const float4*>(yr)[c] : float4{0.f, 0.f, 0.f, 0.f};
-        for (int k = 0; k < K; ++k) {
-          const float w = wr[k];
-          if (w == 0.f) continue;
-          const float4 v = reinterpret_cast<const float4*>(orow + static_cast<size_t>(k) * H)[c];
-          s.x = fmaf(w, v.x, s.x);
-          s.y = fmaf(w, v.y, s.y);
-          s.z = fmaf(w, v.z, s.z);
-          s.w = fmaf(w, v.w, s.w);
-        }
-        reinterpret_cast<float4*>(yr)[c] = s;
-        if (y_act) {
-          put_act(row + 4 * c, s.x);
-          put_act(row + 4 * c + 1, s.y);
-          put_act(row + 4 * c + 2, s.z);
-          put_act(row + 4 * c + 3, s.w);
+      const int c = c0 / 4 + static_cast<int>(threadIdx.x);
+      if (4 * c >= H) continue;
+      float4 s = accumulate ? reinterpret_cast<const float4*>(yr)[c] : float4{0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < K; ++k) {
+        const float w = wr[k];
+        if (w == 0.f) continue;
+        const float4 v = reinterpret_cast<const float4*>(orow + static_cast<size_t>(k) * H)[c];
+        s.x = fmaf(w, v.x, s.x);
+        s.y = fmaf(w, v.y, s.y);
+        s.z = fmaf(w, v.z, s.z);
+        s.w = fmaf(w, v.w, s.w);
+      }
+      reinterpret_cast<float4*>(yr)[c] = s;
+      if (y_act) {
+        // bf16: round to nearest (ties to even).  Four values per store when y_act
+        // is aligned for it (it need only be aligned to its element size).
+        if (!act_vec) {
+          const float v[4] = {s.x, s.y, s.z, s.w};
+          for (int e = 0; e < 4; ++e) {
+            if (act_bf16) static_cast<uint16_t*>(y_act)[row + 4 * c + e] = f32_to_bf16_bits(v[e]);
+            else static_cast<float*>(y_act)[row + 4 * c + e] = v[e];
+          }
+        } else if (act_bf16) {
+          const uint32_t lo = f32_to_bf16_bits(s.x) | (static_cast<uint32_t>(f32_to_bf16_bits(s.y)) << 16);
+          const uint32_t hi = f32_to_bf16_bits(s.z) | (static_cast<uint32_t>(f32_to_bf16_bits(s.w)) << 16);
+          reinterpret_cast<uint2*>(static_cast<uint16_t*>(y_act) + row)[c] = uint2{lo, hi};
+        } else {
+          reinterpret_cast<float4*>(static_cast<float*>(y_act) + row)[c] = s;
         }
       }
     } else {
-      for (int c = threadIdx.x; c < H; c += blockDim.x) {
+      for (int c = c0 + static_cast<int>(threadIdx.x); c < min(H, c0 + kCombineCols); c += blockDim.x) {
         float s = accumulate ? yr[c] : 0.f;
         for (int k = 0; k < K; ++k) {
           const float w = wr[k];
           if (w != 0.f) s = fmaf(w, orow[static_cast<size_t>(k) * H + c], s);
         }
         yr[c] = s;
-        if (y_act) put_act(row + c, s);
+        if (y_act) {
+          if (act_bf16) static_cast<uint16_t*>(y_act)[row + c] = f32_to_bf16_bits(s);
+          else static_cast<float*>(y_act)[row + c] = s;
+        }
       }
     }
   }
@@ -319,7 +335,8 @@ hipError_t launch_down(const ExpertArgs& a, int weight_dtype, hipStream_t stream
 }
 
 hipError_t launch_combine(const ExpertArgs& a, hipStream_t stream) {
-  const int grid = static_cast<int>(std::min<int64_t>(a.T, 4096));
+  const int64_t items = static_cast<int64_t>(a.T) * ceil_div(a.H, kCombineCols);
+  const int grid = static_cast<int>(std::min<int64_t>(items, 65536));
   combine_kernel<<<grid, 256, 0, stream>>>(a.o, a.topk_w, a.y, a.y_act, a.act_bf16, a.T, a.H, a.K,
                                            a.S > 0 ? 1 : 0);
   return hipGetLastError();

@@ -338,14 +338,21 @@ def test_halves_equal_forward():
 
 
 @pytest.mark.parametrize("shape,T", [(W.DRAFTER, 56), (W.TINY, 40)])
-def test_activation_dtype_output(shape, T):
-    """The optional y_act output: the cast of the float32 y to the activation dtype."""
+@pytest.mark.parametrize("element_aligned", [False, True])
+def test_activation_dtype_output(shape, T, element_aligned):
+    """The optional y_act output: the cast of the float32 y to the activation dtype.
+    element_aligned: y_act starts one element into an allocation, aligned only to
+    its element size (the combine pass then stores element by element)."""
     import mixture_experts_layer_05_amd as moe
-    print(f"\n[case] y_act {shape.name} T={T}", flush=True)
+    print(f"\n[case] y_act {shape.name} T={T} element_aligned={element_aligned}", flush=True)
     case = Hn.make_case(shape, T, 14)
     sg = None if case.inp.w_shared_gate is None else case.inp.w_shared_gate.cuda()
     layer = moe.MoELayer(Hn.config(shape), case.weights, case.inp.w_router.cuda(), sg, case.shared,
                          max_tokens=T, act_output=True)
+    if element_aligned:
+        buf = torch.empty(T * shape.hidden_size + 1, dtype=layer.y_act.dtype, device="cuda")
+        layer.y_act = buf[1:].view(T, shape.hidden_size)
+        assert layer.y_act.data_ptr() % 8 != 0
     bias = None if case.inp.logit_bias is None else case.inp.logit_bias.cuda()
     y = layer(case.inp.x.cuda(), bias)
     torch.cuda.synchronize()

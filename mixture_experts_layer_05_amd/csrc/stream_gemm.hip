@@ -62,23 +62,25 @@ enum class SMode { GateUp, Down, Router };
 // FMT is the weight format: kDtypeBf16; kDtypeFp8 (e4m3 codes, float32 scale per
 // row and 128-group, activations quantised the same way) in stages of one group,
 // or kFp8Wide, the same in stages of two groups (contractions that are multiples
-// of 256); kDtypeMxfp4 (E2M1 codes two per byte, E8M0 scale per 32 elements,
+// of 256), or kFp8Quad, in stages of four groups (multiples of 512: one 16-byte
+// scale load per row per stage instead of two 8-byte ones); kDtypeMxfp4 (E2M1 codes two per byte, E8M0 scale per 32 elements,
 // activations MXFP8) in stages of 256 elements, or kMxWide, the same in stages of
 // 512 (contractions that are multiples of 512).
 constexpr int kFp8Wide = 0x12;
 constexpr int kMxWide = 0x13;
+constexpr int kFp8Quad = 0x14;
 
 template <SMode MODE, int BM, int BN, int WM, int FMT>
 struct StreamCfg {
   static constexpr bool kQ = FMT != kDtypeBf16;                // 8-bit activation codes + scales
   static constexpr bool kMX = FMT == kDtypeMxfp4 || FMT == kMxWide;
-  static constexpr bool kWide = kMX || FMT == kFp8Wide;        // 8-bit A in stages of >= 256
+  static constexpr bool kWide = kMX || FMT == kFp8Wide || FMT == kFp8Quad;   // 8-bit A in stages of >= 256
   static constexpr int kWM = WM;                               // compute waves along rows
   static constexpr int kWN = kComputeWaves / WM;               // compute waves along weight rows
   // Contraction elements per stage: 128 (one bf16 row slice of 256 bytes, or one fp8
   // 128-group), 256 for wide fp8 and for MX (a weight row gives 128 contiguous
   // bytes): 256-byte pieces load faster per byte than 128-byte ones.
-  static constexpr int kElems = FMT == kMxWide ? 512 : kWide ? 256 : 128;
+  static constexpr int kElems = (FMT == kMxWide || FMT == kFp8Quad) ? 512 : kWide ? 256 : 128;
   static constexpr int kRowDataA = kQ ? kElems : 256;          // A bytes per row per stage
   static constexpr int kRowDataB = kMX ? kElems / 2 : kRowDataA;   // B bytes per row per stage
   static constexpr int kSub = kQ ? kElems / 128 : 4;           // MFMA k-steps per stage
@@ -96,8 +98,10 @@ struct StreamCfg {
   static constexpr int kSlot = kBOff + BN * kRowStrideB;       // one LDS stage buffer
   static constexpr int kScales = BM + BN;                      // one scale word per row (below)
   // Scale word of a row per stage: the fp8 float32 group scale (two of them for
-  // wide fp8), or the MX row's E8M0 bytes (one per 32 elements: 8 or 16).
-  using ScaleWord = std::conditional_t<FMT == kMxWide, uint4, std::conditional_t<kWide, uint2, uint32_t>>;
+  // wide fp8, four in quad stages), or the MX row's E8M0 bytes (one per 32
+  // elements: 8 or 16).
+  using ScaleWord = std::conditional_t<FMT == kMxWide || FMT == kFp8Quad, uint4,
+                                       std::conditional_t<kWide, uint2, uint32_t>>;
   static_assert(BN % kRowsPerPassB == 0, "BN must be a multiple of the rows per pass");
   static_assert(MODE == SMode::Down || kCB % 2 == 0, "gate/up needs gate and up blocks");
   static_assert(kRM >= 1 && BM % (16 * WM) == 0, "rows per wave must be a multiple of 16");
@@ -591,7 +595,10 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
             const uint4 hi = lds_ld16(p + 64 + 16 * g);
             af[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
             const int row = wrow0 + 16 * i + 4 * g;
-            if constexpr (C::kWide) {
+            if constexpr (kSub == 4) {
+              // Four floats per row (groups 0..3 of the stage).
+              sa[i] = f32x4{scf[4 * row + s], scf[4 * row + 4 + s], scf[4 * row + 8 + s], scf[4 * row + 12 + s]};
+            } else if constexpr (C::kWide) {
               // Two floats per row (groups 0 and 1 of the stage).
               const f32x4 r01 = *reinterpret_cast<const f32x4*>(&scf[2 * row]);
               const f32x4 r23 = *reinterpret_cast<const f32x4*>(&scf[2 * row + 4]);
@@ -607,7 +614,7 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
             const uint4 lo = lds_ld16(p + 16 * g);
             const uint4 hi = lds_ld16(p + 64 + 16 * g);
             bf[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            sb[j] = C::kWide ? scf[2 * (BM + br) + s] : scf[BM + br];
+            sb[j] = scf[kSub * (BM + br) + s];
           }
           const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -751,6 +758,14 @@ constexpr int64_t kStreamTallRows = 48;   // rows per expert from which the tile
 // tiles per CU: its tiles all have H/128 stages, so the count per workgroup sets
 // the balance.  Down tiles keep 128 weight rows: they are short (I/128 stages),
 // there are H/128 of them per row block, and wider tiles re-read fewer h rows.
+// kFp8Quad where its double-buffered 512-byte row stages fit LDS next to the tile
+// schedule (tiles of at most 128 token and weight rows: 64 x 64, 32 x 64); larger
+// tiles run kFp8Wide.  MXFP4 128 x 128 tiles run in 256-element stages.
+template <int FMT, int BM, int BN>
+constexpr int fit_fmt() {
+  return FMT == kMxWide && BM + BN > 192 ? kDtypeMxfp4 : (FMT == kFp8Quad && BM + BN > 128) ? kFp8Wide : FMT;
+}
+
 template <SMode MODE, int FMT>
 hipError_t launch_stream_rho(const ExpertArgs& a, int64_t rho, hipStream_t stream) {
   const int64_t slots = static_cast<int64_t>(a.T) * a.K;
@@ -764,12 +779,12 @@ hipError_t launch_stream_rho(const ExpertArgs& a, int64_t rho, hipStream_t strea
   // ran the large layer 16 % faster at T = 8192; for bf16 and fp8 they ran 3-7 %
   // faster than 128-row LDS-tiled kernels between 48 and 160 rows per expert.
   if (rho >= kStreamTallRows)
-    return launch_stream<MODE, 128, 128, 2, (FMT == kMxWide ? kDtypeMxfp4 : FMT)>(a, stream);
-  if (rho <= 12) return launch_stream<MODE, 16, 128, 1, FMT>(a, stream);
-  if (rho <= 24) return narrow ? launch_stream<MODE, 32, 64, 2, FMT>(a, stream)
-                               : launch_stream<MODE, 32, 128, 1, FMT>(a, stream);
-  return narrow ? launch_stream<MODE, 64, 64, 2, FMT>(a, stream)
-                : launch_stream<MODE, 64, 128, 1, FMT>(a, stream);
+    return launch_stream<MODE, 128, 128, 2, fit_fmt<FMT, 128, 128>()>(a, stream);
+  if (rho <= 12) return launch_stream<MODE, 16, 128, 1, fit_fmt<FMT, 16, 128>()>(a, stream);
+  if (rho <= 24) return narrow ? launch_stream<MODE, 32, 64, 2, fit_fmt<FMT, 32, 64>()>(a, stream)
+                               : launch_stream<MODE, 32, 128, 1, fit_fmt<FMT, 32, 128>()>(a, stream);
+  return narrow ? launch_stream<MODE, 64, 64, 2, fit_fmt<FMT, 64, 64>()>(a, stream)
+                : launch_stream<MODE, 64, 128, 1, fit_fmt<FMT, 64, 128>()>(a, stream);
 }
 
 }  // namespace
@@ -782,8 +797,19 @@ hipError_t launch_router_stream(const ExpertArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// fp8 runs in two-group stages when every contraction (H, I, S) is a multiple of 256.
+// fp8 runs in two-group stages when every contraction (H, I, S) is a multiple of 256,
+// in four-group stages when the projection's contractions are multiples of 512 and
+// its scale arrays are 16-byte aligned (one 16-byte load per row and stage).
 static bool fp8_wide(const ExpertArgs& a) { return a.H % 256 == 0 && a.I % 256 == 0 && a.S % 256 == 0; }
+static bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+static bool fp8_quad_gate_up(const ExpertArgs& a) {
+  return fp8_wide(a) && a.H % 512 == 0 && aligned16(a.xs) && aligned16(a.s_gate) && aligned16(a.s_up) &&
+         aligned16(a.ss_gate) && aligned16(a.ss_up);
+}
+static bool fp8_quad_down(const ExpertArgs& a) {
+  return fp8_wide(a) && a.I % 512 == 0 && a.S % 512 == 0 && aligned16(a.hs) && aligned16(a.s_down) &&
+         aligned16(a.ss_down);
+}
 
 // MXFP4 runs in 512-element stages (256-byte weight row pieces) when the
 // projection's contractions are multiples of 512.
@@ -795,8 +821,9 @@ hipError_t launch_gate_up_stream(const ExpertArgs& a, int weight_dtype, int64_t 
     return mx_wide_gate_up(a) ? launch_stream_rho<SMode::GateUp, kMxWide>(a, rho, stream)
                               : launch_stream_rho<SMode::GateUp, kDtypeMxfp4>(a, rho, stream);
   if (weight_dtype == kDtypeFp8)
-    return fp8_wide(a) ? launch_stream_rho<SMode::GateUp, kFp8Wide>(a, rho, stream)
-                       : launch_stream_rho<SMode::GateUp, kDtypeFp8>(a, rho, stream);
+    return fp8_quad_gate_up(a) ? launch_stream_rho<SMode::GateUp, kFp8Quad>(a, rho, stream)
+           : fp8_wide(a)       ? launch_stream_rho<SMode::GateUp, kFp8Wide>(a, rho, stream)
+                               : launch_stream_rho<SMode::GateUp, kDtypeFp8>(a, rho, stream);
   return launch_stream_rho<SMode::GateUp, kDtypeBf16>(a, rho, stream);
 }
 
@@ -805,8 +832,9 @@ hipError_t launch_down_stream(const ExpertArgs& a, int weight_dtype, int64_t rho
     return mx_wide_down(a) ? launch_stream_rho<SMode::Down, kMxWide>(a, rho, stream)
                            : launch_stream_rho<SMode::Down, kDtypeMxfp4>(a, rho, stream);
   if (weight_dtype == kDtypeFp8)
-    return fp8_wide(a) ? launch_stream_rho<SMode::Down, kFp8Wide>(a, rho, stream)
-                       : launch_stream_rho<SMode::Down, kDtypeFp8>(a, rho, stream);
+    return fp8_quad_down(a) ? launch_stream_rho<SMode::Down, kFp8Quad>(a, rho, stream)
+           : fp8_wide(a)    ? launch_stream_rho<SMode::Down, kFp8Wide>(a, rho, stream)
+                            : launch_stream_rho<SMode::Down, kDtypeFp8>(a, rho, stream);
   return launch_stream_rho<SMode::Down, kDtypeBf16>(a, rho, stream);
 }
 

@@ -98,6 +98,16 @@ def test_fp8_small_ragged(T):
     _run(_SMALL_FP8, T, W.base_seed(0, T) + 11)
 
 
+# fp8 gate/up in four-group stages (H a multiple of 512): 32 x 64 tiles at 16 rows
+# per expert, 64 x 64 at 25, ragged in both.
+_SMALL_FP8_QUAD = W.LayerShape("small_fp8_quad", 1024, 8, 512, 2, 512, W.DT_FP8, W.DT_BF16)
+
+
+@pytest.mark.parametrize("T", [64, 100])
+def test_fp8_quad_stages_ragged(T):
+    _run(_SMALL_FP8_QUAD, T, W.base_seed(0, T) + 17)
+
+
 # MXFP4 at prefill sizes (128 x 128 streaming tiles): few experts with many rows
 # (partial row tiles), and the large layer at T = 8192 on sampled tokens.
 @pytest.mark.parametrize("shape,T,seed,alpha,tokens", [

@@ -210,7 +210,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is not sharded "
-              f"across GPUs in this build.", file=sys.stderr)
+              f"across GPUs (one GPU's share of an expert-parallel layer is the ep_rank workload).",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

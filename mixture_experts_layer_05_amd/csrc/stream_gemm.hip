@@ -159,8 +159,10 @@ struct Walk {
 // the same time on one XCD and share its L2.  Cutting by tile count instead would
 // hand the shared expert's longer down tiles (contraction S instead of I) to the
 // last XCDs only.
-__device__ Walk balanced_walk(const int* sched, int* gcost, long long* cpre, int G, int E, int nk_routed,
-                              int nk_shared) {
+// cpre (G + 1 entries of CostT) receives the cost prefix; a group's tile cost is
+// nk_routed or nk_shared stages.
+template <typename CostT>
+__device__ Walk balanced_walk(const int* sched, CostT* cpre, int G, int E, int nk_routed, int nk_shared) {
   const int* prefix = sched;
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
@@ -170,7 +172,6 @@ __device__ Walk balanced_walk(const int* sched, int* gcost, long long* cpre, int
       long long v = 0;
       if (g < G) {
         const int c = (g < E) ? nk_routed : nk_shared;
-        gcost[g] = c;
         v = static_cast<long long>(c) * (prefix[g + 1] - prefix[g]);
       }
 #pragma unroll
@@ -178,14 +179,14 @@ __device__ Walk balanced_walk(const int* sched, int* gcost, long long* cpre, int
         const long long n = __shfl_up(v, o, kWave);
         if (lane >= o) v += n;
       }
-      if (g < G) cpre[g + 1] = carry + v;
+      if (g < G) cpre[g + 1] = static_cast<CostT>(carry + v);
       carry += __shfl(v, kWave - 1, kWave);
     }
     if (lane == 0) cpre[0] = 0;
   }
   __syncthreads();
   const int total = prefix[G];
-  const long long ctot = cpre[G];
+  const long long ctot = static_cast<long long>(cpre[G]);
   // First tile whose start cost is >= c.  The last group g with cpre[g] <= c < ctot
   // holds tiles (cpre[g + 1] > c), so the quotient stays inside it or at its end.
   auto first_at = [&](long long c) -> int {
@@ -193,10 +194,11 @@ __device__ Walk balanced_walk(const int* sched, int* gcost, long long* cpre, int
     int lo = 0, hi = G;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (cpre[mid] <= c) lo = mid; else hi = mid;
+      if (static_cast<long long>(cpre[mid]) <= c) lo = mid; else hi = mid;
     }
-    const long long off = c - cpre[lo];
-    return prefix[lo] + static_cast<int>((off + gcost[lo] - 1) / gcost[lo]);
+    const long long off = c - static_cast<long long>(cpre[lo]);
+    const int cost = (lo < E) ? nk_routed : nk_shared;
+    return prefix[lo] + static_cast<int>((off + cost - 1) / cost);
   };
   const int xcd = blockIdx.x % 8;
   const int begin = first_at(ctot * xcd / 8);
@@ -215,8 +217,10 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
   using SW = typename C::ScaleWord;
   __shared__ __attribute__((aligned(16))) SW sscale[FP8 ? 2 * C::kScales : 1];
   __shared__ int sched[kSchedInts];
-  __shared__ int gcost[kSchedStride];
-  __shared__ long long cpre[kSchedStride];
+  // Cost prefix of the tile walk.  32-bit in the four-group fp8 kernels, whose
+  // 16 x 128 tile needs the LDS; their launcher checks that the costs fit.
+  using CostT = std::conditional_t<FMT == kFp8Quad, int, long long>;
+  __shared__ CostT cpre[kSchedStride];
 
   const int tid = threadIdx.x;
   const bool has_shared = a.S > 0;
@@ -239,7 +243,7 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
     build_tile_prefix(sched, a.counts, a.offsets, a.E, a.T, has_shared, BM, nt_r, nt_s, a.split);
     const int nk_r = ((MODE == SMode::GateUp) ? H : a.I) / C::kElems;
     const int nk_s = ((MODE == SMode::GateUp) ? H : a.S) / C::kElems;
-    walk = balanced_walk(sched, gcost, cpre, G, a.E, nk_r, nk_s);
+    walk = balanced_walk<CostT>(sched, cpre, G, a.E, nk_r, nk_s);
   }
   if (walk.tile >= walk.end) return;   // uniform across the workgroup
 
@@ -759,11 +763,12 @@ constexpr int64_t kStreamTallRows = 48;   // rows per expert from which the tile
 // the balance.  Down tiles keep 128 weight rows: they are short (I/128 stages),
 // there are H/128 of them per row block, and wider tiles re-read fewer h rows.
 // kFp8Quad where its double-buffered 512-byte row stages fit LDS next to the tile
-// schedule (tiles of at most 128 token and weight rows: 64 x 64, 32 x 64); larger
-// tiles run kFp8Wide.  MXFP4 128 x 128 tiles run in 256-element stages.
+// schedule (tiles of at most 144 token and weight rows: 16 x 128, 64 x 64,
+// 32 x 64); larger tiles run kFp8Wide.  MXFP4 128 x 128 tiles run in 256-element
+// stages.
 template <int FMT, int BM, int BN>
 constexpr int fit_fmt() {
-  return FMT == kMxWide && BM + BN > 192 ? kDtypeMxfp4 : (FMT == kFp8Quad && BM + BN > 128) ? kFp8Wide : FMT;
+  return FMT == kMxWide && BM + BN > 192 ? kDtypeMxfp4 : (FMT == kFp8Quad && BM + BN > 144) ? kFp8Wide : FMT;
 }
 
 template <SMode MODE, int FMT>
@@ -797,19 +802,24 @@ hipError_t launch_router_stream(const ExpertArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// fp8 runs in two-group stages when every contraction (H, I, S) is a multiple of 256,
-// in four-group stages when the projection's contractions are multiples of 512 and
-// its scale arrays are 16-byte aligned (one 16-byte load per row and stage).
+// fp8 runs in two-group stages when every contraction (H, I, S) is a multiple of 256;
+// gate/up in four-group stages when H is a multiple of 512 and its scale arrays are
+// 16-byte aligned (one 16-byte scale load per row and stage: narrow layer 8 %
+// faster; the down projection's one-stage tiles ran 3 % slower in them).
 static bool fp8_wide(const ExpertArgs& a) { return a.H % 256 == 0 && a.I % 256 == 0 && a.S % 256 == 0; }
 static bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+// The four-group kernels keep the tile walk's cost prefix in 32 bits: bound it by
+// the tile count of the smallest tiles (16 rows, 32 columns) times the stages.
+static bool quad_costs_fit(const ExpertArgs& a, int64_t n_routed, int64_t n_shared, int64_t kmax) {
+  const int64_t rows = static_cast<int64_t>(a.T) * a.K / 16 + std::min<int64_t>(a.E, static_cast<int64_t>(a.T) * a.K);
+  const int64_t tiles = rows * ceil_div(n_routed, 32) + ceil_div(a.T, 16) * ceil_div(n_shared, 32);
+  return tiles * (kmax / 512) < (int64_t{1} << 31);
+}
 static bool fp8_quad_gate_up(const ExpertArgs& a) {
   return fp8_wide(a) && a.H % 512 == 0 && aligned16(a.xs) && aligned16(a.s_gate) && aligned16(a.s_up) &&
-         aligned16(a.ss_gate) && aligned16(a.ss_up);
+         aligned16(a.ss_gate) && aligned16(a.ss_up) && quad_costs_fit(a, a.I, a.S, a.H);
 }
-static bool fp8_quad_down(const ExpertArgs& a) {
-  return fp8_wide(a) && a.I % 512 == 0 && a.S % 512 == 0 && aligned16(a.hs) && aligned16(a.s_down) &&
-         aligned16(a.ss_down);
-}
+
 
 // MXFP4 runs in 512-element stages (256-byte weight row pieces) when the
 // projection's contractions are multiples of 512.
@@ -832,9 +842,8 @@ hipError_t launch_down_stream(const ExpertArgs& a, int weight_dtype, int64_t rho
     return mx_wide_down(a) ? launch_stream_rho<SMode::Down, kMxWide>(a, rho, stream)
                            : launch_stream_rho<SMode::Down, kDtypeMxfp4>(a, rho, stream);
   if (weight_dtype == kDtypeFp8)
-    return fp8_quad_down(a) ? launch_stream_rho<SMode::Down, kFp8Quad>(a, rho, stream)
-           : fp8_wide(a)    ? launch_stream_rho<SMode::Down, kFp8Wide>(a, rho, stream)
-                            : launch_stream_rho<SMode::Down, kDtypeFp8>(a, rho, stream);
+    return fp8_wide(a) ? launch_stream_rho<SMode::Down, kFp8Wide>(a, rho, stream)
+                       : launch_stream_rho<SMode::Down, kDtypeFp8>(a, rho, stream);
   return launch_stream_rho<SMode::Down, kDtypeBf16>(a, rho, stream);
 }
 

@@ -98,12 +98,12 @@ def test_fp8_small_ragged(T):
     _run(_SMALL_FP8, T, W.base_seed(0, T) + 11)
 
 
-# fp8 gate/up in four-group stages (H a multiple of 512): 32 x 64 tiles at 16 rows
-# per expert, 64 x 64 at 25, ragged in both.
+# fp8 gate/up in four-group stages (H a multiple of 512): 16 x 128 tiles at 6 rows
+# per expert, 32 x 64 at 16, 64 x 64 at 25, ragged in all three.
 _SMALL_FP8_QUAD = W.LayerShape("small_fp8_quad", 1024, 8, 512, 2, 512, W.DT_FP8, W.DT_BF16)
 
 
-@pytest.mark.parametrize("T", [64, 100])
+@pytest.mark.parametrize("T", [24, 64, 100])
 def test_fp8_quad_stages_ragged(T):
     _run(_SMALL_FP8_QUAD, T, W.base_seed(0, T) + 17)
 

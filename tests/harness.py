@@ -130,14 +130,16 @@ def run_gpu(case: Case, layer=None) -> Dict[str, np.ndarray]:
                              case.shared, max_tokens=max(T, 1), stats=True)
     x = case.inp.x.cuda()
     bias = None if case.inp.logit_bias is None else case.inp.logit_bias.cuda()
-    layer.route_stats.fill_(-7)
+    if layer.route_stats is not None:
+        layer.route_stats.fill_(-7)
     y = layer(x, bias)
     torch.cuda.synchronize()
     v = layer.views(T)
     nkept = int(layer.offsets[-1].item())
     return {
         "ids": v["topk_ids"].cpu().numpy(), "w": v["topk_weights"].cpu().numpy(),
-        "shared_gate": v["shared_gate"].cpu().numpy(), "stats": layer.route_stats.cpu().numpy(),
+        "shared_gate": v["shared_gate"].cpu().numpy(),
+        "stats": None if layer.route_stats is None else layer.route_stats.cpu().numpy(),
         "counts": layer.counts.cpu().numpy(), "offsets": layer.offsets.cpu().numpy(),
         "perm": v["perm"][:nkept].cpu().numpy(), "y": y.cpu().numpy().astype(np.float64),
     }

@@ -223,6 +223,23 @@ def test_fp8_small_budget_drops_experts():
     assert errs["y_rel_l2"] < 1e-3
 
 
+def test_budget_without_statistics_routes_the_same():
+    """MoELayer asks for no routing statistics by default: the budget pass then runs
+    with a null statistics pointer and must route and compute exactly as with one."""
+    import mixture_experts_layer_05_amd as moe
+    shape = W.LayerShape("small_budget", 512, 16, 256, 4, 256, W.DT_FP8, W.DT_BF16, expert_budget=6)
+    print(f"\n[case] {shape.name} budget without statistics", flush=True)
+    case = Hn.make_case(shape, 96, W.base_seed(5, 96), 1.5)
+    with_stats = Hn.run_gpu(case)
+    assert with_stats["stats"][0] > 6 and with_stats["stats"][1] == 6
+    layer = moe.MoELayer(Hn.config(shape), case.weights, case.inp.w_router.cuda(),
+                         case.inp.w_shared_gate.cuda(), case.shared, max_tokens=96)
+    assert layer.route_stats is None
+    plain = Hn.run_gpu(case, layer)
+    for k in ("ids", "w", "counts", "offsets", "perm", "y"):
+        assert np.array_equal(plain[k], with_stats[k]), k
+
+
 # ----------------------------------------------------------------------------- edge cases
 
 EDGE = W.LayerShape("edge_k_eq_e", 256, 4, 256, 4, 128, W.DT_BF16, W.DT_BF16)

@@ -364,7 +364,17 @@ def test_halves_equal_forward():
     assert Hn.rel_l2(layer.views(56)["y"].cpu().numpy(), y1.cpu().numpy()) < 1e-6
 
 
-@pytest.mark.parametrize("shape,T", [(W.DRAFTER, 56), (W.TINY, 40)])
+# fp32 with H, I, S not multiples of 4: the combine pass adds and stores element by
+# element.
+_TINY_ODD = W.TINY.with_(name="tiny_fp32_odd", hidden_size=250, moe_intermediate_size=100,
+                         shared_expert_intermediate_size=60)
+
+
+def test_fp32_layer_with_odd_widths():
+    _run(_TINY_ODD, 40, W.base_seed(0, 40) + 23)
+
+
+@pytest.mark.parametrize("shape,T", [(W.DRAFTER, 56), (W.TINY, 40), (_TINY_ODD, 40)])
 @pytest.mark.parametrize("element_aligned", [False, True])
 def test_activation_dtype_output(shape, T, element_aligned):
     """The optional y_act output: the cast of the float32 y to the activation dtype.

@@ -109,34 +109,35 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     float* yr = y + static_cast<size_t>(t) * H;
     const size_t row = static_cast<size_t>(t) * H;
     if ((H & 3) == 0) {
-      const int c = c0 / 4 + static_cast<int>(threadIdx.x);
-      if (4 * c >= H) continue;
-      float4 s = accumulate ? reinterpret_cast<const float4*>(yr)[c] : float4{0.f, 0.f, 0.f, 0.f};
-      for (int k = 0; k < K; ++k) {
-        const float w = wr[k];
-        if (w == 0.f) continue;
-        const float4 v = reinterpret_cast<const float4*>(orow + static_cast<size_t>(k) * H)[c];
-        s.x = fmaf(w, v.x, s.x);
-        s.y = fmaf(w, v.y, s.y);
-        s.z = fmaf(w, v.z, s.z);
-        s.w = fmaf(w, v.w, s.w);
-      }
-      reinterpret_cast<float4*>(yr)[c] = s;
-      if (y_act) {
-        // bf16: round to nearest (ties to even).  Four values per store when y_act
-        // is aligned for it (it need only be aligned to its element size).
-        if (!act_vec) {
-          const float v[4] = {s.x, s.y, s.z, s.w};
-          for (int e = 0; e < 4; ++e) {
-            if (act_bf16) static_cast<uint16_t*>(y_act)[row + 4 * c + e] = f32_to_bf16_bits(v[e]);
-            else static_cast<float*>(y_act)[row + 4 * c + e] = v[e];
+      const int cend = min(H, c0 + kCombineCols) / 4;
+      for (int c = c0 / 4 + static_cast<int>(threadIdx.x); c < cend; c += blockDim.x) {
+        float4 s = accumulate ? reinterpret_cast<const float4*>(yr)[c] : float4{0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < K; ++k) {
+          const float w = wr[k];
+          if (w == 0.f) continue;
+          const float4 v = reinterpret_cast<const float4*>(orow + static_cast<size_t>(k) * H)[c];
+          s.x = fmaf(w, v.x, s.x);
+          s.y = fmaf(w, v.y, s.y);
+          s.z = fmaf(w, v.z, s.z);
+          s.w = fmaf(w, v.w, s.w);
+        }
+        reinterpret_cast<float4*>(yr)[c] = s;
+        if (y_act) {
+          // bf16: round to nearest (ties to even).  Four values per store when y_act
+          // is aligned for it (it need only be aligned to its element size).
+          if (!act_vec) {
+            const float v[4] = {s.x, s.y, s.z, s.w};
+            for (int e = 0; e < 4; ++e) {
+              if (act_bf16) static_cast<uint16_t*>(y_act)[row + 4 * c + e] = f32_to_bf16_bits(v[e]);
+              else static_cast<float*>(y_act)[row + 4 * c + e] = v[e];
+            }
+          } else if (act_bf16) {
+            const uint32_t lo = f32_to_bf16_bits(s.x) | (static_cast<uint32_t>(f32_to_bf16_bits(s.y)) << 16);
+            const uint32_t hi = f32_to_bf16_bits(s.z) | (static_cast<uint32_t>(f32_to_bf16_bits(s.w)) << 16);
+            reinterpret_cast<uint2*>(static_cast<uint16_t*>(y_act) + row)[c] = uint2{lo, hi};
+          } else {
+            reinterpret_cast<float4*>(static_cast<float*>(y_act) + row)[c] = s;
           }
-        } else if (act_bf16) {
-          const uint32_t lo = f32_to_bf16_bits(s.x) | (static_cast<uint32_t>(f32_to_bf16_bits(s.y)) << 16);
-          const uint32_t hi = f32_to_bf16_bits(s.z) | (static_cast<uint32_t>(f32_to_bf16_bits(s.w)) << 16);
-          reinterpret_cast<uint2*>(static_cast<uint16_t*>(y_act) + row)[c] = uint2{lo, hi};
-        } else {
-          reinterpret_cast<float4*>(static_cast<float*>(y_act) + row)[c] = s;
         }
       }
     } else {

@@ -32,9 +32,16 @@ What it computes, step by step, each from the page that defines it:
    decoded code * 2^(e - 127); the activations entering their contractions are
    quantised per row and 32-block to MXFP8 (see oracle.mx.quantise_mxfp8).
 
+8. Diagnostic variant (not the parity reference): h rounded to bfloat16
+   (nearest, ties to even, straight from float64) before the down contraction,
+   which is what a kernel that stores h in bf16 consumes.  It separates kernel
+   errors from the bf16 rounding of h, which alone moves y by ~1.7e-3 relative L2.
+   For fp8 / MXFP4 weights a "plain" variant leaves the activations unquantised
+   (dequantised weights only), to report the format's own error apart.
+
 Readings where the pages are silent (all listed in the design notes):
   * top-k selection is decided on float32 logits, ties to the lower expert id;
-    the k ids are stored by descending weight;
+    a NaN logit counts as -inf; the k ids are stored by descending weight;
   * the budget ranks experts by (aggregate weight desc, id asc), triggers only
     when the union exceeds B (B = 0 is off), compacts kept slots to the front
     and marks dropped slots id -1 / weight 0; a token that loses every slot is
@@ -64,13 +71,26 @@ from . import mx
 
 def as_f64(a) -> np.ndarray:
     """Any numeric array (numpy or a CPU torch tensor, incl. bfloat16) -> float64."""
-    if hasattr(a, "detach"):  # torch tensor; bf16 -> fp32 is exact
+    if hasattr(a, "detach"):  # torch tensor; bf16 / fp16 / fp32 -> float64 is exact
         import torch
-        t = a.detach().cpu()
-        if t.dtype in (torch.bfloat16, torch.float16):
-            t = t.to(torch.float32)
-        return t.numpy().astype(np.float64)
+        return a.detach().cpu().to(torch.float64).numpy()
     return np.asarray(a, dtype=np.float64)
+
+
+def round_bf16(v) -> np.ndarray:
+    """float64 -> nearest bfloat16 value (8 significant bits, ties to even), as float64.
+
+    Rounds straight from float64 (no intermediate float32 step, which could round
+    twice).  bf16 shares float32's exponent range: below 2^-126 the spacing is
+    2^-133 (subnormals); results of magnitude 2^128 or more are infinite.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)                                   # v = m * 2^e, 0.5 <= |m| < 1
+    q = np.maximum(e - 8, -133)                          # exponent of one unit in the last place
+    r = np.ldexp(np.rint(np.ldexp(v, -q)), q)           # np.rint rounds half to even
+    with np.errstate(invalid="ignore"):
+        r = np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, v), r)
+    return np.where(np.isfinite(v), r, v)
 
 
 def silu(a: np.ndarray) -> np.ndarray:
@@ -107,7 +127,7 @@ def topk_softmax(z: np.ndarray, K: int, norm_topk: bool = True):
     expert id; ids are listed by descending logit.  Returns ids int32 [T, K],
     weights float64 [T, K].
     """
-    z = np.asarray(z, dtype=np.float64)
+    z = np.where(np.isnan(z), -np.inf, np.asarray(z, dtype=np.float64))
     T, E = z.shape
     z32 = z.astype(np.float32)
     ids = np.empty((T, K), dtype=np.int32)
@@ -262,49 +282,77 @@ def _mx_activation(v: np.ndarray) -> np.ndarray:
     return mx.dequant_mxfp8(*mx.quantise_mxfp8(v.astype(np.float32)))
 
 
-def swiglu_ffn(xrows: np.ndarray, wdict: Dict, weight_dtype: str) -> np.ndarray:
+# Output variants of the expert math: name -> (quantise activations, round h to bf16).
+#   "model":  the parity reference: activations quantised as the fp8 / MXFP4
+#             contractions consume them (no-op for f32 / bf16 weights);
+#   "bf16_h": the diagnostic of step 8, h rounded to bf16 before down;
+#   "plain":  activations left unquantised (dequantised weights only).
+VARIANTS = {"model": (True, False), "bf16_h": (False, True), "plain": (False, False)}
+
+
+def swiglu_ffn(xrows: np.ndarray, wdict: Dict, weight_dtype: str, quantise_acts: bool = True,
+               h_bf16: bool = False, weights=None) -> np.ndarray:
     """down(silu(gate x) * (up x)) for each row of xrows (float64).
 
     With fp8 weights the rows of x and of h are quantised per 128-group before
     they enter the contraction, matching what an fp8 x fp8 contraction consumes;
     with MXFP4 weights they are quantised to MXFP8 (32-element blocks, E8M0
     scales), what the block-scaled fp8 x fp4 contraction consumes.
+    quantise_acts=False skips that (the plain layer of the dequantised weights);
+    h_bf16 rounds h to bfloat16 before down.  `weights`: the float64 (gate, up,
+    down) of wdict if already decoded.
     """
-    wg, wu, wd = _weights_f64(wdict, weight_dtype)
+    wg, wu, wd = weights if weights is not None else _weights_f64(wdict, weight_dtype)
     quant = {"fp8_e4m3_g128": _fp8_activation, "mxfp4": _mx_activation}.get(weight_dtype)
+    if not quantise_acts:
+        quant = None
     xa = quant(xrows) if quant else xrows
     a = xa @ wg.T
     b = xa @ wu.T
     h = silu(a) * b
     if quant:
         h = quant(h.astype(np.float32))
+    if h_bf16:
+        h = round_bf16(h)
     return h @ wd.T
 
 
 def moe_combine(x, ids, w, shared_gate: Optional[np.ndarray],
                 expert: Callable[[int], Dict], shared: Optional[Dict],
-                weight_dtype: str, tokens: Optional[Sequence[int]] = None) -> np.ndarray:
+                weight_dtype: str, tokens: Optional[Sequence[int]] = None,
+                variants: Optional[Sequence[str]] = None):
     """y for the given tokens (all by default): sum over each token's kept slots of
     w * expert_e(x_t), plus sigmoid(g_t) * shared(x_t).
 
     `expert(e)` returns routed expert e's weight dict; `shared_gate` holds
     sigmoid(g) per token.  Experts are visited one at a time so the full weight set
-    never has to sit in host memory.
+    never has to sit in host memory.  Returns the "model" variant's y, or, if
+    `variants` names several of VARIANTS, a dict of y per variant (each expert's
+    weights decoded once for all of them).
     """
+    names = ["model"] if variants is None else list(variants)
     x64 = as_f64(x)
     ids = np.asarray(ids)
     w = np.asarray(w, dtype=np.float64)
     toks = np.arange(x64.shape[0]) if tokens is None else np.asarray(tokens, dtype=np.int64)
-    y = np.zeros((len(toks), x64.shape[1]), dtype=np.float64)
+    ys = {n: np.zeros((len(toks), x64.shape[1]), dtype=np.float64) for n in names}
     sub_ids = ids[toks]
     sub_w = w[toks]
     for e in sorted({int(v) for v in sub_ids.ravel() if v >= 0}):
         rows, ks = np.nonzero(sub_ids == e)
-        out = swiglu_ffn(x64[toks[rows]], expert(e), weight_dtype)
-        y[rows] += sub_w[rows, ks][:, None] * out
+        wdict = expert(e)
+        wts = _weights_f64(wdict, weight_dtype)
+        for n in names:
+            q, hb = VARIANTS[n]
+            out = swiglu_ffn(x64[toks[rows]], wdict, weight_dtype, q, hb, wts)
+            ys[n][rows] += sub_w[rows, ks][:, None] * out
     if shared is not None:
-        y += np.asarray(shared_gate, dtype=np.float64)[toks][:, None] * swiglu_ffn(x64[toks], shared, weight_dtype)
-    return y
+        wts = _weights_f64(shared, weight_dtype)
+        sg = np.asarray(shared_gate, dtype=np.float64)[toks][:, None]
+        for n in names:
+            q, hb = VARIANTS[n]
+            ys[n] += sg * swiglu_ffn(x64[toks], shared, weight_dtype, q, hb, wts)
+    return ys["model"] if variants is None else ys
 
 
 # ----------------------------------------------------------------------------- whole layer
@@ -323,10 +371,15 @@ def route(x, w_router, w_shared_gate, logit_bias, K: int, norm_topk: bool = True
 
 def moe_layer(x, w_router, w_shared_gate, logit_bias, K: int, E: int,
               expert: Callable[[int], Dict], shared: Optional[Dict], weight_dtype: str,
-              norm_topk: bool = True, budget: int = 0, tokens=None, top_p: float = 0.0) -> Dict:
-    """The whole forward: route, dispatch, y (for `tokens`, default all)."""
+              norm_topk: bool = True, budget: int = 0, tokens=None, top_p: float = 0.0,
+              variants: Optional[Sequence[str]] = None) -> Dict:
+    """The whole forward: route, dispatch, y (for `tokens`, default all).  With
+    `variants`, also y_<name> for each named output variant (y is "model")."""
     r = route(x, w_router, w_shared_gate, logit_bias, K, norm_topk, budget, top_p)
     counts, offsets, perm = dispatch(r["ids"], E)
-    y = moe_combine(x, r["ids"], r["w"], r["shared_gate"], expert, shared, weight_dtype, tokens)
-    r.update(counts=counts, offsets=offsets, perm=perm, y=y)
+    names = ["model"] + [n for n in (variants or []) if n != "model"]
+    ys = moe_combine(x, r["ids"], r["w"], r["shared_gate"], expert, shared, weight_dtype, tokens, names)
+    r.update(counts=counts, offsets=offsets, perm=perm, y=ys["model"])
+    for n in names[1:]:
+        r["y_" + n] = ys[n]
     return r

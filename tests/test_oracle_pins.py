@@ -469,3 +469,137 @@ def test_fp8_swiglu_matches_torch_float8_pipeline():
     h = torch.nn.functional.silu(a) * b
     ref = tq(h.to(torch.float32)) @ tw("down").T
     assert np.allclose(mine, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- router bias, NaN logits
+
+def test_logit_bias_is_added_to_the_logits():
+    """A one-hot bias of +20 on expert e must make e the first pick of that token
+    (a subtracted bias would make it the last), and a -inf bias masks an expert."""
+    rng = np.random.default_rng(30)
+    T, H, E, K = 12, 16, 8, 2
+    x = rng.normal(size=(T, H))
+    wr = rng.normal(scale=0.1, size=(E, H))
+    target = rng.integers(0, E, size=T)
+    bias = np.zeros((T, E))
+    bias[np.arange(T), target] = 20.0
+    r = O.route(x, wr, None, bias, K)
+    assert np.array_equal(r["ids"][:, 0], target)
+    assert np.allclose(r["logits"] - x @ wr.T, bias)
+    masked = np.zeros((T, E))
+    masked[:, 0] = -np.inf
+    r0 = O.route(x, wr, None, None, K)
+    r1 = O.route(x, wr, None, masked, K)
+    assert not (r1["ids"] == 0).any()
+    keep = (r0["ids"] != 0).all(axis=1)        # tokens whose picks never included expert 0
+    assert np.array_equal(r1["ids"][keep], r0["ids"][keep])
+
+
+def test_nan_logits_count_as_minus_infinity():
+    rng = np.random.default_rng(31)
+    z = rng.normal(size=(20, 10))
+    z[:, [1, 4, 7]] = np.nan
+    z[3, :] = np.nan
+    z[3, 5] = 0.5                               # one finite expert: the other picks follow by id
+    ref = np.where(np.isnan(z), -np.inf, z)
+    for K in (2, 8):
+        a = O.topk_softmax(z, K)
+        b = O.topk_softmax(ref, K)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    ids, w = O.topk_softmax(z, 3)
+    assert ids[3].tolist() == [5, 0, 1] and w[3].tolist() == [1.0, 0.0, 0.0]
+    # brute force on the finite experts: the picks maximise the summed finite logits first
+    for t in range(20):
+        if t == 3:
+            continue
+        fin = [e for e in range(10) if not np.isnan(z[t, e])]
+        best = max(itertools.combinations(fin, 2), key=lambda c: sum(z[t, list(c)]))
+        assert set(O.topk_softmax(z[t:t + 1], 2)[0][0].tolist()) == set(best)
+
+
+# ----------------------------------------------------------------------------- bf16 rounding, output variants
+
+def test_round_bf16_matches_torch_on_float32_inputs():
+    rng = np.random.default_rng(32)
+    v = np.concatenate([
+        rng.normal(scale=0.05, size=200_000),
+        np.exp2(rng.uniform(-140, 127.9, 100_000)) * rng.choice([-1, 1], 100_000),
+        [0.0, -0.0, 1.0, 3.3895313892515355e38, 3.4e38, -3.4e38, 1e-45, 2.0 ** -126, 2.0 ** -133],
+    ]).astype(np.float32)
+    # exact ties between neighbouring bf16 values: bf16 bits b and b+1 share the top 16 bits of a float32
+    bits = rng.integers(0, 0x7F7F, size=50_000, dtype=np.uint32)
+    ties = ((bits << 16) | 0x8000).view(np.float32)
+    v = np.concatenate([v, ties, -ties])
+    mine = O.round_bf16(v.astype(np.float64))
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(mine, ref)
+
+
+def test_round_bf16_rounds_float64_once():
+    # 1 + 2^-8 is the midpoint of bf16 1 and 1 + 2^-7; a hair above it must round up.
+    # Rounding to float32 first (spacing 2^-23) would land on the midpoint and tie to 1.
+    assert O.round_bf16(1.0 + 2.0 ** -8 + 2.0 ** -40) == 1.0 + 2.0 ** -7
+    assert O.round_bf16(1.0 + 2.0 ** -8 - 2.0 ** -40) == 1.0
+    assert O.round_bf16(1.0 + 2.0 ** -8) == 1.0                      # tie to even
+    assert O.round_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2 * 2.0 ** -7  # tie to even (up)
+    assert np.isinf(O.round_bf16(3.4e38)) and O.round_bf16(np.inf) == np.inf
+    assert np.isnan(O.round_bf16(np.nan))
+
+
+def test_bf16_h_variant_rounds_h_before_down():
+    """The diagnostic variant equals torch's pipeline: h = silu(a) * b in float64,
+    cast to bfloat16 (through float32, checked to be away from any bf16 tie so that
+    the two roundings agree), then the down contraction in float64."""
+    rng, experts, shared = _tiny_layer(E=3, H=32, I=24, S=16, seed=33)
+    T = 10
+    x = rng.normal(size=(T, 32))
+    wr = rng.normal(size=(3, 32))
+    wgate = rng.normal(size=32)
+    r = O.moe_layer(x, wr, wgate, None, 2, 3, lambda e: experts[e], shared, "f32",
+                    variants=["bf16_h", "plain"])
+    assert np.array_equal(r["y_plain"], r["y"])      # no activation quantisation with f32 weights
+
+    def torch_ffn(xr, wdict):
+        xt = torch.as_tensor(xr)
+        h = torch.nn.functional.silu(xt @ torch.as_tensor(wdict["gate"]).T) * (xt @ torch.as_tensor(wdict["up"]).T)
+        h32 = h.to(torch.float32)
+        # away from ties: h lies closer to its bf16 value than the float32 step can
+        # move it (half a bf16 step is 2^(e-9) for h = m 2^e, 0.5 <= |m| < 1)
+        hn = h.numpy()
+        half = np.ldexp(1.0, np.frexp(hn)[1] - 9)
+        to_mid = half - np.abs(hn - h.to(torch.bfloat16).to(torch.float64).numpy())
+        assert (np.abs(hn - h32.to(torch.float64).numpy()) < to_mid).all()
+        return (h32.to(torch.bfloat16).to(torch.float64) @ torch.as_tensor(wdict["down"]).T).numpy()
+
+    expect = np.zeros((T, 32))
+    for t in range(T):
+        for k in range(2):
+            e = int(r["ids"][t, k])
+            expect[t] += r["w"][t, k] * torch_ffn(x[t:t + 1], experts[e])[0]
+    expect += r["shared_gate"][:, None] * torch_ffn(x, shared)
+    assert np.allclose(r["y_bf16_h"], expect, rtol=1e-12, atol=1e-13)
+    # bf16 h moves y by about the bf16 step (2^-9 relative per element of h)
+    rel = np.linalg.norm(r["y_bf16_h"] - r["y"]) / np.linalg.norm(r["y"])
+    assert 1e-4 < rel < 2.0 ** -8
+
+
+def test_plain_variant_leaves_fp8_activations_unquantised():
+    """fp8 weights: "plain" is the layer of the dequantised weights (torch float8
+    decode) on unquantised activations; "model" quantises x and h as well."""
+    shape = W.LARGE_FP8.with_(hidden_size=256, moe_intermediate_size=256)
+    wd = W.expert_weights(shape, 4, 0)
+    x = torch.randn(5, 256, generator=torch.Generator().manual_seed(4)).to(torch.bfloat16)
+
+    def tw(name):
+        q = wd[name].view(torch.float8_e4m3fn).to(torch.float64)
+        s = wd[name + "_s"].to(torch.float64)
+        return (q.reshape(q.shape[0], -1, 128) * s[:, :, None]).reshape(q.shape)
+
+    xt = x.to(torch.float64)
+    h = torch.nn.functional.silu(xt @ tw("gate").T) * (xt @ tw("up").T)
+    ref = (h @ tw("down").T).numpy()
+    plain = O.swiglu_ffn(O.as_f64(x), wd, "fp8_e4m3_g128", quantise_acts=False)
+    model = O.swiglu_ffn(O.as_f64(x), wd, "fp8_e4m3_g128")
+    assert np.allclose(plain, ref, rtol=1e-12, atol=1e-14)
+    rel = np.linalg.norm(model - plain) / np.linalg.norm(plain)
+    assert 5e-3 < rel < 0.1        # the activation quantisation error, a few percent

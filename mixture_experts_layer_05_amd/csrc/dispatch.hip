@@ -9,6 +9,9 @@
 
 namespace moe {
 
+// Slots whose id lies outside [0, E) (-1: dropped by the budget or the top-p
+// trim) are skipped by every kernel here.
+//
 // One workgroup of 1024 threads (16 waves).
 //  1. counts[e] via LDS atomics over all slots.
 //  2. Exclusive scan of counts in LDS -> offsets[0..E].
@@ -33,7 +36,7 @@ __global__ void __launch_bounds__(1024) dispatch_kernel(
   const int nslots = T * K;
   for (int s = tid; s < nslots; s += 1024) {
     const int e = ids[s];
-    if (e >= 0) atomicAdd(&cnt[e], 1);
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
   }
   __syncthreads();
 
@@ -64,7 +67,7 @@ __global__ void __launch_bounds__(1024) dispatch_kernel(
     if (live) {
       for (int k = 0; k < K; ++k) {
         const int e = row[k];
-        if (e >= 0) atomicOr(&mask[wave][e], 1ull << lane);
+        if (e >= 0 && e < E) atomicOr(&mask[wave][e], 1ull << lane);
       }
     }
     __syncthreads();
@@ -72,7 +75,7 @@ __global__ void __launch_bounds__(1024) dispatch_kernel(
       const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
       for (int k = 0; k < K; ++k) {
         const int e = row[k];
-        if (e < 0) continue;
+        if (e < 0 || e >= E) continue;
         int rank = cursor[e] + __popcll(mask[wave][e] & below);
         for (int q = 0; q < wave; ++q) rank += __popcll(mask[q][e]);
         perm[rank] = t * K + k;

@@ -100,7 +100,9 @@ __global__ void __launch_bounds__(256) router_logits_f32_kernel(
 //
 // One wave per token.  Lane l holds experts l, l+64, ... (up to 8 each).  K rounds
 // of a wave-wide argmax on (logit desc, id asc) pick the ids in descending
-// order.  Weights: exp(z_k - z_max) over the K picks, divided by their sum
+// order.  A NaN logit counts as -inf; a picked expert is marked taken (a per-lane
+// bit mask) and leaves the candidates, so even -inf logits (experts masked through
+// the bias) are picked at most once and every id lies in [0, E).  Weights: exp(z_k - z_max) over the K picks, divided by their sum
 // (renormalised top-k) or by the sum over all E experts (plain softmax).
 // top_p in (0, 1): pick k survives iff the picks before it hold less than top_p
 // of the K picks' summed weight (so pick 0 always survives); the others become
@@ -130,6 +132,7 @@ __global__ void __launch_bounds__(256) topk_kernel(
     if (e < E) {
       val = logit(e);
       if (bias) val += bias[static_cast<size_t>(t) * E + e];
+      if (val != val) val = -INFINITY;   // NaN
     }
     v[j] = val;
   }
@@ -147,14 +150,16 @@ __global__ void __launch_bounds__(256) topk_kernel(
   }
   int my_id = -1;
   float my_z = 0.f;
+  unsigned taken = 0;   // bit j: expert lane + 64 j already picked
   for (int k = 0; k < K; ++k) {
-    // Lane-local best: largest value, lowest id on ties (ids grow with j).
+    // Lane-local best among the untaken: largest value, lowest id on ties (ids
+    // grow with j).  be = 0x7fffffff marks a lane with no candidate left.
     float bv = -INFINITY;
     int be = 0x7fffffff;
 #pragma unroll
     for (int j = 0; j < kMaxExperts / kWave; ++j) {
       const int e = lane + kWave * j;
-      if (e < E && (v[j] > bv || (v[j] == bv && e < be))) { bv = v[j]; be = e; }
+      if (e < E && !((taken >> j) & 1u) && (v[j] > bv || (v[j] == bv && e < be))) { bv = v[j]; be = e; }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -162,11 +167,8 @@ __global__ void __launch_bounds__(256) topk_kernel(
       const int oe = __shfl_xor(be, o, kWave);
       if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
     }
-    if ((be & 63) == lane) {
-#pragma unroll
-      for (int j = 0; j < kMaxExperts / kWave; ++j)
-        if (j == (be >> 6)) v[j] = -INFINITY;
-    }
+    // K <= E, so some lane still had a candidate and be is a valid id.
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
     if (lane == k) { my_id = be; my_z = bv; }
   }
   // The first pick is the maximum logit.

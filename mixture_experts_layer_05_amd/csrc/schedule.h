@@ -153,9 +153,16 @@ struct XcdWalk {
   }
 };
 
+// A dispatch entry clamped into [0, T*K): every slot index the kernels derive an
+// address from stays inside its buffer, whatever perm holds (the dispatch leaves
+// entries unwritten only for invalid ids, which the header rules out).
+__device__ __forceinline__ int slot_clamp(int s, const ExpertArgs& a) {
+  return static_cast<int>(min(static_cast<unsigned>(s), static_cast<unsigned>(a.T * a.K - 1)));
+}
+
 // Token behind row m of a tile (m clamped into the group by the caller).
 __device__ __forceinline__ int row_token(const ExpertArgs& a, const TileInfo& t, int m) {
-  return t.shared ? m : a.perm[t.rowbase + m] / a.K;
+  return t.shared ? m : slot_clamp(a.perm[t.rowbase + m], a) / a.K;
 }
 
 // Destination of row m of a down-projection tile: routed rows go, unweighted, to
@@ -167,7 +174,7 @@ struct DownDst {
 
 __device__ __forceinline__ DownDst down_row(const ExpertArgs& a, const TileInfo& t, int m) {
   if (t.shared) return {a.y + static_cast<size_t>(m) * a.H, a.shared_gate[m]};
-  return {a.o + static_cast<size_t>(a.perm[t.rowbase + m]) * a.H, 1.0f};
+  return {a.o + static_cast<size_t>(slot_clamp(a.perm[t.rowbase + m], a)) * a.H, 1.0f};
 }
 
 }  // namespace

@@ -330,9 +330,9 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
 #pragma unroll
         for (int q = 0; q < C::kAPasses; ++q) {
           const int mc = min(t.m0 + lrow + q * C::kRowsPerPassA, t.rows - 1);
-          p.pv[q] = a.perm[base + mc];
+          p.pv[q] = t.shared ? a.perm[base + mc] : slot_clamp(a.perm[base + mc], a);
         }
-        if constexpr (FP8) p.ps = a.perm[base + min(t.m0 + min(tid, BM - 1), t.rows - 1)];
+        if constexpr (FP8) p.ps = slot_clamp(a.perm[base + min(t.m0 + min(tid, BM - 1), t.rows - 1)], a);
       }
       return p;
     };
@@ -647,7 +647,7 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int mc = min(t.m0 + wrow0 + 16 * i + 4 * g + e, t.rows - 1);
-            dslot[i][e] = a.perm[base + mc];
+            dslot[i][e] = t.shared ? a.perm[base + mc] : slot_clamp(a.perm[base + mc], a);
             dgate[i][e] = has_shared ? a.shared_gate[min(mc, a.T - 1)] : 1.0f;
           }
       }

@@ -31,6 +31,19 @@
  *   - T = 0 is valid: moe_route and moe_forward* then return MOE_OK without
  *     reading any pointer but cfg and enqueue nothing; moe_dispatch writes zero
  *     counts and offsets (topk_ids and perm may be NULL).
+ *   - Tile override, for benchmarks and tests only: the environment variable
+ *     MOE_FORCE_TILE, read on every moe_forward / moe_forward_gate_up /
+ *     moe_forward_down call (nothing is cached), forces the expert kernels' tile
+ *     family.  Unset, empty or "auto": the per-call choice from the rows per expert
+ *     (the small-M / large-M family choice of [DeepGEMM fork PR #5, "Dynamic
+ *     family selection"]).  "stream16", "stream32", "stream64", "stream128": the
+ *     weight-streaming kernel alone with tiles of that many token rows.  "split":
+ *     the rows divided by the realised counts between the 256-row LDS-tiled kernel
+ *     and the streaming kernel (BF16 and FP8 weights only).  Any other value, or a
+ *     value the configuration cannot use (F32 weights; "split" with MXFP4
+ *     weights), returns MOE_ERR_BAD_SHAPE before anything is launched, as invalid
+ *     overrides fail loudly in [DeepGEMM PR #381, "Forced-wave calibration"].
+ *     Every setting computes the same y up to float32 summation order.
  *   - Supported dtype combinations (weight_dtype / act_dtype):
  *       F32 / F32, BF16 / BF16, FP8_E4M3_G128 / BF16, MXFP4 / BF16.
  *     With BF16 or FP8 weights, hidden_size, moe_intermediate_size and
@@ -139,7 +152,12 @@ int moe_workspace_size(const moe_config* cfg, int32_t max_tokens, size_t* bytes)
  *   x            (device) [T, H] act_dtype
  *   w_router     (device) [E, H] act_dtype
  *   w_shared_gate(device) [H] act_dtype; required iff S > 0, else ignored
- *   logit_bias   (device) [T, E] float32 or NULL (added to the logits)
+ *   logit_bias   (device) [T, E] float32 or NULL (added to the logits).  An entry
+ *                may be -inf to mask an expert for a token; a NaN logit counts as
+ *                -inf.  Masked experts are still picked (after every finite one,
+ *                lower id first) when fewer than K are finite, each at most once,
+ *                with weight 0; a token whose logits are all -inf gets NaN weights.
+ *                +inf is not allowed (its weights would be NaN).
  *   topk_ids     (device) out [T, K] int32, by descending weight; dropped slots
  *                are moved to the end of their row as id -1
  *   topk_weights (device) out [T, K] float32; 0 for dropped slots
@@ -155,21 +173,33 @@ int moe_route(const moe_config* cfg, int32_t num_tokens, const void* x, const vo
               float* topk_weights, float* shared_gate, int32_t* route_stats, void* workspace,
               size_t workspace_bytes, void* stream);
 
-/* Dispatch: expert_counts[e] = number of slots with id e (ids < 0 are skipped);
+/* Dispatch: the token-to-expert grouping that a grouped GEMM over
+ * expert-contiguous rows consumes ([SpecForge PR #943, "Modifications": grouped_mm
+ * dispatch]; the per-expert counts are the received-token counters of [DeepGEMM
+ * PR #381, description]).  expert_counts[e] = number of slots with id e;
  * expert_offsets = exclusive prefix sum of counts (E+1 entries, last = kept
  * slots); perm[offsets[e] + j] = t*K + k for the j-th token (ascending t) routed
- * to e.  Entries of perm past offsets[E] are left untouched.
- *   topk_ids (device) [T, K] int32 in [-1, E)
+ * to e.  Slots whose id lies outside [0, E) (-1: dropped) are skipped.  The ids of
+ * one token must be distinct (moe_route guarantees it); with a repeated id some
+ * entries of perm below offsets[E] stay unwritten.  Entries of perm past
+ * offsets[E] are left untouched.
+ *   topk_ids (device) [T, K] int32
  *   expert_counts (device) out [E], expert_offsets (device) out [E+1],
  *   perm (device) out [T*K] int32 */
 int moe_dispatch(const moe_config* cfg, int32_t num_tokens, const int32_t* topk_ids,
                  int32_t* expert_counts, int32_t* expert_offsets, int32_t* perm, void* workspace,
                  size_t workspace_bytes, void* stream);
 
-/* Experts and combine:
+/* Experts and combine: the routed SwiGLU experts weighted by the renormalised
+ * top-k gates, plus the sigmoid-gated shared expert [SpecForge PR #943,
+ * "Modifications": shared expert (2048, sigmoid-gated), softmax renormalised
+ * top-k; the expert FFN shape of its parameter counts, 3 * H * I per expert]:
  *   y[t,:] = sum_k topk_weights[t,k] * down_e(silu(gate_e x_t) * up_e x_t)
  *          + shared_gate[t] * down_s(silu(gate_s x_t) * up_s x_t)
- * with e = topk_ids[t,k], taken through the dispatch outputs.  y (device) out
+ * with e = topk_ids[t,k], taken through the dispatch outputs.  A slot that the
+ * dispatch skipped (id -1, or outside [0, E)) must have topk_weights 0, as
+ * moe_route writes it: its row of the per-slot outputs is never computed, and a
+ * non-zero weight would add that row's stale contents to y.  y (device) out
  * [T, H] float32, 16-byte aligned, overwritten.  The intermediate activations
  * are stored in the workspace as bf16 (BF16 weights), float32 (F32), e4m3 +
  * group-128 scales (FP8) or MXFP8 codes + E8M0 block-32 scales (MXFP4; x is

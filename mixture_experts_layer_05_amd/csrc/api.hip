@@ -2,6 +2,8 @@
 // Everything is enqueued on the caller's stream; nothing is allocated, nothing is
 // read back to the host.
 #include <algorithm>
+#include <cstdlib>
+#include <cstring>
 
 #include "moe_mi355x.h"
 #include "kernels.h"
@@ -127,12 +129,37 @@ int check_act_output(const moe_config& c, const void* y_act) {
   return (y_act && reinterpret_cast<uintptr_t>(y_act) % size != 0) ? MOE_ERR_UNSUPPORTED : MOE_OK;
 }
 
+// The tile override of the header's conventions: MOE_FORCE_TILE, read on every
+// call.  Writes the kernels' setting (ExpertArgs::force_tile) or returns
+// MOE_ERR_BAD_SHAPE for a value this configuration cannot use.
+int tile_override(const moe_config& c, int* force) {
+  *force = 0;
+  const char* v = std::getenv("MOE_FORCE_TILE");
+  if (!v || !*v || std::strcmp(v, "auto") == 0) return MOE_OK;
+  if (c.weight_dtype == MOE_DTYPE_F32) return MOE_ERR_BAD_SHAPE;
+  static const struct { const char* name; int rows; } kStream[] = {
+      {"stream16", 16}, {"stream32", 32}, {"stream64", 64}, {"stream128", 128}};
+  for (const auto& s : kStream)
+    if (std::strcmp(v, s.name) == 0) {
+      *force = s.rows;
+      return MOE_OK;
+    }
+  if (std::strcmp(v, "split") == 0 &&
+      (c.weight_dtype == MOE_DTYPE_BF16 || c.weight_dtype == MOE_DTYPE_FP8_E4M3_G128)) {
+    *force = kForceSplit;
+    return MOE_OK;
+  }
+  return MOE_ERR_BAD_SHAPE;
+}
+
 int check_forward(const moe_config* cfg, int32_t T, const void* x, const float* topk_w,
                   const float* shared_gate, const int32_t* counts, const int32_t* offsets,
                   const int32_t* perm, const moe_expert_weights* w, float* y) {
   int st = check_config(cfg);
   if (st) return st;
   if ((st = check_tokens(cfg, T))) return st;
+  int force = 0;
+  if ((st = tile_override(*cfg, &force))) return st;
   if (T == 0) return MOE_OK;
   // The expert kernels address x and h (per-slot activations) with 32-bit byte
   // offsets, and keep offsets from 3 GiB up free to mark rows that load zeros.
@@ -193,6 +220,7 @@ ExpertArgs expert_args(const moe_config& c, int32_t T, const void* x, const floa
   }
   a.o = at<float>(ws, L.o);
   a.split = 0;
+  tile_override(c, &a.force_tile);   // validated by check_forward
   a.y = y;
   a.T = T;
   a.H = c.hidden_size;

@@ -296,7 +296,23 @@ int64_t rest_rows(int64_t rho) { return rho >= 192 ? 47 : rho; }
 
 int64_t rows_per_expert(const ExpertArgs& a) { return static_cast<int64_t>(a.T) * a.K / a.E; }
 
+// A forced streaming tile height as the rows per expert that select it (see
+// launch_stream_rho in stream_gemm.hip: <= 12 -> 16 rows, <= 24 -> 32, < 48 -> 64,
+// else 128).
+int64_t forced_rho(int force_tile) {
+  switch (force_tile) {
+    case 16: return 1;
+    case 32: return 20;
+    case 64: return 40;
+    default: return 48;
+  }
+}
+
 }  // namespace
+
+bool split_allowed(const ExpertArgs& a, int weight_dtype) {
+  return (weight_dtype == kDtypeBf16 || weight_dtype == kDtypeFp8) && tall_tiles_fit(a);
+}
 
 hipError_t launch_gate_up(const ExpertArgs& a, int weight_dtype, hipStream_t stream) {
   if (weight_dtype == kDtypeF32) {
@@ -305,8 +321,9 @@ hipError_t launch_gate_up(const ExpertArgs& a, int weight_dtype, hipStream_t str
     return hipGetLastError();
   }
   const int64_t rho = rows_per_expert(a);
+  if (a.force_tile > 0) return launch_gate_up_stream(a, weight_dtype, forced_rho(a.force_tile), stream);
   // MXFP4 weights run on the streaming kernel at every size (no LDS-tiled form).
-  if (split_call(a, weight_dtype, rho)) {
+  if (a.force_tile == kForceSplit || split_call(a, weight_dtype, rho)) {
     ExpertArgs tall = a, rest = a;
     tall.split = 1;
     rest.split = 2;
@@ -324,7 +341,8 @@ hipError_t launch_down(const ExpertArgs& a, int weight_dtype, hipStream_t stream
     return hipGetLastError();
   }
   const int64_t rho = rows_per_expert(a);
-  if (split_call(a, weight_dtype, rho) && a.H % 256 == 0) {
+  if (a.force_tile > 0) return launch_down_stream(a, weight_dtype, forced_rho(a.force_tile), stream);
+  if ((a.force_tile == kForceSplit || split_call(a, weight_dtype, rho)) && a.H % 256 == 0) {
     ExpertArgs tall = a, rest = a;
     tall.split = 1;
     rest.split = 2;

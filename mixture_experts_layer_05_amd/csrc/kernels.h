@@ -45,6 +45,10 @@ struct ExpertArgs {
   // Which of a call's rows this launch serves when the expert launchers divide
   // them between two kernels by the realised counts (0: all; see schedule.h).
   int split;
+  // Tile override (host side only, from MOE_FORCE_TILE): 0 = the per-call choice;
+  // 16, 32, 64 or 128 = the streaming kernel alone with tiles of that many rows;
+  // kForceSplit = rows divided between the 256-row and the streaming kernels.
+  int force_tile;
   void* y_act;                   // [T, H] act dtype or null: the cast of y
   int act_bf16;                  // y_act is bf16 (else float32)
   // Router logits (router mode of the streaming kernel): z[t, c] = x_t . col_c with
@@ -55,6 +59,8 @@ struct ExpertArgs {
   int ldz, ncols;
   int T, H, I, S, E, K;
 };
+
+constexpr int kForceSplit = -1;
 
 // route.hip
 __global__ void router_logits_bf16_kernel(const uint16_t*, const uint16_t*, const uint16_t*, int, int,
@@ -74,6 +80,10 @@ __global__ void dispatch_scatter_kernel(const int32_t*, int, int, int, const int
 
 // experts.hip: host-side launchers (they pick tile shapes and grid sizes).
 hipError_t launch_gate_up(const ExpertArgs& a, int weight_dtype, hipStream_t stream);
+// Whether the rows of a call may be divided between the 256-row LDS-tiled kernels
+// and the streaming kernel (BF16 / FP8 weights whose operands the 256-row kernels
+// can address).
+bool split_allowed(const ExpertArgs& a, int weight_dtype);
 hipError_t launch_down(const ExpertArgs& a, int weight_dtype, hipStream_t stream);
 // 256-row LDS-tiled kernels (tile_gemm.hip); tall_tiles_fit: their 32-bit
 // operand offsets cover the call's activation matrices.

@@ -189,3 +189,30 @@ def test_workspace_size_is_monotone_in_tokens(kw):
         assert st == OK
         sizes.append(n)
     assert all(b >= a for a, b in zip(sizes, sizes[1:])), sizes
+
+
+@pytest.mark.parametrize("value,kw,status", [
+    ("bogus", {}, BAD_SHAPE),
+    ("stream48", {}, BAD_SHAPE),
+    ("Split", {}, BAD_SHAPE),
+    ("split", dict(weight_dtype="mxfp4"), BAD_SHAPE),
+    ("stream16", dict(weight_dtype="f32", act_dtype="f32"), BAD_SHAPE),
+    ("split", dict(weight_dtype="f32", act_dtype="f32"), BAD_SHAPE),
+])
+def test_tile_override_rejects_bad_values_before_launching(monkeypatch, value, kw, status):
+    # The bench-only tile override fails loudly: every forward entry point returns
+    # the status before touching a pointer (FAKE pointers are never dereferenced).
+    monkeypatch.setenv("MOE_FORCE_TILE", value)
+    cfg = _cfg(**kw)
+    extra = {} if cfg.weight_dtype != "mxfp4" else dict(s_gate=FAKE, s_up=FAKE, s_down=FAKE,
+                                                          ss_gate=FAKE, ss_up=FAKE, ss_down=FAKE)
+    for name in ("moe_forward", "moe_forward_gate_up", "moe_forward_down"):
+        assert _forward(cfg, name=name, **extra) == status
+        assert _forward(cfg, T=0, name=name, **extra) == status
+
+
+@pytest.mark.parametrize("value", ["", "auto", "stream16", "stream32", "stream64", "stream128", "split"])
+def test_tile_override_accepts_documented_values(monkeypatch, value):
+    monkeypatch.setenv("MOE_FORCE_TILE", value)
+    for name in ("moe_forward", "moe_forward_gate_up", "moe_forward_down"):
+        assert _forward(_cfg(), T=0, name=name) == OK

@@ -26,6 +26,29 @@ TOPP_MARGIN = 1e-3
 BUDGET_MARGIN = 1e-4
 
 TOL = {"f32": 1e-5, "bf16": 2e-3, "fp8_e4m3_g128": 1e-2, "mxfp4": 1e-2}   # relative L2 of y
+
+# Kernel-bug checks, tighter than the parity bars above, against the oracle variant
+# that sees what the kernels see:
+#   bf16 weights: the bf16-h diagnostic (h rounded to bf16 before down).  What is
+#   left is float32 summation order, plus the rare element of h whose float32
+#   value rounds to the other bf16 neighbour than the exact value does: a
+#   relative difference d ~ 1e-6 moves about d / 2^-8 of the elements by one bf16
+#   step (2^-8 relative), ~1e-4 relative L2 in all.
+#   fp8 / MXFP4 weights: the oracle that models the activation quantisation; a
+#   code that lands on the other side of a rounding boundary moves that element
+#   by one 3-bit-mantissa step, ~1e-3 relative L2 in all.
+#   f32 weights: the plain oracle, float32 summation order only.
+BUG_TOL = {"f32": 1e-5, "bf16": 2e-4, "fp8_e4m3_g128": 3e-3, "mxfp4": 3e-3}
+# The same per token (relative L2 of each checked token's row of y): every token
+# within TOKEN_TOL, and the median token within BUG_TOL.  With fp8 / MXFP4 weights a
+# single code of h landing on the other side of a rounding boundary moves that
+# element of h by one 3-bit-mantissa step (up to 2^-3 of it); if it is the largest
+# element of a short row (I = 256: |h_max| / ||h|| up to ~0.3) the token's output
+# moves by up to ~4 %, so the per-token bound is 5e-2 there and the median carries
+# the check.
+TOKEN_TOL = {"f32": 1e-4, "bf16": 1e-3, "fp8_e4m3_g128": 5e-2, "mxfp4": 5e-2}
+# Oracle variant each bug check compares with (see oracle.moe.VARIANTS).
+BUG_REF = {"f32": "model", "bf16": "bf16_h", "fp8_e4m3_g128": "model", "mxfp4": "model"}
 # Routing weights, absolute.  The pages fix no tolerance here; the bound comes from
 # the arithmetic: the logits are float32 sums of H <= 7168 bf16 products with
 # |z| = O(1), whose rounding (random-walk ~ sqrt(H) * 2^-24 * |partial sums|) is a
@@ -145,12 +168,68 @@ def run_gpu(case: Case, layer=None) -> Dict[str, np.ndarray]:
     }
 
 
-def run_oracle(case: Case, tokens: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+def cover_tokens(ids: np.ndarray, offsets: np.ndarray, perm: np.ndarray, K: int, n: int,
+                 seed: int = 0) -> np.ndarray:
+    """About n tokens whose rows reach every kind of tile the kernels form: the first
+    and last token; up to 16 tokens left with no expert; for every touched expert
+    its first and last dispatch row; for
+    the busiest experts also the rows on both sides of every 128-row boundary (the
+    streaming kernel's tallest tiles and the 256-row kernel's tiles and their short
+    tails); the rest a seeded sample."""
+    T = ids.shape[0]
+    E = len(offsets) - 1
+    counts = np.diff(offsets)
+    must, extra = {0, T - 1}, set()
+    # Tokens that lost every slot (their y must be exactly the shared term, or 0).
+    must |= set(np.nonzero((ids < 0).all(axis=1))[0][:16].tolist())
+    busiest = np.argsort(-counts, kind="stable")[:8]
+    for e in range(E):
+        c = int(counts[e])
+        if c == 0:
+            continue
+        rows = {0, c - 1}
+        if e in busiest:
+            rows |= {r for b in range(128, c, 128) for r in (b - 1, b)}
+            rows |= {c - c % 256 - 1, c - c % 256} if c > 256 else set()
+        toks = {int(perm[offsets[e] + r]) // K for r in rows if 0 <= r < c}
+        (must if e in busiest else extra).update(toks)
+    rng = np.random.default_rng(seed)
+    pick = sorted(must)
+    if len(pick) > n:
+        pick = sorted(rng.choice(pick, size=n, replace=False).tolist())
+    rest = sorted(extra - set(pick))
+    if len(pick) + len(rest) > n:
+        rest = rng.choice(rest, size=n - len(pick), replace=False).tolist() if n > len(pick) else []
+    pick = sorted(set(pick) | set(rest))
+    if len(pick) < n:
+        free = np.setdiff1d(np.arange(T), pick)
+        pick = sorted(set(pick) | set(rng.choice(free, size=min(n - len(pick), len(free)),
+                                                 replace=False).tolist()))
+    return np.asarray(pick, dtype=np.int64)
+
+
+def run_oracle(case: Case, tokens=None) -> Dict[str, np.ndarray]:
+    """The oracle on the case: routing and dispatch of every token, y (the parity
+    reference) and the bug-check / report variants for `tokens` (all by default;
+    an int n picks n covering tokens, see cover_tokens).  ora["tokens"] holds the
+    tokens y was computed for (None: all)."""
     shape = case.shape
-    return O.moe_layer(case.inp.x, case.inp.w_router, case.inp.w_shared_gate, case.inp.logit_bias,
-                       shape.num_experts_per_tok, shape.n_routed_experts, case.expert_cpu,
-                       case.shared_cpu(), shape.weight_dtype, bool(shape.norm_topk_prob),
-                       shape.expert_budget, tokens, shape.top_p)
+    K, E = shape.num_experts_per_tok, shape.n_routed_experts
+    r = O.route(case.inp.x, case.inp.w_router, case.inp.w_shared_gate, case.inp.logit_bias, K,
+                bool(shape.norm_topk_prob), shape.expert_budget, shape.top_p)
+    counts, offsets, perm = O.dispatch(r["ids"], E)
+    if isinstance(tokens, (int, np.integer)):
+        tokens = cover_tokens(r["ids"], offsets, perm, K, int(tokens), case.seed)
+    variants = ["model", BUG_REF[shape.weight_dtype]]
+    if shape.weight_dtype in ("fp8_e4m3_g128", "mxfp4"):
+        variants.append("plain")
+    variants = list(dict.fromkeys(variants))
+    ys = O.moe_combine(case.inp.x, r["ids"], r["w"], r["shared_gate"], case.expert_cpu, case.shared_cpu(),
+                       shape.weight_dtype, tokens, variants)
+    r.update(counts=counts, offsets=offsets, perm=perm, y=ys["model"], tokens=tokens)
+    for n in variants[1:]:
+        r["y_" + n] = ys[n]
+    return r
 
 
 def rel_l2(a: np.ndarray, b: np.ndarray) -> float:
@@ -158,9 +237,18 @@ def rel_l2(a: np.ndarray, b: np.ndarray) -> float:
     return float(np.linalg.norm(a - b) / den) if den > 0 else float(np.linalg.norm(a))
 
 
+def token_rel_l2(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Relative L2 of each row (rows whose reference is all zero are left out)."""
+    den = np.linalg.norm(b, axis=1)
+    num = np.linalg.norm(a - b, axis=1)
+    return num[den > 0] / den[den > 0]
+
+
 def compare(case: Case, gpu: Dict, ora: Dict, tokens: Optional[Sequence[int]] = None) -> Dict[str, float]:
-    """Assert parity; return the measured errors."""
+    """Assert parity and the kernel-bug checks; return the measured errors."""
     shape = case.shape
+    if tokens is None:
+        tokens = ora.get("tokens")
     K = shape.num_experts_per_tok
     assert np.array_equal(gpu["ids"], ora["ids"]), "expert ids differ"
     werr = float(np.abs(gpu["w"] - ora["w"]).max()) if gpu["w"].size else 0.0
@@ -181,15 +269,32 @@ def compare(case: Case, gpu: Dict, ora: Dict, tokens: Optional[Sequence[int]] = 
         sg_err = float(np.abs(gpu["shared_gate"] - ora["shared_gate"]).max())
         assert sg_err <= 1e-5, f"shared gate differs by {sg_err}"
     y_gpu = gpu["y"] if tokens is None else gpu["y"][np.asarray(tokens)]
+    dt = shape.weight_dtype
     err = rel_l2(y_gpu, ora["y"])
-    tol = TOL[shape.weight_dtype]
+    tol = TOL[dt]
     assert err <= tol, f"y relative L2 {err:.3e} > {tol:.0e}"
+    # Kernel-bug checks against the oracle variant that sees what the kernels see.
+    ref = ora["y"] if BUG_REF[dt] == "model" else ora["y_" + BUG_REF[dt]]
+    bug = rel_l2(y_gpu, ref)
+    assert bug <= BUG_TOL[dt], f"y relative L2 vs the {BUG_REF[dt]} oracle {bug:.3e} > {BUG_TOL[dt]:.0e}"
+    per_tok = token_rel_l2(y_gpu, ref)
+    tok_max = float(per_tok.max()) if per_tok.size else 0.0
+    tok_med = float(np.median(per_tok)) if per_tok.size else 0.0
+    assert tok_max <= TOKEN_TOL[dt], f"a token's relative L2 vs the {BUG_REF[dt]} oracle is {tok_max:.3e}"
+    assert tok_med <= BUG_TOL[dt], f"median token relative L2 vs the {BUG_REF[dt]} oracle is {tok_med:.3e}"
+    out = {"y_rel_l2": err, "y_bug_rel_l2": bug, "y_token_max": tok_max, "y_token_median": tok_med,
+           "y_token_max_vs_plain": float(token_rel_l2(y_gpu, ora["y"]).max()) if y_gpu.size else 0.0,
+           "w_max_abs": werr, "shared_gate_max_abs": sg_err}
+    if "y_plain" in ora:
+        # fp8 / MXFP4: the format's own error against the unquantised layer, reported, not gated.
+        out["quant_err_vs_plain"] = rel_l2(y_gpu, ora["y_plain"])
     # Tokens with no kept expert and no shared expert must be exactly zero.
     if shape.shared_expert_intermediate_size == 0:
         toks = np.arange(case.T) if tokens is None else np.asarray(tokens)
         empty = (ora["ids"][toks] < 0).all(axis=1)
         assert (y_gpu[empty] == 0).all()
-    return {"y_rel_l2": err, "w_max_abs": werr, "shared_gate_max_abs": sg_err}
+        out["empty_tokens_checked"] = int(empty.sum())
+    return out
 
 
 def sample_tokens(T: int, n: int, seed: int = 0) -> np.ndarray:

@@ -22,8 +22,9 @@ def _run(shape, T, seed, alpha=None, tokens=None, condition=True, mutate=None):
         mutate(case)
     gpu = Hn.run_gpu(case)
     ora = Hn.run_oracle(case, tokens)
-    errs = Hn.compare(case, gpu, ora, tokens)
-    print(f"[case] ok {errs} redrawn_rows={case.redrawn_rows}", flush=True)
+    errs = Hn.compare(case, gpu, ora)
+    n = case.T if ora["tokens"] is None else len(ora["tokens"])
+    print(f"[case] ok {errs} tokens_checked={n} redrawn_rows={case.redrawn_rows}", flush=True)
     return case, gpu, ora, errs
 
 
@@ -42,27 +43,27 @@ def test_narrow_layer(T):
 
 
 def test_narrow_layer_224_sampled():
-    _run(W.NARROW, 224, W.base_seed(2, 224), tokens=Hn.sample_tokens(224, 48))
+    _run(W.NARROW, 224, W.base_seed(2, 224), tokens=48)
 
 
 @pytest.mark.parametrize("alpha", [0.0, 1.5])
 def test_large_layer_512(alpha):
-    _run(W.LARGE, 512, W.base_seed(3, 512), alpha, tokens=Hn.sample_tokens(512, 24))
+    _run(W.LARGE, 512, W.base_seed(3, 512), alpha, tokens=64)
 
 
 def test_large_layer_2048_uniform_sampled():
-    _run(W.LARGE, 2048, W.base_seed(3, 2048), 0.0, tokens=Hn.sample_tokens(2048, 16))
+    _run(W.LARGE, 2048, W.base_seed(3, 2048), 0.0, tokens=128)
 
 
 def test_large_layer_8192_skewed_sampled():
-    _run(W.LARGE, 8192, W.base_seed(3, 8192), 1.5, tokens=Hn.sample_tokens(8192, 16))
+    _run(W.LARGE, 8192, W.base_seed(3, 8192), 1.5, tokens=128)
 
 
 # The rest of the large layer's (T, alpha) grid, on sampled tokens: the middle
 # skew at every size, the skewed middle size and the uniform full size.
 @pytest.mark.parametrize("T,alpha", [(512, 1.0), (2048, 1.0), (2048, 1.5), (8192, 0.0), (8192, 1.0)])
 def test_large_layer_grid_sampled(T, alpha):
-    _run(W.LARGE, T, W.base_seed(3, T), alpha, tokens=Hn.sample_tokens(T, 16))
+    _run(W.LARGE, T, W.base_seed(3, T), alpha, tokens=64)
 
 
 # MXFP4 expert weights x MXFP8 activations (block-scaled fp8 x fp4 contraction).
@@ -75,7 +76,7 @@ def test_large_layer_grid_sampled(T, alpha):
     (W.LARGE_MX4.with_(name="large_mxfp4_budget64", expert_budget=64), 512, 4, 1.5, 24),
 ])
 def test_mxfp4_layer(shape, T, idx, alpha, tokens):
-    _run(shape, T, W.base_seed(idx, T), alpha, tokens=None if tokens is None else Hn.sample_tokens(T, tokens))
+    _run(shape, T, W.base_seed(idx, T), alpha, tokens=tokens)
 
 
 # fp8 e4m3 group-128 weights on the decode layers (two-group streaming stages).
@@ -85,7 +86,7 @@ def test_mxfp4_layer(shape, T, idx, alpha, tokens):
     (W.NARROW_FP8, 56, 2, None),
 ])
 def test_fp8_decode_layer(shape, T, idx, tokens):
-    _run(shape, T, W.base_seed(idx, T), tokens=None if tokens is None else Hn.sample_tokens(T, tokens))
+    _run(shape, T, W.base_seed(idx, T), tokens=tokens)
 
 
 # A small fp8 layer on the two-group stages (H, I, S multiples of 256; the down
@@ -115,7 +116,7 @@ def test_fp8_quad_stages_ragged(T):
     (W.LARGE_MX4, 8192, W.base_seed(3, 8192), 1.5, 16),
 ])
 def test_mxfp4_prefill(shape, T, seed, alpha, tokens):
-    _run(shape, T, seed, alpha, tokens=None if tokens is None else Hn.sample_tokens(T, tokens))
+    _run(shape, T, seed, alpha, tokens=tokens)
 
 
 # A small MXFP4 layer (contraction of 2 stages) with ragged row tiles: one token,
@@ -137,9 +138,8 @@ def test_mxfp4_small_ragged(T):
     (W.LARGE_FP8.with_(name="large_fp8_topp_budget", top_p=0.7), 512, W.base_seed(4, 512), 0.7, 24),
 ])
 def test_top_p_trim(shape, T, seed, top_p, tokens):
-    toks = None if tokens is None else Hn.sample_tokens(T, tokens)
     alpha = 1.5 if shape.weight_dtype == W.DT_FP8 else None
-    case, gpu, ora, _ = _run(shape, T, seed, alpha, tokens=toks)
+    case, gpu, ora, _ = _run(shape, T, seed, alpha, tokens=tokens)
     K = shape.num_experts_per_tok
     kept = (gpu["ids"] >= 0).sum(axis=1)
     assert kept.min() >= 1 and kept.max() <= K
@@ -196,28 +196,34 @@ def test_expert_parallel_rank_share_sampled():
     assert np.array_equal(layer.offsets.cpu().numpy(), offsets)
     assert np.array_equal(layer.perm[:nkept].cpu().numpy(), perm)
     assert 0 < nkept < T * K
-    # Sampled tokens, plus tokens the rank receives nothing for (their y must be 0).
-    tokens = Hn.sample_tokens(T, 16)
+    # Covering tokens (every local expert's first and last row, the busiest ones'
+    # tile boundaries, tokens the rank receives nothing for), y vs the oracle and
+    # vs its bf16-h diagnostic.
+    tokens = Hn.cover_tokens(ids_o, offsets, perm, K, 96, seed)
     expert_cpu = lambda e: {k: v[e].cpu() for k, v in weights.items()}  # noqa: E731
-    y_o = O.moe_combine(inp.x, ids_o, w_o, None, expert_cpu, None, loc.weight_dtype, tokens)
+    ys = O.moe_combine(inp.x, ids_o, w_o, None, expert_cpu, None, loc.weight_dtype, tokens,
+                       ["model", "bf16_h"])
     y_g = layer.y.cpu().numpy().astype(np.float64)
-    err = Hn.rel_l2(y_g[tokens], y_o)
+    err = Hn.rel_l2(y_g[tokens], ys["model"])
     assert err <= Hn.TOL[loc.weight_dtype], err
+    bug = Hn.rel_l2(y_g[tokens], ys["bf16_h"])
+    assert bug <= Hn.BUG_TOL["bf16"], bug
+    tok = Hn.token_rel_l2(y_g[tokens], ys["bf16_h"])
+    assert tok.max() <= Hn.TOKEN_TOL["bf16"], tok.max()
     empty = (ids_o < 0).all(axis=1)
     assert empty.any() and (y_g[empty] == 0).all()
-    print(f"[case] ok y_rel_l2={err:.3e} w_max_abs={werr:.1e} rank={rank} kept={nkept} of {T * K} slots",
-          flush=True)
+    print(f"[case] ok y_rel_l2={err:.3e} y_bug_rel_l2={bug:.3e} y_token_max={tok.max():.3e} "
+          f"w_max_abs={werr:.1e} rank={rank} kept={nkept} of {T * K} slots", flush=True)
 
 
 def test_fp8_budget_layer_8192_sampled():
-    case, gpu, ora, errs = _run(W.LARGE_FP8, 8192, W.base_seed(4, 8192), 1.5,
-                                tokens=Hn.sample_tokens(8192, 16))
+    case, gpu, ora, errs = _run(W.LARGE_FP8, 8192, W.base_seed(4, 8192), 1.5, tokens=128)
     assert gpu["stats"][1] == 64 and gpu["stats"][0] > 64
 
 
 def test_fp8_small_budget_drops_experts():
     shape = W.LARGE_FP8.with_(expert_budget=32)
-    case, gpu, ora, errs = _run(shape, 512, W.base_seed(4, 512), 1.5, tokens=Hn.sample_tokens(512, 24))
+    case, gpu, ora, errs = _run(shape, 512, W.base_seed(4, 512), 1.5, tokens=64)
     assert gpu["stats"][0] > 32 and gpu["stats"][1] == 32 and gpu["stats"][2] > 0
     # Same quantisation decisions on both sides: far below the fp8 bar.
     assert errs["y_rel_l2"] < 1e-3
@@ -238,6 +244,103 @@ def test_budget_without_statistics_routes_the_same():
     plain = Hn.run_gpu(case, layer)
     for k in ("ids", "w", "counts", "offsets", "perm", "y"):
         assert np.array_equal(plain[k], with_stats[k]), k
+
+
+def test_large_budget_empties_tokens_full_size():
+    """The large layer with uniform routing (alpha 0) and a budget of 64 at T = 8192:
+    hundreds of tokens lose every slot [colibri issue_budget.md, "How it works"
+    step 4, "Safety"]; with no shared expert their y must be exactly 0."""
+    shape = W.LARGE.with_(name="large_budget64", expert_budget=64)
+    case, gpu, ora, errs = _run(shape, 8192, W.base_seed(3, 8192) + 64, 0.0, tokens=128)
+    assert gpu["stats"][0] > 64 and gpu["stats"][1] == 64 and gpu["stats"][3] > 100, gpu["stats"]
+    assert errs["empty_tokens_checked"] > 0
+    empty = (gpu["ids"] < 0).all(axis=1)
+    assert (gpu["y"][empty] == 0).all()          # every emptied token, not only the checked ones
+
+
+# A mid-size layer for the tile override: about 128 rows per expert, so every
+# streaming tile height and the 256-row kernels each see full and partial tiles.
+_INVARIANCE = W.LayerShape("tile_invariance", 1024, 16, 512, 4, 512, W.DT_BF16, W.DT_BF16)
+
+
+@pytest.mark.parametrize("dt", [W.DT_BF16, W.DT_FP8, W.DT_MXFP4])
+def test_tile_override_config_invariance(dt, monkeypatch):
+    """Every setting of the tile override (MOE_FORCE_TILE) on one case: routing and
+    dispatch bit-identical, y within the parity and kernel-bug bars for each, and
+    every setting's y within float32 summation order of the default's [DeepGEMM
+    PR #381, "Validation": config invariance across forced settings]."""
+    import mixture_experts_layer_05_amd as moe
+    shape = _INVARIANCE.with_(name=f"tile_invariance_{dt}", weight_dtype=dt)
+    T = 512
+    case = Hn.make_case(shape, T, W.base_seed(6, T), 1.0)
+    ora = Hn.run_oracle(case)
+    settings = ["auto", "stream16", "stream32", "stream64", "stream128"]
+    if dt != W.DT_MXFP4:
+        settings.append("split")
+    base = None
+    for st in settings:
+        print(f"\n[case] {shape.name} T={T} MOE_FORCE_TILE={st}", flush=True)
+        monkeypatch.setenv("MOE_FORCE_TILE", st)
+        gpu = Hn.run_gpu(case)
+        errs = Hn.compare(case, gpu, ora)
+        if base is None:
+            base = gpu
+        for k in ("ids", "w", "counts", "offsets", "perm", "stats"):
+            assert np.array_equal(gpu[k], base[k]), (st, k)
+        # Tile shapes change the float32 summation order of h, and with it the
+        # rare rounding of h to bf16 / e4m3 / MXFP8: within the kernel-bug bar.
+        d = Hn.rel_l2(gpu["y"], base["y"])
+        assert d <= Hn.BUG_TOL[dt], (st, d)
+        print(f"[case] ok {st}: {errs} vs default {d:.2e}", flush=True)
+    if dt == W.DT_MXFP4:
+        monkeypatch.setenv("MOE_FORCE_TILE", "split")
+        with pytest.raises(moe.MoEError) as ei:
+            Hn.run_gpu(case)
+        assert ei.value.status == -2
+
+
+def test_invalid_tile_override_launches_nothing(monkeypatch):
+    import mixture_experts_layer_05_amd as moe
+    case = Hn.make_case(_INVARIANCE, 64, 77)
+    layer = moe.MoELayer(Hn.config(case.shape), case.weights, case.inp.w_router.cuda(),
+                         case.inp.w_shared_gate.cuda(), case.shared, max_tokens=64)
+    x = case.inp.x.cuda()
+    layer.route(x)
+    layer.dispatch(64)
+    layer.y.fill_(float("nan"))
+    torch.cuda.synchronize()
+    for bad in ("stream48", "tall", "SPLIT", "1"):
+        monkeypatch.setenv("MOE_FORCE_TILE", bad)
+        with pytest.raises(moe.MoEError) as ei:
+            layer.forward(x)
+        assert ei.value.status == -2
+    torch.cuda.synchronize()
+    assert torch.isnan(layer.y).all()          # nothing was launched
+
+
+@pytest.mark.parametrize("poison", ["-inf", "nan"])
+def test_masked_experts_fewer_finite_than_k(poison):
+    """A bias that masks E - K + 2 experts leaves K - 2 finite logits per token: the
+    top-k still returns K distinct valid ids (the masked ones after the finite ones,
+    lower id first, weight 0), and the layer matches the oracle."""
+    shape = W.LayerShape("masked_experts", 256, 8, 256, 4, 128, W.DT_BF16, W.DT_BF16)
+    T = 24
+
+    def mask(case):
+        # Mask every expert but each token's two largest logits (whose gap the
+        # conditioned inputs keep above the top-k margin).
+        from oracle import moe as O
+        z = O.router_logits(case.inp.x, case.inp.w_router)
+        b = torch.zeros(T, shape.n_routed_experts)
+        for t in range(T):
+            off = np.argsort(-z[t])[2:]
+            b[t, torch.as_tensor(off)] = float(poison)
+        case.inp.logit_bias = b
+    case, gpu, ora, _ = _run(shape, T, 66, mutate=mask)
+    ids = gpu["ids"]
+    assert ((ids >= 0) & (ids < shape.n_routed_experts)).all()
+    assert all(len(set(r)) == len(r) for r in ids.tolist())
+    assert (gpu["w"][:, 2:] == 0).all()
 
 
 # ----------------------------------------------------------------------------- edge cases

@@ -53,6 +53,7 @@ class LayerShape:
     norm_topk_prob: int = 1
     expert_budget: int = 0            # B, 0 = off
     top_p: float = 0.0                # per-token top-p trim of the top-k, 0 = off
+    block_bias: bool = False          # router bias shared per 7-token block (the drafter family)
     weight_std: float = 0.02
     x_std: float = 1.0
     router_std: Optional[float] = None  # default 1/sqrt(H)
@@ -68,7 +69,8 @@ class LayerShape:
 # The five workloads (index order matters: the fp8 + budget case reuses index 3's shape).
 TINY = LayerShape("tiny_fp32", 256, 8, 512, 2, 0, DT_F32, DT_F32,
                   weight_std=0.02, x_std=0.02, router_std=0.02)
-DRAFTER = LayerShape("drafter_16x1024_top2_shared2048", 5120, 16, 1024, 2, 2048, DT_BF16, DT_BF16)
+DRAFTER = LayerShape("drafter_16x1024_top2_shared2048", 5120, 16, 1024, 2, 2048, DT_BF16, DT_BF16,
+                     block_bias=True)
 NARROW = LayerShape("narrow_512x512_top10_shared2048", 5120, 512, 512, 10, 2048, DT_BF16, DT_BF16)
 LARGE = LayerShape("large_256x2048_top8_h7168", 7168, 256, 2048, 8, 0, DT_BF16, DT_BF16)
 LARGE_FP8 = LARGE.with_(name="large_fp8_budget64", weight_dtype=DT_FP8, expert_budget=64)
@@ -295,7 +297,7 @@ def layer_inputs(shape: LayerShape, T: int, seed: int, alpha: Optional[float] = 
                  bias_attempt: int = 0) -> LayerInputs:
     """Activations and router inputs for one call (expert weights come separately)."""
     bias = None
-    if shape.name == DRAFTER.name:
+    if shape.block_bias:
         bias = drafter_block_bias(shape, seed, T)
     elif alpha is not None and alpha != 0.0:
         bias = zipf_rank_bias(shape, seed, T, alpha, bias_attempt)

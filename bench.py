@@ -1,12 +1,16 @@
 """Benchmark of the routed MoE FFN forward on one MI355X.
 
 One step = route -> dispatch -> forward (every kernel of the layer) over one
-batch of synthetic tokens, inputs already resident in HBM.  The default workload
-is the 16 x 1024 top-2 drafter layer with its 2048-wide sigmoid-gated shared
-expert at 32 concurrent 7-token blocks (T = 224), the decode-sized point of
-[SpecForge PR #943, "End-to-end serving speed"].  Several copies of the layer
-weights are cycled (one per step, like the layers of a model) so that no step
-finds its weights in the 256 MB last-level cache.
+batch of synthetic tokens, inputs already resident in HBM.  The headline workload
+is the largest configuration: the 256-expert top-8 layer (hidden 7168,
+intermediate 2048, bf16) at T = 8192 tokens with a Zipf router skew of 1.5, the
+shape of [DeepGEMM PR #381, "Validation" and "B200 performance"]; its gate/up
+stage is priced against the bf16 MFMA peak.  The same line nests a decode record:
+the 16 x 1024 top-2 drafter layer with its 2048-wide sigmoid-gated shared expert
+at 32 concurrent 7-token blocks (T = 224) [SpecForge PR #943, "End-to-end serving
+speed"], priced against the HBM peak.  Where a layer's weights are smaller than
+~2 GB, several copies are cycled (one per step, like the layers of a model) so
+that no step finds its weights in the 256 MB last-level cache.
 
 Prints ONE JSON line (rank 0): tokens/s of the whole layer plus TFLOP/s, weight
 GB/s, the roofline of the dominant kernel (timed with HIP events on the stream
@@ -36,12 +40,13 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="drafter",
+    p.add_argument("--workload", default="large",
                    choices=["drafter", "narrow", "large", "large_fp8", "tiny", "ep_rank",
                             "drafter_mxfp4", "narrow_mxfp4", "large_mxfp4", "drafter_fp8", "narrow_fp8"])
     p.add_argument("--tokens", type=int, default=None, help="T (default: the workload's bench size)")
     p.add_argument("--alpha", type=float, default=None, help="Zipf router skew for the large layers")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-decode", action="store_true", help="leave out the nested decode record")
     p.add_argument("--cpu-sample-tokens", type=int, default=None)
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (the reference for HBM byte counters)")
@@ -193,7 +198,9 @@ CPU_BASELINE_SECONDS = 10.0
 
 def cpu_baseline(shape, case_inputs, expert_cpu, shared_cpu, T, sample_tokens):
     """The CPU oracle as it stands, on a bounded sample: routing of every token plus
-    the expert math of `sample_tokens` tokens; reported per token of the sample."""
+    the expert math of `sample_tokens` tokens; reported per token of the sample.
+    expert_cpu / shared_cpu hand out host copies staged before the timing (the
+    device-to-host copy of the weights is input staging, not oracle work)."""
     import numpy as np
     import threadpoolctl
     from oracle import moe as O
@@ -212,37 +219,19 @@ def cpu_baseline(shape, case_inputs, expert_cpu, shared_cpu, T, sample_tokens):
     threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
     return {"value": reps * len(toks) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{len(toks)} of {T} tokens: routing of all {T} tokens + expert math of the "
-                      f"first {len(toks)}, float64 numpy on the host; {reps} passes in {dt:.2f} s"}
+                      f"first {len(toks)}, float64 numpy on the host (weights staged in host memory "
+                      f"before timing); {reps} passes in {dt:.2f} s"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is not sharded "
-              f"across GPUs (one GPU's share of an expert-parallel layer is the ep_rank workload).",
-              file=sys.stderr)
-        sys.exit(2)
-
+def measure(args, shape, idx, T, alpha, steps, warmup):
+    """Time `steps` steps of one workload; returns (JSON record, context for the CPU
+    baseline)."""
     import numpy as np
     import torch
     import workloads as W
     import mixture_experts_layer_05_amd as moe
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    moe.lib()   # fail loudly if the HIP library is missing
-
-    if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": 1 << 30, "launches": 5}), flush=True)
-        return
-
-    shape, idx, T, alpha = workload(args)
     seed = W.base_seed(idx, T)
     ep_rank = shape.name == W.EP_RANK.name
     cfg = moe.MoEConfig(shape.hidden_size, shape.n_routed_experts, shape.moe_intermediate_size,
@@ -306,21 +295,21 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     # The timed steps: the layer alone (no event records between its launches).
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = wall * 1e3 / steps
     # A second pass of as many steps with HIP events between the stages, on the
     # launching stream: per-stage times and the gate/up duration of the roofline.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i, evs[i])
     torch.cuda.synchronize()
     step_ev = np.array([e[0].elapsed_time(e[3]) for e in evs])
@@ -338,7 +327,8 @@ def main():
     t_hbm = a["gate_up_bytes"] / (HBM_PEAK_GBPS * 1e9)
     t_mfma = a["gate_up_flops"] / (peak_tf * 1e12)
     kernel = gate_up_kernel(shape, T)
-    traffic = stored_traffic("gate_up", f"{args.workload}_T{T}", kernel_source_file(kernel))
+    wl = args.workload if args is not None else "drafter"
+    traffic = stored_traffic("gate_up", f"{wl}_T{T}", kernel_source_file(kernel))
     if t_mfma > t_hbm and shape.weight_dtype != "f32":
         achieved = a["gate_up_flops"] / (gate_up_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 1), "peak": peak_tf,
@@ -347,19 +337,10 @@ def main():
         achieved = a["gate_up_bytes"] / (gate_up_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic}
-    line = {
-        "metric": METRIC,
-        "value": round(tokens_per_s, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+    rec = {
         "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
+        "tokens_per_s": round(tokens_per_s, 1),
         "dtype": shape.weight_dtype,
-        "data": "synthetic (seeded; random-init weights)",
         "config": {"workload": f"{shape.name} T={T}" + (f" alpha={alpha}" if alpha is not None else ""),
                    "tokens": T, "hidden": shape.hidden_size, "experts": shape.n_routed_experts,
                    "intermediate": shape.moe_intermediate_size, "topk": shape.num_experts_per_tok,
@@ -377,12 +358,74 @@ def main():
         "layer_roofline": layer_roofline(shape, a, ms_per_step),
     }
     if shape.weight_dtype != "f32" and a["gate_up_flops"] / (gate_up_ms * 1e-3) / 1e12 > 0:
-        line["gate_up_tflops"] = round(a["gate_up_flops"] / (gate_up_ms * 1e-3) / 1e12, 2)
-    if not args.no_cpu_baseline and not ep_rank:
-        L0 = layers[0]
-        expert_cpu = lambda e: {k: v[e].cpu() for k, v in L0.weights_dict.items()}  # noqa: E731
+        rec["gate_up_tflops"] = round(a["gate_up_flops"] / (gate_up_ms * 1e-3) / 1e12, 2)
+    return rec, {"inp": inp, "layer": layers[0], "ep_rank": ep_rank}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is not sharded "
+              f"across GPUs (one GPU's share of an expert-parallel layer is the ep_rank workload).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import workloads as W
+    import mixture_experts_layer_05_amd as moe
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    moe.lib()   # fail loudly if the HIP library is missing
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 1 << 30, "launches": 5}), flush=True)
+        return
+
+    shape, idx, T, alpha = workload(args)
+    print(f"[bench] {shape.name} T={T} alpha={alpha}: {args.steps} steps after {args.warmup}",
+          file=sys.stderr, flush=True)
+    rec, ctx = measure(args, shape, idx, T, alpha, args.steps, args.warmup)
+    line = {
+        "metric": METRIC,
+        "value": rec["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": rec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": rec["dtype"],
+        "data": "synthetic (seeded; random-init weights)",
+    }
+    line.update({k: v for k, v in rec.items() if k not in ("ms_per_step", "tokens_per_s", "dtype")})
+    if not args.no_decode and args.workload == "large":
+        # The decode record: the drafter layer at T = 224, HBM-bound.  Its steps are
+        # ~0.2 ms, so it runs ten times the headline's step count.
+        print("[bench] decode record: drafter T=224", file=sys.stderr, flush=True)
+        drec, _ = measure(None, W.DRAFTER, 1, 224, None, 10 * args.steps, args.warmup)
+        line["decode"] = {"ms_per_step": drec["ms_per_step"], "tokens_per_s": drec["tokens_per_s"],
+                          "steps": 10 * args.steps, **{k: v for k, v in drec.items()
+                                                       if k not in ("ms_per_step", "tokens_per_s")}}
+    if not args.no_cpu_baseline and not ctx["ep_rank"]:
+        print("[bench] CPU baseline (oracle)", file=sys.stderr, flush=True)
+        L0, inp = ctx["layer"], ctx["inp"]
+        sample = args.cpu_sample_tokens or min(T, 224 if shape.hidden_size <= 5120 else 4)
+        # Stage the sample's experts in host memory before timing.
+        ids = L0.topk_ids[:sample].cpu().numpy()
+        host = {int(e): {k: v[int(e)].cpu() for k, v in L0.weights_dict.items()} for e in np.unique(ids)
+                if e >= 0}
+        expert_cpu = lambda e: host[e] if e in host else {k: v[e].cpu() for k, v in L0.weights_dict.items()}  # noqa: E731
         shared_cpu = None if L0.shared_dict is None else {k: v.cpu() for k, v in L0.shared_dict.items()}
-        sample = args.cpu_sample_tokens or min(T, 224 if shape.hidden_size <= 5120 else 16)
         line["cpu_baseline"] = cpu_baseline(shape, inp, expert_cpu, shared_cpu, T, sample)
     print(json.dumps(line), flush=True)
 

@@ -1,6 +1,8 @@
-"""Build the HIP library in-tree: one hipcc invocation for gfx950."""
+"""Build the HIP library in-tree for gfx950: each source compiled to an object in
+parallel, then one link into libmoe_mi355x.so."""
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -9,6 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_mi355x.so")
+OBJDIR = os.path.join(HERE, "_build")
 SOURCES = ["api.hip", "route.hip", "dispatch.hip", "experts.hip", "tile_gemm.hip", "stream_gemm.hip"]
 
 FLAGS = [
@@ -16,7 +19,6 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-munsafe-fp-atomics",                         # float atomics as native global_atomic_add_f32
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
@@ -25,8 +27,21 @@ FLAGS = [
 
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    os.makedirs(OBJDIR, exist_ok=True)
+    objs = [os.path.join(OBJDIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+
+    def compile_one(src_obj):
+        src, obj = src_obj
+        cmd = [hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+
+    jobs = min(len(SOURCES), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as pool:
+        list(pool.map(compile_one, zip(SOURCES, objs)))
     tmp = LIB + ".tmp"
-    cmd = [hipcc, *FLAGS, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

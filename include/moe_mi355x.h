@@ -18,7 +18,9 @@
  * Conventions shared by every entry point:
  *   - Pointers marked (device) are device pointers; (host) are host pointers.
  *     The caller owns every buffer.  The library allocates nothing, keeps no
- *     mutable global state and caches nothing between calls.
+ *     mutable global state and caches nothing between calls, except the static
+ *     scratch of moe_forward_noalloc (one array per GPU, held from module load to
+ *     process exit) and that array's device address, looked up once per GPU.
  *   - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *     default stream).  Nothing synchronises with the host and nothing is copied
  *     device-to-host, so the calls may be captured into a HIP graph.
@@ -68,7 +70,9 @@ typedef enum moe_status {
   MOE_ERR_BAD_DTYPE = -3,           /* unknown dtype or unsupported combination    */
   MOE_ERR_UNSUPPORTED = -4,         /* valid but not implemented (alignment, E>512) */
   MOE_ERR_WORKSPACE_TOO_SMALL = -5, /* ws_bytes < moe_workspace_size(...)          */
-  MOE_ERR_LAUNCH_FAILED = -6        /* a HIP launch reported an error              */
+  MOE_ERR_LAUNCH_FAILED = -6,       /* a HIP launch reported an error              */
+  MOE_ERR_SCRATCH_TOO_SMALL = -7    /* moe_forward_noalloc: the call needs more
+                                       workspace than its static scratch holds    */
 } moe_status;
 
 typedef enum moe_dtype {
@@ -238,6 +242,26 @@ int moe_forward_down(const moe_config* cfg, int32_t num_tokens, const void* x,
                      const int32_t* expert_counts, const int32_t* expert_offsets,
                      const int32_t* perm, const moe_expert_weights* weights, float* y,
                      void* y_act, void* workspace, size_t workspace_bytes, void* stream);
+
+/* moe_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, checks, kernels and result as moe_forward,
+ * which it calls with a static scratch in place of the workspace: a file-scope
+ * device array of 64 MiB that each GPU the library runs on holds from module load
+ * until the process ends.  Its device address is looked up with
+ * hipGetSymbolAddress on the first call on each GPU (with that GPU current) and
+ * kept; nothing is allocated and nothing is freed, ever.  A call whose
+ * moe_workspace_size(cfg, T) exceeds 64 MiB returns MOE_ERR_SCRATCH_TOO_SMALL
+ * before anything is launched (the drafter layer at T = 224 needs ~12 MiB, the
+ * 512 x 512 top-10 layer ~50 MiB).  Every call on one GPU shares that GPU's
+ * scratch, which keeps the last call's contents; no kernel needs it zeroed.
+ * Calls that overlap on one GPU (on different streams, or from different host
+ * threads without ordering) race on it: serialise them. */
+int moe_forward_noalloc(const moe_config* cfg, int32_t num_tokens, const void* x,
+                        const float* topk_weights, const float* shared_gate,
+                        const int32_t* expert_counts, const int32_t* expert_offsets,
+                        const int32_t* perm, const moe_expert_weights* weights, float* y,
+                        void* y_act, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* moe_status_string(int status);

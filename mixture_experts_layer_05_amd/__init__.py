@@ -26,7 +26,10 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "moe_mi355x.h")
 
 DTYPES = {"f32": 0, "bf16": 1, "fp8_e4m3_g128": 2, "mxfp4": 3}
 ENTRY_POINTS = ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_forward",
-                "moe_forward_gate_up", "moe_forward_down", "moe_status_string", "moe_version")
+                "moe_forward_gate_up", "moe_forward_down", "moe_forward_noalloc", "moe_status_string",
+                "moe_version")
+# Static scratch of moe_forward_noalloc (bytes), as the header states it.
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MoEError(RuntimeError):
@@ -66,8 +69,10 @@ def lib() -> ctypes.CDLL:
         fwd = [cfgp, i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(_Weights), vp, vp, vp, sz, vp]
         for name in ("moe_forward", "moe_forward_gate_up", "moe_forward_down"):
             getattr(L, name).argtypes = fwd
+        L.moe_forward_noalloc.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(_Weights), vp, vp,
+                                          vp]
         for name in ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_forward",
-                     "moe_forward_gate_up", "moe_forward_down", "moe_version"):
+                     "moe_forward_gate_up", "moe_forward_down", "moe_forward_noalloc", "moe_version"):
             getattr(L, name).restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -230,6 +235,19 @@ def forward_down(cfg, x, topk_weights, shared_gate, counts, offsets, perm, weigh
                  stream=None, y_act=None) -> None:
     _forward_call("moe_forward_down", cfg, x, topk_weights, shared_gate, counts, offsets, perm,
                   weights, y, workspace, stream, y_act)
+
+
+def forward_noalloc(cfg, x, topk_weights, shared_gate, counts, offsets, perm, weights: _Weights, y,
+                    stream=None, y_act=None) -> None:
+    """moe_forward on the library's static per-GPU scratch (no workspace argument)."""
+    T, H = x.shape[0], cfg.hidden_size
+    _expect(y, (T, H), torch.float32, "y")
+    _expect(topk_weights, (T, cfg.num_experts_per_tok), torch.float32, "topk_weights")
+    if y_act is not None:
+        _expect(y_act, (T, H), torch.bfloat16 if cfg.act_dtype == "bf16" else torch.float32, "y_act")
+    _check(lib().moe_forward_noalloc(ctypes.byref(cfg.c()), T, _ptr(x), _ptr(topk_weights), _ptr(shared_gate),
+                                     _ptr(counts), _ptr(offsets), _ptr(perm), ctypes.byref(weights), _ptr(y),
+                                     _ptr(y_act), _stream(stream)), "moe_forward_noalloc")
 
 
 class MoELayer:

@@ -2,6 +2,7 @@
 // Everything is enqueued on the caller's stream; nothing is allocated, nothing is
 // read back to the host.
 #include <algorithm>
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 
@@ -231,6 +232,39 @@ ExpertArgs expert_args(const moe_config& c, int32_t T, const void* x, const floa
   return a;
 }
 
+// ---------------------------------------------------------------- static scratch
+//
+// The scratch of moe_forward_noalloc: a file-scope device array that every GPU the
+// library runs on holds from module load until the process ends.  Its host-side
+// name is not a device address; the address comes from hipGetSymbolAddress, once
+// per device, with that device current.
+constexpr size_t kScratchBytes = size_t{64} << 20;
+constexpr int kMaxDevices = 64;
+
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::atomic<void*> scratch_ptr[kMaxDevices];
+
+// The current device's scratch address, or nullptr with *status set on failure.
+void* device_scratch(int* status) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *status = MOE_ERR_LAUNCH_FAILED;
+    return nullptr;
+  }
+  void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    // Two threads may both look the address up; they store the same value.
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      *status = MOE_ERR_LAUNCH_FAILED;
+      return nullptr;
+    }
+    scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *status = MOE_OK;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -246,6 +280,8 @@ const char* moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED: return "configuration not supported (alignment or limits)";
     case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than moe_workspace_size()";
     case MOE_ERR_LAUNCH_FAILED: return "a HIP kernel launch failed";
+    case MOE_ERR_SCRATCH_TOO_SMALL:
+      return "the call needs more workspace than the static scratch of moe_forward_noalloc holds";
     default: return "unknown status";
   }
 }
@@ -407,6 +443,22 @@ int moe_forward(const moe_config* cfg, int32_t T, const void* x, const float* to
   if (st) return st;
   return moe_forward_down(cfg, T, x, topk_w, shared_gate, counts, offsets, perm, w, y, y_act, ws,
                           ws_bytes, stream);
+}
+
+int moe_forward_noalloc(const moe_config* cfg, int32_t T, const void* x, const float* topk_w,
+                        const float* shared_gate, const int32_t* counts, const int32_t* offsets,
+                        const int32_t* perm, const moe_expert_weights* w, float* y, void* y_act,
+                        void* stream) {
+  // Every check moe_forward makes, with the workspace checked against the static
+  // scratch's size, before the scratch address is looked up or anything launched.
+  int st = check_forward(cfg, T, x, topk_w, shared_gate, counts, offsets, perm, w, y);
+  if (st || T == 0) return st;
+  if ((st = check_act_output(*cfg, y_act))) return st;
+  if (layout(*cfg, T).total > kScratchBytes) return MOE_ERR_SCRATCH_TOO_SMALL;
+  void* ws = device_scratch(&st);
+  if (!ws) return st;
+  return moe_forward(cfg, T, x, topk_w, shared_gate, counts, offsets, perm, w, y, y_act, ws, kScratchBytes,
+                     stream);
 }
 
 }  // extern "C"

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared_functions():
         assert hasattr(lib, name), name
     assert lib.moe_version() == 0x000100
-    for st in (0, -1, -2, -3, -4, -5, -6, 99):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, 99):
         assert moe.status_string(st)
 
 
@@ -216,3 +216,23 @@ def test_tile_override_accepts_documented_values(monkeypatch, value):
     monkeypatch.setenv("MOE_FORCE_TILE", value)
     for name in ("moe_forward", "moe_forward_gate_up", "moe_forward_down"):
         assert _forward(_cfg(), T=0, name=name) == OK
+
+
+def test_noalloc_forward_checks_before_launching():
+    """moe_forward_noalloc: moe_forward's argument checks, then the workspace the
+    call needs against the 64 MiB static scratch, all before any HIP call."""
+    lib = moe.lib()
+    cfg = _cfg()
+    w = moe._Weights(FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, FAKE, None, None, None)
+
+    def call(c, T, x=FAKE, y=FAKE):
+        return lib.moe_forward_noalloc(ctypes.byref(c.c()), T, x, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       ctypes.byref(w), y, None, None)
+    assert call(cfg, 4, x=None) == NULL_PTR
+    assert call(cfg, 4, y=FAKE + 4) == UNSUPPORTED
+    assert call(cfg, -1) == BAD_SHAPE
+    assert call(cfg, 0) == OK
+    # The drafter layer at T = 224 fits; at T = 4096 it needs more than 64 MiB.
+    assert _ws(cfg, 224)[1] <= moe.NOALLOC_SCRATCH_BYTES < _ws(cfg, 4096)[1]
+    assert call(cfg, 4096) == -7
+    assert "scratch" in moe.status_string(-7)

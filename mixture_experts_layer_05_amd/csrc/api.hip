@@ -64,7 +64,7 @@ int check_tokens(const moe_config* c, int32_t T) {
 }
 
 struct Layout {
-  size_t z, h, o, xq, xs, hq, hs, chunks, ranks, total;
+  size_t z, h, o, xq, xs, hq, hs, chunks, ranks, bpart, bcount, total;
   int ldz;
   int64_t zrows;   // rows of z: T per logit plane
   size_t h_shared;  // element offset of the shared expert's rows in h
@@ -88,6 +88,9 @@ Layout layout(const moe_config& c, int64_t T) {
   L.z = take(static_cast<size_t>(L.zrows) * L.ldz * sizeof(float));
   L.chunks = take(static_cast<size_t>(ceil_div(T, 1024)) * E * sizeof(int32_t));
   L.ranks = take(static_cast<size_t>(T) * c.num_experts_per_tok * sizeof(int32_t));
+  // Expert budget: fixed-point aggregates and presence flags.
+  L.bpart = take(static_cast<size_t>(E) * sizeof(unsigned long long));
+  L.bcount = take(static_cast<size_t>(E) * sizeof(int32_t));
   const size_t routed = static_cast<size_t>(T) * c.num_experts_per_tok * c.moe_intermediate_size;
   const size_t elems = routed + static_cast<size_t>(T) * c.shared_expert_intermediate_size;
   L.h_shared = routed;
@@ -347,14 +350,22 @@ int moe_route(const moe_config* cfg, int32_t T, const void* x, const void* w_rou
         static_cast<const float*>(has_shared ? w_shared_gate : w_router), T, H, E, ncols, z, L.ldz);
   }
   if ((st = launched(hipGetLastError()))) return st;
+  const bool budget_pass = cfg->expert_budget > 0 || route_stats;
+  unsigned long long* bagg = at<unsigned long long>(ws, L.bpart);
+  int32_t* bpresent = at<int32_t>(ws, L.bcount);
   topk_kernel<<<static_cast<unsigned>(ceil_div(T, 4)), 256, 0, s>>>(
       z, L.ldz, parts, plane, logit_bias, T, E, K, cfg->norm_topk_prob,
       (cfg->top_p > 0.f && cfg->top_p < 1.f) ? cfg->top_p : 0.f, has_shared ? 1 : 0, topk_ids, topk_w,
-      shared_gate);
+      shared_gate, budget_pass ? bagg : nullptr, bpresent);
   if ((st = launched(hipGetLastError()))) return st;
-  if (cfg->expert_budget > 0 || route_stats) {
-    budget_kernel<<<1, 1024, 0, s>>>(topk_ids, topk_w, T, E, K, cfg->expert_budget,
-                                     cfg->norm_topk_prob, route_stats);
+  if (budget_pass) {
+    const unsigned nchunks = static_cast<unsigned>(ceil_div(T, kBudgetChunkTokens));
+    budget_aggregate_kernel<<<nchunks, kBudgetChunkTokens, 0, s>>>(topk_ids, topk_w, T, E, K, bagg, bpresent,
+                                                                   route_stats);
+    if ((st = launched(hipGetLastError()))) return st;
+    // Without a budget only workgroup 0 runs (it writes the statistics).
+    budget_apply_kernel<<<cfg->expert_budget > 0 ? nchunks : 1u, kBudgetChunkTokens, 0, s>>>(
+        topk_ids, topk_w, T, E, K, cfg->expert_budget, cfg->norm_topk_prob, bagg, bpresent, route_stats);
     if ((st = launched(hipGetLastError()))) return st;
   }
   return MOE_OK;

@@ -68,8 +68,12 @@ __global__ void router_logits_bf16_kernel(const uint16_t*, const uint16_t*, cons
 __global__ void router_logits_f32_kernel(const float*, const float*, const float*, int, int, int, int,
                                          float*, int);
 __global__ void topk_kernel(const float*, int, int, size_t, const float*, int, int, int, int, float, int,
-                            int32_t*, float*, float*);
-__global__ void budget_kernel(int32_t*, float*, int, int, int, int, int, int32_t*);
+                            int32_t*, float*, float*, unsigned long long*, int32_t*);
+constexpr int kBudgetChunkTokens = 256;   // tokens (and threads) per workgroup of the budget passes
+__global__ void budget_aggregate_kernel(const int32_t*, const float*, int, int, int, unsigned long long*, int32_t*,
+                                        int32_t*);
+__global__ void budget_apply_kernel(int32_t*, float*, int, int, int, int, int, const unsigned long long*,
+                                    const int32_t*, int32_t*);
 
 // dispatch.hip
 __global__ void dispatch_kernel(const int32_t*, int, int, int, int32_t*, int32_t*, int32_t*);

@@ -111,7 +111,16 @@ __global__ void __launch_bounds__(256) router_logits_f32_kernel(
 __global__ void __launch_bounds__(256) topk_kernel(
     const float* __restrict__ z, int ldz, int parts, size_t plane, const float* __restrict__ bias, int T,
     int E, int K, int norm_topk, float top_p, int has_shared, int32_t* __restrict__ topk_ids,
-    float* __restrict__ topk_w, float* __restrict__ shared_gate) {
+    float* __restrict__ topk_w, float* __restrict__ shared_gate, unsigned long long* __restrict__ budget_agg,
+    int32_t* __restrict__ budget_present) {
+  // The expert budget's accumulators start at zero in every call (the budget pass
+  // runs after this kernel on the same stream).
+  if (budget_agg && blockIdx.x == 0) {
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+      budget_agg[e] = 0ull;
+      budget_present[e] = 0;
+    }
+  }
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -195,94 +204,132 @@ __global__ void __launch_bounds__(256) topk_kernel(
 
 // ------------------------------------------------------------------ expert budget
 //
-// One workgroup of 1024 threads over the whole batch.
-//  1. Aggregate gate weight per distinct expert (float64; per-wave LDS copies).
-//  2-3. Rank the experts of the union by (aggregate desc, id asc); keep rank < B.
-//  4. Per token: compact kept slots to the front in their original order, write
-//     -1 / 0 into the tail, renormalise kept weights if norm_topk (not when none
-//     is left).
-//  5. Statistics {union before, union after, dropped slots, empty tokens}.
-// With B = 0 or union <= B only the statistics are written.
-__global__ void __launch_bounds__(1024) budget_kernel(
-    int32_t* __restrict__ ids, float* __restrict__ w, int T, int E, int K, int budget,
-    int norm_topk, int32_t* __restrict__ stats) {
-  constexpr int kWaves = 16;
-  __shared__ double agg[kWaves][kMaxExperts];  // 64 KiB
-  __shared__ int present[kMaxExperts];
-  __shared__ int keep[kMaxExperts];
-  __shared__ int s_union, s_dropped, s_empty;
-  const int tid = threadIdx.x, wave = tid >> 6;
-  for (int i = tid; i < kWaves * kMaxExperts; i += 1024) (&agg[0][0])[i] = 0.0;
-  for (int e = tid; e < kMaxExperts; e += 1024) present[e] = 0;
-  if (tid == 0) { s_union = 0; s_dropped = 0; s_empty = 0; }
+// Two passes over the batch.  The aggregate gate weight of an expert is an exact
+// sum of fixed-point weights (each float32 weight rounded to a multiple of 2^-33,
+// summed as 64-bit integers), so it does not depend on the order the slots are
+// added in, and the keep-set is a pure function of the routing whatever the
+// timing.  Its distance to the float64 sum is at most T * K * 2^-34 (4e-6 at
+// 65536 slots), far inside the gaps the ranking is decided on.
+//  1. budget_aggregate_kernel, one workgroup per 256-token chunk: integer atomics
+//     into LDS per expert, then one global 64-bit atomic per touched expert (the
+//     accumulators are zeroed by the top-k kernel of the same call)
+//     [colibri issue_budget.md, "How it works" step 1];
+//  2. budget_apply_kernel, one workgroup per 256 tokens: every workgroup ranks the
+//     union by (aggregate desc, id asc) and keeps rank < B [steps 2-3] (the same
+//     few microseconds in each, instead of a third launch); then one thread per
+//     token compacts its kept slots to the front in
+//     their original order, -1 / 0 into the tail, and renormalises the kept
+//     weights if norm_topk (not when none is left) [steps 4-5].  Workgroup 0
+//     writes statistics 0-1; dropped slots and emptied tokens go into statistics
+//     2-3 by integer atomics (zeroed by the first pass).
+// With B = 0 or union <= B the routing is left as it is and only the statistics
+// {union, union, 0, 0} are written.
+constexpr int kBudgetChunk = kBudgetChunkTokens;   // tokens per workgroup of both passes
+constexpr double kBudgetFixed = 8589934592.0;   // 2^33
+
+__global__ void __launch_bounds__(kBudgetChunk) budget_aggregate_kernel(
+    const int32_t* __restrict__ ids, const float* __restrict__ w, int T, int E, int K,
+    unsigned long long* __restrict__ agg_fixed, int32_t* __restrict__ present, int32_t* __restrict__ stats) {
+  __shared__ unsigned long long lagg[kMaxExperts];
+  __shared__ int lcnt[kMaxExperts];
+  const int tid = threadIdx.x;
+  if (stats && blockIdx.x == 0 && tid < 2) stats[2 + tid] = 0;
+  for (int e = tid; e < kMaxExperts; e += kBudgetChunk) {
+    lagg[e] = 0ull;
+    lcnt[e] = 0;
+  }
   __syncthreads();
-  const int nslots = T * K;
-  const bool need_agg = budget > 0;   // without a budget only the union is counted
-  for (int s = tid; s < nslots; s += 1024) {
-    const int e = ids[s];
-    if (e >= 0) {
-      if (need_agg) atomicAdd(&agg[wave][e], static_cast<double>(w[s]));
-      present[e] = 1;
+  const size_t s0 = static_cast<size_t>(blockIdx.x) * kBudgetChunk * K;
+  const int nslot = max(0, min(kBudgetChunk, T - static_cast<int>(blockIdx.x) * kBudgetChunk)) * K;
+  for (int i = tid; i < nslot; i += kBudgetChunk) {
+    const int e = ids[s0 + i];
+    if (e >= 0 && e < E) {
+      const unsigned long long f =
+          static_cast<unsigned long long>(llrint(static_cast<double>(w[s0 + i]) * kBudgetFixed));
+      atomicAdd(&lagg[e], f);
+      lcnt[e] = 1;
     }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += 1024) {
-    double a = 0.0;
-#pragma unroll
-    for (int q = 0; q < kWaves; ++q) a += agg[q][e];
-    agg[0][e] = a;
-    if (present[e]) atomicAdd(&s_union, 1);
+  for (int e = tid; e < E; e += kBudgetChunk)
+    if (lcnt[e]) {
+      if (lagg[e]) atomicAdd(&agg_fixed[e], lagg[e]);
+      present[e] = 1;
+    }
+}
+
+__global__ void __launch_bounds__(kBudgetChunk) budget_apply_kernel(
+    int32_t* __restrict__ ids, float* __restrict__ w, int T, int E, int K, int budget, int norm_topk,
+    const unsigned long long* __restrict__ agg_fixed, const int32_t* __restrict__ present,
+    int32_t* __restrict__ stats) {
+  __shared__ double key[kMaxExperts];
+  __shared__ int keep[kMaxExperts];
+  __shared__ int s_union, s_dropped, s_empty;
+  const int tid = threadIdx.x;
+  if (tid == 0) { s_union = 0; s_dropped = 0; s_empty = 0; }
+  __syncthreads();
+  // The union ranked by (aggregate desc, id asc); an absent expert gets key -1,
+  // below every present one.
+  for (int e = tid; e < kMaxExperts; e += kBudgetChunk) {
+    const bool p = e < E && present[e] != 0;
+    key[e] = p ? static_cast<double>(agg_fixed[e]) : -1.0;
+    if (p) atomicAdd(&s_union, 1);
   }
   __syncthreads();
   const int nu = s_union;
   const bool active = budget > 0 && nu > budget;
-  if (active) {
-    for (int e = tid; e < E; e += 1024) {
-      int k = 0;
-      if (present[e]) {
-        const double a = agg[0][e];
-        int rank = 0;
-        for (int o = 0; o < E; ++o)
-          rank += (present[o] && (agg[0][o] > a || (agg[0][o] == a && o < e))) ? 1 : 0;
-        k = rank < budget;
-      }
-      keep[e] = k;
-    }
-    __syncthreads();
-    for (int t = tid; t < T; t += 1024) {
-      int32_t* ir = ids + static_cast<size_t>(t) * K;
-      float* wr = w + static_cast<size_t>(t) * K;
-      int nk = 0, nd = 0;
-      float sum = 0.f;
-      for (int k = 0; k < K; ++k) {
-        const int e = ir[k];
-        if (e < 0) continue;
-        if (keep[e]) { sum += wr[k]; ++nk; } else { ++nd; }
-      }
-      if (nd) {
-        // Compact in place: position j <= k has already been read when it is written.
-        int j = 0;
-        for (int k = 0; k < K; ++k) {
-          const int e = ir[k];
-          if (e >= 0 && keep[e]) {
-            const float v = wr[k];
-            ir[j] = e;
-            wr[j] = norm_topk ? v / sum : v;
-            ++j;
-          }
-        }
-        for (; j < K; ++j) { ir[j] = -1; wr[j] = 0.f; }
-      }
-      if (nd) atomicAdd(&s_dropped, nd);
-      if (nk == 0) atomicAdd(&s_empty, 1);
-    }
-    __syncthreads();
-  }
-  if (tid == 0 && stats) {
+  if (blockIdx.x == 0 && tid == 0 && stats) {
     stats[0] = nu;
     stats[1] = active ? budget : nu;
-    stats[2] = s_dropped;
-    stats[3] = s_empty;
+  }
+  if (!active) return;   // uniform
+  // Rank of each present expert: the present experts with a larger aggregate, or
+  // an equal one and a lower id (every thread reads the same key at a time).
+  for (int e = tid; e < E; e += kBudgetChunk) {
+    const double a = key[e];
+    int r = 0;
+    if (a >= 0.0) {
+#pragma unroll 8
+      for (int o = 0; o < E; ++o) {
+        const double b = key[o];
+        r += (b > a || (b == a && o < e)) ? 1 : 0;
+      }
+    }
+    keep[e] = (a >= 0.0 && r < budget) ? 1 : 0;
+  }
+  __syncthreads();
+  const int t = blockIdx.x * kBudgetChunk + tid;
+  if (t < T) {
+    int32_t* ir = ids + static_cast<size_t>(t) * K;
+    float* wr = w + static_cast<size_t>(t) * K;
+    int nk = 0, nd = 0;
+    float sum = 0.f;
+    for (int k = 0; k < K; ++k) {
+      const int e = ir[k];
+      if (e < 0 || e >= E) continue;
+      if (keep[e]) { sum += wr[k]; ++nk; } else { ++nd; }
+    }
+    if (nd) {
+      // Compact in place: position j <= k has already been read when it is written.
+      int j = 0;
+      for (int k = 0; k < K; ++k) {
+        const int e = ir[k];
+        if (e >= 0 && e < E && keep[e]) {
+          const float v = wr[k];
+          ir[j] = e;
+          wr[j] = norm_topk ? v / sum : v;
+          ++j;
+        }
+      }
+      for (; j < K; ++j) { ir[j] = -1; wr[j] = 0.f; }
+      atomicAdd(&s_dropped, nd);
+    }
+    if (nk == 0) atomicAdd(&s_empty, 1);
+  }
+  __syncthreads();
+  if (tid == 0 && stats) {
+    if (s_dropped) atomicAdd(&stats[2], s_dropped);
+    if (s_empty) atomicAdd(&stats[3], s_empty);
   }
 }
 

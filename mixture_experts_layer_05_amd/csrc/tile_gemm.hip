@@ -312,36 +312,72 @@ __global__ void __launch_bounds__(kPPThreads) tiledpp_expert_kernel(ExpertArgs a
       compute(ks + 1);
     }
     wait_vm<0>();                    // no load may still be writing registers or LDS
+    __syncthreads();                 // every wave is done reading the stage buffers
 
-    // 32x32 output placement: lane l, element v -> row 8 (v / 4) + 4 (l / 32) +
-    // v % 4, column l % 32.
+    // The tile leaves through LDS so that every global store is a whole row
+    // segment: 16 bytes per lane, 256 contiguous bytes (h) or 1 KiB (down) per row
+    // [the row-staged output of DeepGEMM fork PR #5, "What changed - large M", L2
+    // scatter].  32x32 output placement: lane l, element v -> row 8 (v / 4) +
+    // 4 (l / 32) + v % 4, column l % 32.
     if constexpr (MODE == Mode::GateUp) {
+      // The whole 256 x 128 bf16 h tile, rows padded to 136 elements (272 bytes:
+      // the two row halves a 32x32 store touches fall on disjoint banks).
+      constexpr int kHs = 136;
+      uint32_t* stg = reinterpret_cast<uint32_t*>(smem);
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float hv = silu_f32(acc[i][0][v]) * acc[i][1][v];
+          const uint32_t b = f32_to_bf16_bits(hv);
+          const uint32_t nb = __shfl_xor(b, 1, kWave);   // the neighbouring column
+          if ((r32 & 1) == 0) {
+            const int row = arow0 + 32 * i + 8 * (v >> 2) + 4 * hi + (v & 3);
+            stg[(row * kHs + wn * 32 + r32) / 2] = b | (nb << 16);
+          }
+        }
+      __syncthreads();
       const int width = t.shared ? a.S : a.I;
       uint16_t* hbase = static_cast<uint16_t*>(a.h) +
                         (t.shared ? static_cast<size_t>(a.h_shared) : static_cast<size_t>(t.rowbase) * width);
-      const int col = n0 + wn * 32 + r32;
+      const int piece = lane & 15;
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = t.m0 + arow0 + 32 * i + 8 * (v >> 2) + 4 * hi + (v & 3);
-          if (m < t.rows)
-            hbase[static_cast<size_t>(m) * width + col] = f32_to_bf16_bits(silu_f32(acc[i][0][v]) * acc[i][1][v]);
-        }
+      for (int k = 0; k < 8; ++k) {
+        const int row = 32 * wave + 4 * k + (lane >> 4);
+        const int m = t.m0 + row;
+        const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(smem) + row * kHs * 2 +
+                                                        piece * 16);
+        if (m < t.rows) *reinterpret_cast<uint4*>(hbase + static_cast<size_t>(m) * width + n0 + 8 * piece) = v;
+      }
+      __syncthreads();               // the next tile's first loads overwrite the staging rows
     } else {
-      const int col0 = n0 + wn * 64 + r32;
+      // Four rounds of 64 tile rows (32 from each row half) x 256 float32 columns,
+      // rows padded to 264 floats (the two row halves of a 32x32 store fall on
+      // disjoint banks).  In each round wave w stores 8 whole rows, one 1 KiB
+      // row segment per instruction.
+      constexpr int kOs = 264;
+      float* stg = reinterpret_cast<float*>(smem);
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
+      for (int i = 0; i < NI; ++i) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = t.m0 + arow0 + 32 * i + 8 * (v >> 2) + 4 * hi + (v & 3);
-          if (m < t.rows) {
+        for (int v = 0; v < 16; ++v)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            stg[(wm * 32 + 8 * (v >> 2) + 4 * hi + (v & 3)) * kOs + wn * 64 + 32 * j + r32] = acc[i][j][v];
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int R = 8 * wave + k;
+          const int m = t.m0 + (R < 32 ? 32 * i + R : 128 + 32 * i + (R - 32));
+          if (m < t.rows) {          // uniform across the wave
             const DownDst dst = down_row(a, t, m);
-            float* yr = dst.row + col0;
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) yr[32 * j] = dst.w * acc[i][j][v];
+            float4 v = *reinterpret_cast<const float4*>(stg + R * kOs + 4 * lane);
+            v.x *= dst.w; v.y *= dst.w; v.z *= dst.w; v.w *= dst.w;
+            *reinterpret_cast<float4*>(dst.row + n0 + 4 * lane) = v;
           }
         }
+        __syncthreads();
+      }
     }
   }
 }

@@ -55,6 +55,20 @@ constexpr int kXcdCount = 8;   // the tile walk assumes grids that are multiples
 // (the host limits x and h to 3 GiB), so such loads return zeros.
 constexpr uint32_t kDeadRow = 0xC0000000u;
 
+// LDS rows of a stage are stored unpadded, with the 16-byte pieces of a row
+// permuted so that both the loaders' 16-byte stores (16 lanes: one row's
+// consecutive pieces, or two 128-byte rows) and the MFMA fragment reads (16 lanes:
+// one piece of 16 consecutive rows) touch every bank once per 16 lanes.  A 256- or
+// 512-byte row keeps piece p at p ^ (row mod 16) (the low four bits; a row starts
+// at bank 0); a 128-byte row (two per 256-byte bank line) at p ^ ((row / 2) mod 8).
+// Byte offset of piece p of row `row` in rows of RB bytes.
+template <int RB>
+__device__ __forceinline__ int lds_at(int row, int p) {
+  static_assert(RB == 128 || RB == 256 || RB == 512, "row size");
+  const int q = RB == 128 ? (p ^ ((row >> 1) & 7)) : (p ^ (row & 15));
+  return row * RB + 16 * q;
+}
+
 // GateUp: h = SwiGLU(x W_gate^T, x W_up^T); Down: o / y = h W_down^T; Router: the
 // router logits z = x [W_r; w_g]^T over all T tokens (one group of T rows).
 enum class SMode { GateUp, Down, Router };
@@ -84,8 +98,8 @@ struct StreamCfg {
   static constexpr int kRowDataA = kQ ? kElems : 256;          // A bytes per row per stage
   static constexpr int kRowDataB = kMX ? kElems / 2 : kRowDataA;   // B bytes per row per stage
   static constexpr int kSub = kQ ? kElems / 128 : 4;           // MFMA k-steps per stage
-  static constexpr int kRowStrideA = kRowDataA + 8;            // padded LDS rows (8 mod 16)
-  static constexpr int kRowStrideB = kRowDataB + 8;
+  static constexpr int kRowStrideA = kRowDataA;                // unpadded LDS rows, pieces swizzled
+  static constexpr int kRowStrideB = kRowDataB;
   static constexpr int kLanesPerRowA = kRowDataA / 16;
   static constexpr int kLanesPerRowB = kRowDataB / 16;
   static constexpr int kRowsPerPassA = kLoadThreads / kLanesPerRowA;
@@ -459,10 +473,11 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
 #pragma unroll
       for (int q = 0; q < C::kAPasses; ++q)
         if (lrow + q * C::kRowsPerPassA < BM)
-          lds_st16(base + (lrow + q * C::kRowsPerPassA) * C::kRowStrideA + lcol, R.a[q]);
+          *reinterpret_cast<uint4*>(base + lds_at<C::kRowStrideA>(lrow + q * C::kRowsPerPassA, lcol / 16)) = R.a[q];
 #pragma unroll
       for (int q = 0; q < C::kBPasses; ++q)
-        lds_st16(base + C::kBOff + (lrowb + q * C::kRowsPerPassB) * C::kRowStrideB + lcolb, R.b[q]);
+        *reinterpret_cast<uint4*>(base + C::kBOff + lds_at<C::kRowStrideB>(lrowb + q * C::kRowsPerPassB, lcolb / 16)) =
+            R.b[q];
       if constexpr (FP8) {
         if (tid < C::kScales) sscale[slot * C::kScales + tid] = R.s;
       }
@@ -527,19 +542,24 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
         for (int j = 0; j < C::kCB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
 
+    // 16-byte piece p of A row (wrow0 + 16 i + r), or of B row br.
+    auto a_ld = [&](const uint8_t* base, int i, int p) {
+      return *reinterpret_cast<const uint4*>(base + lds_at<C::kRowStrideA>(wrow0 + 16 * i + r, p));
+    };
+    auto b_ld = [&](const uint8_t* base, int br, int p) {
+      return *reinterpret_cast<const uint4*>(base + C::kBOff + lds_at<C::kRowStrideB>(br, p));
+    };
     auto compute = [&](int slot) {
-      const uint8_t* As = smem + slot * C::kSlot + (wrow0 + r) * C::kRowStrideA;
-      const uint8_t* Bs = smem + slot * C::kSlot + C::kBOff;
+      const uint8_t* base = smem + slot * C::kSlot;
       if constexpr (!FP8) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           uint4 af[C::kRM], bf[C::kCB];
 #pragma unroll
-          for (int i = 0; i < C::kRM; ++i) af[i] = lds_ld16(As + 16 * i * C::kRowStrideA + 64 * s + 16 * g);
+          for (int i = 0; i < C::kRM; ++i) af[i] = a_ld(base, i, 4 * s + g);
 #pragma unroll
           for (int j = 0; j < C::kCB; ++j)
-            bf[j] = lds_ld16(Bs + stream_b_row<MODE, BN, C::kWN, C::kCB>(wn, j, r) * C::kRowStrideB + 64 * s +
-                             16 * g);
+            bf[j] = b_ld(base, stream_b_row<MODE, BN, C::kWN, C::kCB>(wn, j, r), 4 * s + g);
 #pragma unroll
           for (int i = 0; i < C::kRM; ++i)
 #pragma unroll
@@ -559,9 +579,8 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
           int sa[C::kRM], sb[C::kCB];
 #pragma unroll
           for (int i = 0; i < C::kRM; ++i) {
-            const uint8_t* p = As + 16 * i * C::kRowStrideA + 128 * s;
-            const uint4 lo = lds_ld16(p + 16 * g);
-            const uint4 hi = lds_ld16(p + 64 + 16 * g);
+            const uint4 lo = a_ld(base, i, 8 * s + g);
+            const uint4 hi = a_ld(base, i, 8 * s + 4 + g);
             af[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
             const uint32_t w = reinterpret_cast<const uint32_t*>(&sc[wrow0 + 16 * i + r])[s];
             sa[i] = static_cast<int>((w >> (8 * g)) & 0xffu);
@@ -569,7 +588,7 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
 #pragma unroll
           for (int j = 0; j < C::kCB; ++j) {
             const int br = stream_b_row<MODE, BN, C::kWN, C::kCB>(wn, j, r);
-            const uint4 v = lds_ld16(Bs + br * C::kRowStrideB + 64 * s + 16 * g);
+            const uint4 v = b_ld(base, br, 4 * s + g);
             bf[j] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
             const uint32_t w = reinterpret_cast<const uint32_t*>(&sc[BM + br])[s];
             sb[j] = static_cast<int>((w >> (8 * g)) & 0xffu);
@@ -594,9 +613,8 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
           float sb[C::kCB];
 #pragma unroll
           for (int i = 0; i < C::kRM; ++i) {
-            const uint8_t* p = As + 16 * i * C::kRowStrideA + 128 * s;
-            const uint4 lo = lds_ld16(p + 16 * g);
-            const uint4 hi = lds_ld16(p + 64 + 16 * g);
+            const uint4 lo = a_ld(base, i, 8 * s + g);
+            const uint4 hi = a_ld(base, i, 8 * s + 4 + g);
             af[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
             const int row = wrow0 + 16 * i + 4 * g;
             if constexpr (kSub == 4) {
@@ -614,9 +632,8 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
 #pragma unroll
           for (int j = 0; j < C::kCB; ++j) {
             const int br = stream_b_row<MODE, BN, C::kWN, C::kCB>(wn, j, r);
-            const uint8_t* p = Bs + br * C::kRowStrideB + 128 * s;
-            const uint4 lo = lds_ld16(p + 16 * g);
-            const uint4 hi = lds_ld16(p + 64 + 16 * g);
+            const uint4 lo = b_ld(base, br, 8 * s + g);
+            const uint4 hi = b_ld(base, br, 8 * s + 4 + g);
             bf[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
             sb[j] = scf[kSub * (BM + br) + s];
           }

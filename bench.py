@@ -50,6 +50,8 @@ def parse():
     p.add_argument("--cpu-sample-tokens", type=int, default=None)
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (the reference for HBM byte counters)")
+    p.add_argument("--library-gemm", action="store_true",
+                   help="only time torch.matmul (hipBLASLt) on dense bf16 GEMMs of the workload's expert shapes")
     return p.parse_args()
 
 
@@ -362,6 +364,33 @@ def measure(args, shape, idx, T, alpha, steps, warmup):
     return rec, {"inp": inp, "layer": layers[0], "ep_rank": ep_rank}
 
 
+def library_gemm(shape, T, reps=20):
+    """The vendor library's dense bf16 GEMM rate on this GPU for the layer's projection
+    shapes: all T*K routed rows as one matrix, and one expert's worth of T rows.
+    Context for the MFMA roofline (what a plain GEMM of the same size reaches here),
+    not a measurement of this library."""
+    import torch
+    H, I, K = shape.hidden_size, shape.moe_intermediate_size, shape.num_experts_per_tok
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    for name, (M, N, Kd) in (("gate_up, T*K rows", (T * K, 2 * I, H)), ("down, T*K rows", (T * K, H, I)),
+                             ("gate_up, T rows", (T, 2 * I, H)), ("down, T rows", (T, H, I))):
+        a = torch.randn(M, Kd, device="cuda", dtype=torch.bfloat16, generator=gen)
+        b = torch.randn(Kd, N, device="cuda", dtype=torch.bfloat16, generator=gen)
+        for _ in range(3):
+            c = a @ b
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            c = a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        print(json.dumps({"library_gemm": name, "M": M, "N": N, "K": Kd, "dtype": "bf16", "ms": round(ms, 4),
+                          "tflops": round(2 * M * N * Kd / (ms * 1e-3) / 1e12, 1)}), flush=True)
+        del a, b, c
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -390,6 +419,9 @@ def main():
         return
 
     shape, idx, T, alpha = workload(args)
+    if args.library_gemm:
+        library_gemm(shape, T)
+        return
     print(f"[bench] {shape.name} T={T} alpha={alpha}: {args.steps} steps after {args.warmup}",
           file=sys.stderr, flush=True)
     rec, ctx = measure(args, shape, idx, T, alpha, args.steps, args.warmup)

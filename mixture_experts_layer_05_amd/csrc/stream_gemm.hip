@@ -653,6 +653,9 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
     // Down tiles: the destination of each output row this lane writes (tile rows
     // wrow0 + 16i + 4g + e), fetched when the tile starts.  Routed rows go,
     // unweighted, to their slot's row of o; shared rows to y, weighted by sigmoid(g).
+    // The loaded values are left untouched until the epilogue: an instruction that
+    // used them at once would wait for every older memory operation of the wave,
+    // the previous tile's output stores included (one counter covers both).
     int dslot[MODE == SMode::Down ? C::kRM : 1][4];
     float dgate[MODE == SMode::Down ? C::kRM : 1][4];
     auto fetch_dst = [&](const Tile& d) {
@@ -664,7 +667,7 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int mc = min(t.m0 + wrow0 + 16 * i + 4 * g + e, t.rows - 1);
-            dslot[i][e] = t.shared ? a.perm[base + mc] : slot_clamp(a.perm[base + mc], a);
+            dslot[i][e] = a.perm[base + mc];
             dgate[i][e] = has_shared ? a.shared_gate[min(mc, a.T - 1)] : 1.0f;
           }
       }
@@ -711,7 +714,7 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
             const int m = t.m0 + wrow0 + 16 * i + 4 * g + e;
             if (m < t.rows) {
               float* row = t.shared ? a.y + static_cast<size_t>(m) * H
-                                    : a.o + static_cast<size_t>(dslot[i][e]) * H;
+                                    : a.o + static_cast<size_t>(slot_clamp(dslot[i][e], a)) * H;
               const float w = t.shared ? dgate[i][e] : 1.0f;
 #pragma unroll
               for (int j = 0; j < C::kCB; ++j)

@@ -222,6 +222,18 @@ __global__ void __launch_bounds__(kPPThreads) tiledpp_expert_kernel(ExpertArgs a
     const __amdgpu_buffer_rsrc_t rb0v = buf_rsrc(b0p, 128 * krow);
     const __amdgpu_buffer_rsrc_t rb1v = buf_rsrc(b1p, 128 * krow);
     const uint32_t bvoff = static_cast<uint32_t>(tid >> 3) * krow + (tid & 7) * 16;
+    // Down: the destinations of the 32 rows this wave stores in the epilogue (lane
+    // l < 32: round l / 8, row 8 wave + l % 8 of it), loaded here and not touched
+    // before the epilogue.  A load issued between the epilogue's stores would make
+    // the wave wait for those stores (one counter covers loads and stores).
+    int pre_slot = 0;
+    float pre_w = 1.0f;
+    if constexpr (MODE == Mode::Down) {
+      const int l = lane & 31, R = 8 * wave + (l & 7), ri = l >> 3;
+      const int m = min(t.m0 + (R < 32 ? 32 * ri + R : 128 + 32 * ri + (R - 32)), t.rows - 1);
+      pre_slot = a.perm[t.rowbase + m];
+      if (t.shared) pre_w = a.shared_gate[m];
+    }
 
     auto issue_a = [&](int ks) {
       const uint32_t buf = lds0 + static_cast<uint32_t>(ks & 1) * kT4Stage + 4 * wave * 1024;
@@ -369,11 +381,14 @@ __global__ void __launch_bounds__(kPPThreads) tiledpp_expert_kernel(ExpertArgs a
         for (int k = 0; k < 8; ++k) {
           const int R = 8 * wave + k;
           const int m = t.m0 + (R < 32 ? 32 * i + R : 128 + 32 * i + (R - 32));
+          const int slot = __shfl(pre_slot, 8 * i + k, kWave);
+          const float w = __shfl(pre_w, 8 * i + k, kWave);
           if (m < t.rows) {          // uniform across the wave
-            const DownDst dst = down_row(a, t, m);
+            float* row = t.shared ? a.y + static_cast<size_t>(m) * a.H
+                                  : a.o + static_cast<size_t>(slot_clamp(slot, a)) * a.H;
             float4 v = *reinterpret_cast<const float4*>(stg + R * kOs + 4 * lane);
-            v.x *= dst.w; v.y *= dst.w; v.z *= dst.w; v.w *= dst.w;
-            *reinterpret_cast<float4*>(dst.row + n0 + 4 * lane) = v;
+            v.x *= w; v.y *= w; v.z *= w; v.w *= w;
+            *reinterpret_cast<float4*>(row + n0 + 4 * lane) = v;
           }
         }
         __syncthreads();
@@ -505,6 +520,17 @@ __global__ void __launch_bounds__(kF8PPThreads) tiled8pp_expert_kernel(ExpertArg
 #pragma unroll
       for (int h = 0; h < 2; ++h) boff[h] = static_cast<uint32_t>(drow) * krow + dpiece[h];
     }
+    // Down: the destinations of the wave's 64 output rows (lane l: row 64 wm + l),
+    // loaded here and not touched before the epilogue (a load issued between the
+    // epilogue's stores would make the wave wait for them).
+    int pre_slot = 0;
+    float pre_w = 1.0f;
+    if constexpr (MODE == Mode::Down) {
+      const int m = min(t.m0 + wm * 64 + lane, t.rows - 1);
+      pre_slot = a.perm[t.rowbase + m];
+      if (t.shared) pre_w = a.shared_gate[m];
+    }
+
     // The scale vector this wave stages: waves 0-3 the activation rows
     // [64 wave, +64); waves 4-7 the weight half (wave & 1).
     const bool a_scales = wave < 4;
@@ -627,11 +653,13 @@ __global__ void __launch_bounds__(kF8PPThreads) tiled8pp_expert_kernel(ExpertArg
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int m = t.m0 + wm * 64 + 16 * i + 4 * g + e;
+          const int slot = __shfl(pre_slot, 16 * i + 4 * g + e, kWave);
+          const float w = __shfl(pre_w, 16 * i + 4 * g + e, kWave);
           if (m < t.rows) {
-            const DownDst dst = down_row(a, t, m);
-            float* yr = dst.row + col0;
+            float* yr = (t.shared ? a.y + static_cast<size_t>(m) * a.H
+                                  : a.o + static_cast<size_t>(slot_clamp(slot, a)) * a.H) + col0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) yr[16 * j] = dst.w * acc[i][j][e];
+            for (int j = 0; j < 4; ++j) yr[16 * j] = w * acc[i][j][e];
           }
         }
     }

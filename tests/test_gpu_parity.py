@@ -453,6 +453,19 @@ def test_routing_is_deterministic():
     assert np.array_equal(a["y"], b["y"])   # no atomics: bit-reproducible
 
 
+def test_split_budget_path_is_deterministic():
+    """The rows-divided (256-row + streaming) kernels with fp8 weights and the
+    expert budget, twice on the same inputs: routing, the budget's keep-set
+    (order-independent fixed-point aggregates) and y are bit-identical
+    [colibri issue_budget.md, "How it works"]."""
+    case = Hn.make_case(W.LARGE_FP8, 512, W.base_seed(4, 512), 1.5)
+    a = Hn.run_gpu(case)
+    b = Hn.run_gpu(case)
+    for k in ("ids", "w", "counts", "offsets", "perm", "stats"):
+        assert np.array_equal(a[k], b[k]), k
+    assert np.array_equal(a["y"], b["y"])
+
+
 def test_halves_equal_forward():
     import mixture_experts_layer_05_amd as moe
     case = Hn.make_case(W.DRAFTER, 56, 13)

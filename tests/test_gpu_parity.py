@@ -553,6 +553,38 @@ def test_seeded_shape_sweep(shape, T, seed):
     _run(shape, T, seed)
 
 
+def _large_sweep_shapes(n=9, seed=11):
+    """Larger random layers whose calls divide their rows between the 256-row and the
+    streaming kernels (bf16, fp8: at least 16 rows per expert and T*K*I of at least
+    twice 256 x 256 x 128) or run the 128-row streaming tiles (MXFP4), with Zipf
+    router skew, shared expert, budget and top-p drawn at random.  H is a multiple
+    of 512, so the fp8 and MXFP4 decode stages take their widest forms."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dt = (W.DT_BF16, W.DT_FP8, W.DT_MXFP4)[i % 3]
+        H = int(rng.choice([512, 1024, 1536]))
+        I = int(rng.choice([512, 1024]))
+        E = int(rng.integers(8, 33))
+        K = int(rng.integers(2, 9))
+        S = int(rng.choice([0, 256, 512]))
+        T = int(rng.choice([2048, 3072, 4096]))
+        while T * K * I < 2 * 256 * 256 * 128 or T * K // E < 16:
+            K = min(K + 1, E)
+            T *= 2
+        alpha = float(rng.choice([0.0, 1.0, 1.5]))
+        budget = int(rng.integers(max(1, E // 2), E + 1)) if rng.random() < 0.3 else 0
+        top_p = float(np.round(rng.uniform(0.5, 0.9), 2)) if rng.random() < 0.3 else 0.0
+        shape = W.LayerShape(f"lsweep{i}_{dt}", H, E, I, K, S, dt, W.DT_BF16, expert_budget=budget, top_p=top_p)
+        out.append((shape, T, 900 + i, alpha))
+    return out
+
+
+@pytest.mark.parametrize("shape,T,seed,alpha", _large_sweep_shapes(), ids=lambda v: getattr(v, "name", str(v)))
+def test_seeded_large_shape_sweep(shape, T, seed, alpha):
+    _run(shape, T, seed, alpha, tokens=48)
+
+
 def test_graph_capture_replays_match_eager():
     """route -> dispatch -> forward captured once into a HIP graph: the library
     launches on the caller's stream with no host synchronisation, copy back or

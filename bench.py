@@ -364,31 +364,37 @@ def measure(args, shape, idx, T, alpha, steps, warmup):
     return rec, {"inp": inp, "layer": layers[0], "ep_rank": ep_rank}
 
 
+def dense_gemm_ms(M, N, K, reps=20):
+    """Average time of torch.matmul (hipBLASLt) on a dense bf16 [M, K] x [K, N]
+    product, with HIP events on torch's stream after 3 warm-up calls."""
+    import torch
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16, generator=gen)
+    b = torch.randn(K, N, device="cuda", dtype=torch.bfloat16, generator=gen)
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    del a, b, c
+    return e0.elapsed_time(e1) / reps
+
+
 def library_gemm(shape, T, reps=20):
     """The vendor library's dense bf16 GEMM rate on this GPU for the layer's projection
     shapes: all T*K routed rows as one matrix, and one expert's worth of T rows.
     Context for the MFMA roofline (what a plain GEMM of the same size reaches here),
     not a measurement of this library."""
-    import torch
     H, I, K = shape.hidden_size, shape.moe_intermediate_size, shape.num_experts_per_tok
-    gen = torch.Generator(device="cuda").manual_seed(0)
     for name, (M, N, Kd) in (("gate_up, T*K rows", (T * K, 2 * I, H)), ("down, T*K rows", (T * K, H, I)),
                              ("gate_up, T rows", (T, 2 * I, H)), ("down, T rows", (T, H, I))):
-        a = torch.randn(M, Kd, device="cuda", dtype=torch.bfloat16, generator=gen)
-        b = torch.randn(Kd, N, device="cuda", dtype=torch.bfloat16, generator=gen)
-        for _ in range(3):
-            c = a @ b
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            c = a @ b
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
+        ms = dense_gemm_ms(M, N, Kd, reps)
         print(json.dumps({"library_gemm": name, "M": M, "N": N, "K": Kd, "dtype": "bf16", "ms": round(ms, 4),
                           "tflops": round(2 * M * N * Kd / (ms * 1e-3) / 1e12, 1)}), flush=True)
-        del a, b, c
 
 
 def main():
@@ -440,6 +446,14 @@ def main():
         "data": "synthetic (seeded; random-init weights)",
     }
     line.update({k: v for k, v in rec.items() if k not in ("ms_per_step", "tokens_per_s", "dtype")})
+    if rec["roofline"]["bound"] == "mfma" and shape.weight_dtype == W.DT_BF16 and not ctx["ep_rank"]:
+        # Context for the MFMA fraction: the vendor library's dense bf16 GEMM over the
+        # same number of rows (all T*K routed rows as one matrix, no routing).
+        M, N, Kd = T * shape.num_experts_per_tok, 2 * shape.moe_intermediate_size, shape.hidden_size
+        lib_tf = 2 * M * N * Kd / (dense_gemm_ms(M, N, Kd) * 1e-3) / 1e12
+        line["library_gemm"] = {"kind": "torch.matmul (hipBLASLt), dense bf16 [T*K, H] x [H, 2I]",
+                                "tflops": round(lib_tf, 1), "frac_of_peak": round(lib_tf / rec["roofline"]["peak"], 4),
+                                "gate_up_stage_vs_library": round(rec["gate_up_tflops"] / lib_tf, 4)}
     if not args.no_decode and args.workload == "large":
         # The decode record: the drafter layer at T = 224, HBM-bound.  Its steps are
         # ~0.2 ms, so it runs ten times the headline's step count.

@@ -798,6 +798,12 @@ hipError_t launch_stream_rho(const ExpertArgs& a, int64_t rho, hipStream_t strea
   const int64_t n_out = (MODE == SMode::GateUp) ? a.I : a.H;
   const int64_t tiles128 = touched * (MODE == SMode::GateUp ? n_out / 64 : n_out / 128);
   const bool narrow = MODE == SMode::GateUp && tiles128 < 3 * 256;
+  // Down tiles of 64 weight rows only where 128-row ones would leave most CUs
+  // without a tile (fewer than 256 of them), for bf16 and fp8 weights: the
+  // one-token drafter step's down projection ran 17 % (bf16) and 13 % (fp8)
+  // faster; from 7 tokens on they were no faster, at 56 and 224 tokens slower
+  // (8 %, 13 %), and with MXFP4 weights 3 % slower at one token.
+  const bool narrow_down = MODE == SMode::Down && tiles128 < 256 && FMT != kDtypeMxfp4 && FMT != kMxWide;
   // From kStreamTallRows rows per expert: 128 x 128 tiles (MXFP4 in 256-element
   // stages: the 512-element form of this tile does not fit LDS).  For MXFP4 they
   // give 33 % more flops per loaded byte than 64 x 128 in 512-element stages and
@@ -805,6 +811,9 @@ hipError_t launch_stream_rho(const ExpertArgs& a, int64_t rho, hipStream_t strea
   // faster than 128-row LDS-tiled kernels between 48 and 160 rows per expert.
   if (rho >= kStreamTallRows)
     return launch_stream<MODE, 128, 128, 2, fit_fmt<FMT, 128, 128>()>(a, stream);
+  if constexpr (MODE == SMode::Down) {
+    if (rho <= 12 && narrow_down) return launch_stream<MODE, 16, 64, 1, fit_fmt<FMT, 16, 64>()>(a, stream);
+  }
   if (rho <= 12) return launch_stream<MODE, 16, 128, 1, fit_fmt<FMT, 16, 128>()>(a, stream);
   if (rho <= 24) return narrow ? launch_stream<MODE, 32, 64, 2, fit_fmt<FMT, 32, 64>()>(a, stream)
                                : launch_stream<MODE, 32, 128, 1, fit_fmt<FMT, 32, 128>()>(a, stream);

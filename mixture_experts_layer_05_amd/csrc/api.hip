@@ -64,11 +64,32 @@ int check_tokens(const moe_config* c, int32_t T) {
 }
 
 struct Layout {
-  size_t z, h, o, xq, xs, hq, hs, chunks, ranks, bpart, bcount, total;
+  size_t z, h, o, xq, xs, hq, hs, chunks, ranks, bpart, bcount, gpart, total;
   int ldz;
   int64_t zrows;   // rows of z: T per logit plane
   size_t h_shared;  // element offset of the shared expert's rows in h
 };
+
+// Bytes of the partial gate/up sums that any call of at most T tokens needs (the
+// largest contraction-split count times one part's floats over T' <= T, so the size
+// is monotone in T).  A split needs fewer 64-column tiles than CUs, so beyond
+// t_hi = 256 * 64 / (I K) tokens only a layer whose experts alone give fewer than
+// 256 tiles can split; for those the bound 16 parts of the largest call is taken.
+size_t gate_up_part_bytes(const moe_config& c, int64_t T) {
+  const int K = std::max(c.num_experts_per_tok, 1), E = c.n_routed_experts;
+  const int I = c.moe_intermediate_size, S = c.shared_expert_intermediate_size;
+  const int64_t t_rho = int64_t{48} * E / K + 1;                   // rows per expert below 48
+  const int64_t t_hi = ceil_div(int64_t{256} * 64, static_cast<int64_t>(std::max(I, 1)) * K);
+  const bool few_tiles = static_cast<int64_t>(E) * (I / 64) < 256;
+  const int64_t scan = std::min<int64_t>(T, few_tiles ? std::min<int64_t>(t_rho, 512) : std::min(t_rho, t_hi));
+  size_t need = 0;
+  for (int64_t t = 1; t <= scan; ++t) {
+    const int p = gate_up_kparts(t, K, E, c.hidden_size, I, S, c.weight_dtype);
+    if (p > 1) need = std::max(need, p * gate_up_part_floats(t, K, I, S));
+  }
+  if (few_tiles && std::min(T, t_rho) > scan) need = std::max(need, 16 * gate_up_part_floats(std::min(T, t_rho), K, I, S));
+  return need * sizeof(float);
+}
 
 Layout layout(const moe_config& c, int64_t T) {
   Layout L{};
@@ -97,6 +118,7 @@ Layout layout(const moe_config& c, int64_t T) {
   const size_t hsize = (c.weight_dtype == MOE_DTYPE_BF16) ? 2 : 4;
   L.h = take(elems * hsize);
   L.o = take(static_cast<size_t>(T) * c.num_experts_per_tok * c.hidden_size * sizeof(float));
+  L.gpart = take(gate_up_part_bytes(c, T));   // decode-sized calls' contraction split
   if (c.weight_dtype == MOE_DTYPE_FP8_E4M3_G128) {
     L.xq = take(static_cast<size_t>(T) * c.hidden_size);
     L.xs = take(static_cast<size_t>(T) * (c.hidden_size / kGroup) * sizeof(float));
@@ -224,6 +246,8 @@ ExpertArgs expert_args(const moe_config& c, int32_t T, const void* x, const floa
   }
   a.o = at<float>(ws, L.o);
   a.split = 0;
+  a.kparts = 1;   // the gate/up launcher sets the contraction split
+  a.gpart = at<float>(ws, L.gpart);
   tile_override(c, &a.force_tile);   // validated by check_forward
   a.y = y;
   a.T = T;

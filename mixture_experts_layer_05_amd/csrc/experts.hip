@@ -331,7 +331,9 @@ hipError_t launch_gate_up(const ExpertArgs& a, int weight_dtype, hipStream_t str
     if (e != hipSuccess) return e;
     return launch_gate_up_stream(rest, weight_dtype, rest_rows(rho), stream);
   }
-  return launch_gate_up_stream(a, weight_dtype, rho, stream);
+  ExpertArgs s = a;
+  s.kparts = gate_up_kparts(a.T, a.K, a.E, a.H, a.I, a.S, weight_dtype);
+  return launch_gate_up_stream(s, weight_dtype, rho, stream);
 }
 
 hipError_t launch_down(const ExpertArgs& a, int weight_dtype, hipStream_t stream) {

@@ -49,6 +49,12 @@ struct ExpertArgs {
   // 16, 32, 64 or 128 = the streaming kernel alone with tiles of that many rows;
   // kForceSplit = rows divided between the 256-row and the streaming kernels.
   int force_tile;
+  // Contraction split of a gate/up streaming launch (1: none).  Each tile then
+  // covers 1/kparts of the contraction and writes its raw gate and up sums,
+  // float32, to part p of gpart (layout: gate_up_part_floats); a finishing pass
+  // adds the parts in order p = 0, 1, ... and applies SwiGLU.
+  int kparts;
+  float* gpart;
   void* y_act;                   // [T, H] act dtype or null: the cast of y
   int act_bf16;                  // y_act is bf16 (else float32)
   // Router logits (router mode of the streaming kernel): z[t, c] = x_t . col_c with
@@ -95,6 +101,15 @@ bool tall_tiles_fit(const ExpertArgs& a);
 hipError_t launch_gate_up_tall(const ExpertArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_down_tall(const ExpertArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_gate_up_stream(const ExpertArgs& a, int weight_dtype, int64_t rho, hipStream_t stream);
+// Contraction parts of a call's gate/up streaming launch (1: unsplit; see
+// stream_gemm.hip).
+int gate_up_kparts(int64_t T, int K, int E, int H, int I, int S, int weight_dtype);
+// Floats of one contraction part's partial sums: per routed dispatch row (T*K
+// rows) 2*I values, the I gate sums then the I up sums; then per shared-expert row
+// (T rows) 2*S values.
+__host__ __device__ inline size_t gate_up_part_floats(int64_t T, int K, int I, int S) {
+  return static_cast<size_t>(T) * K * 2 * I + static_cast<size_t>(T) * 2 * S;
+}
 hipError_t launch_down_stream(const ExpertArgs& a, int weight_dtype, int64_t rho, hipStream_t stream);
 hipError_t launch_combine(const ExpertArgs& a, hipStream_t stream);
 hipError_t launch_router_stream(const ExpertArgs& a, hipStream_t stream);

@@ -241,6 +241,9 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
   const int G = a.E + (has_shared ? 1 : 0);
   const int H = a.H;
   const int bn_cols = (MODE == SMode::GateUp) ? BN / 2 : BN;
+  // Contraction parts per (group, m-tile, n-tile) of a gate/up launch: tile index
+  // n' = P n + p covers n-tile n over the p-th 1/P of the contraction.
+  const int P = (MODE == SMode::GateUp) ? max(1, a.kparts) : 1;
   const size_t esz = FP8 ? 1 : 2;   // bytes per A (activation) element
   // Bytes of one weight row of `k` elements.
   auto b_row_bytes = [&](int k) -> size_t { return MX ? static_cast<size_t>(k) / 2 : static_cast<size_t>(k) * esz; };
@@ -252,11 +255,11 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
     walk = Walk{total * xcd / 8 + static_cast<int>(blockIdx.x / 8), total * (xcd + 1) / 8,
                 static_cast<int>(gridDim.x / 8)};
   } else {
-    const int nt_r = (MODE == SMode::GateUp) ? a.I / bn_cols : H / bn_cols;
-    const int nt_s = has_shared ? ((MODE == SMode::GateUp) ? a.S / bn_cols : H / bn_cols) : 0;
+    const int nt_r = ((MODE == SMode::GateUp) ? a.I / bn_cols : H / bn_cols) * P;
+    const int nt_s = has_shared ? ((MODE == SMode::GateUp) ? a.S / bn_cols : H / bn_cols) * P : 0;
     build_tile_prefix(sched, a.counts, a.offsets, a.E, a.T, has_shared, BM, nt_r, nt_s, a.split);
-    const int nk_r = ((MODE == SMode::GateUp) ? H : a.I) / C::kElems;
-    const int nk_s = ((MODE == SMode::GateUp) ? H : a.S) / C::kElems;
+    const int nk_r = ((MODE == SMode::GateUp) ? H : a.I) / C::kElems / P;
+    const int nk_s = ((MODE == SMode::GateUp) ? H : a.S) / C::kElems / P;
     walk = balanced_walk<CostT>(sched, cpre, G, a.E, nk_r, nk_s);
   }
   if (walk.tile >= walk.end) return;   // uniform across the workgroup
@@ -265,6 +268,7 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
   struct Tile {
     TileInfo t;
     int kdim, nk, n0;
+    int part, kb;   // contraction part and its first stage
   };
   // gc: the caller's group cursor (a group at or before the tile's; tiles only move
   // forward, so each role keeps one and the lookup scans forward from it).
@@ -284,7 +288,10 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
       d.t = tile_in_group(sched, gc, tile, a, BM);
     }
     d.kdim = (MODE != SMode::Down) ? H : (d.t.shared ? a.S : a.I);
-    d.nk = d.kdim / C::kElems;
+    d.part = d.t.nt % P;
+    d.t.nt /= P;
+    d.nk = d.kdim / C::kElems / P;
+    d.kb = d.part * d.nk;
     d.n0 = d.t.nt * bn_cols;
     return d;
   };
@@ -301,8 +308,8 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
   const int ntiles = (last - walk.tile) / walk.step + 1;
   int nstages = ntiles * (H / C::kElems);
   if constexpr (MODE != SMode::Router) {
-    const int nk_r = ((MODE == SMode::GateUp) ? H : a.I) / C::kElems;
-    const int nk_s = ((MODE == SMode::GateUp) ? H : a.S) / C::kElems;
+    const int nk_r = ((MODE == SMode::GateUp) ? H : a.I) / C::kElems / P;
+    const int nk_s = ((MODE == SMode::GateUp) ? H : a.S) / C::kElems / P;
     const int first_shared = has_shared ? sched[a.E] : walk.end;
     const int skip = first_shared <= walk.tile ? 0 : (first_shared - walk.tile + walk.step - 1) / walk.step;
     const int n_shared = max(0, ntiles - skip);
@@ -493,7 +500,7 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
     Tile nld = make_tile(min(walk.tile + walk.step, last), lg);
     Pend np = fetch(nld);
     auto issue = [&](Regs& R) {
-      gload(R, lb, ls, ld_ks);
+      gload(R, lb, ls, ld.kb + ld_ks);
       if (ld_ks + 1 < ld.nk) {
         ++ld_ks;
       } else if (ld_tile < last) {
@@ -689,6 +696,27 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
           }
       } else if constexpr (MODE == SMode::GateUp) {
         const int width = t.shared ? a.S : a.I;
+        if (P > 1) {
+          // Raw gate and up sums of this contraction part (gate_up_part_floats layout).
+          float* part = a.gpart + static_cast<size_t>(d.part) * gate_up_part_floats(a.T, a.K, a.I, a.S) +
+                        (t.shared ? static_cast<size_t>(a.T) * a.K * 2 * a.I : 0);
+#pragma unroll
+          for (int i = 0; i < C::kRM; ++i)
+#pragma unroll
+            for (int jh = 0; jh < C::kCB / 2; ++jh) {
+              const int col = d.n0 + wn * (BN / (2 * C::kWN)) + 16 * jh + r;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int m = t.m0 + wrow0 + 16 * i + 4 * g + e;
+                if (m < t.rows) {
+                  float* prow = part + static_cast<size_t>(t.shared ? m : t.rowbase + m) * 2 * width;
+                  prow[col] = acc[i][jh][e];
+                  prow[width + col] = acc[i][jh + C::kCB / 2][e];
+                }
+              }
+            }
+          return;
+        }
 #pragma unroll
         for (int i = 0; i < C::kRM; ++i)
 #pragma unroll
@@ -747,6 +775,45 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
   }
 }
 
+// Finishing pass of a contraction-split gate/up launch: the parts' gate and up
+// sums are added in order p = 0, 1, ... and h = SwiGLU is written where the
+// unsplit kernel writes it.  Routed dispatch rows [0, offsets[E]) (I columns),
+// then the shared expert's T rows (S columns); four columns per thread.
+template <bool H_F32>
+__global__ void __launch_bounds__(256) gate_up_finish_kernel(ExpertArgs a) {
+  const size_t pf = gate_up_part_floats(a.T, a.K, a.I, a.S);
+  const size_t shared0 = static_cast<size_t>(a.T) * a.K * 2 * a.I;
+  const int64_t routed = static_cast<int64_t>(a.offsets[a.E]) * (a.I / 4);
+  const int64_t items = routed + (a.S > 0 ? static_cast<int64_t>(a.T) * (a.S / 4) : 0);
+  for (int64_t it = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; it < items;
+       it += static_cast<int64_t>(gridDim.x) * 256) {
+    const bool sh = it >= routed;
+    const int64_t j = sh ? it - routed : it;
+    const int width = sh ? a.S : a.I;
+    const int64_t row = j / (width / 4);
+    const int c = static_cast<int>(j - row * (width / 4)) * 4;
+    const float* src = a.gpart + (sh ? shared0 : 0) + static_cast<size_t>(row) * 2 * width + c;
+    float4 gs = *reinterpret_cast<const float4*>(src);
+    float4 us = *reinterpret_cast<const float4*>(src + width);
+    for (int p = 1; p < a.kparts; ++p) {
+      const float4 gv = *reinterpret_cast<const float4*>(src + p * pf);
+      const float4 uv = *reinterpret_cast<const float4*>(src + p * pf + width);
+      gs.x += gv.x; gs.y += gv.y; gs.z += gv.z; gs.w += gv.w;
+      us.x += uv.x; us.y += uv.y; us.z += uv.z; us.w += uv.w;
+    }
+    const float hv[4] = {silu_f32(gs.x) * us.x, silu_f32(gs.y) * us.y, silu_f32(gs.z) * us.z,
+                         silu_f32(gs.w) * us.w};
+    const size_t idx = sh ? a.h_shared + static_cast<size_t>(row) * a.S + c : static_cast<size_t>(row) * a.I + c;
+    if constexpr (H_F32) {
+      *reinterpret_cast<float4*>(static_cast<float*>(a.h) + idx) = float4{hv[0], hv[1], hv[2], hv[3]};
+    } else {
+      const uint32_t lo = f32_to_bf16_bits(hv[0]) | (static_cast<uint32_t>(f32_to_bf16_bits(hv[1])) << 16);
+      const uint32_t hi = f32_to_bf16_bits(hv[2]) | (static_cast<uint32_t>(f32_to_bf16_bits(hv[3])) << 16);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.h) + idx) = uint2{lo, hi};
+    }
+  }
+}
+
 // Upper bound of the tile count (host side; the device computes the exact one).
 int64_t stream_tiles(const ExpertArgs& a, int BM, int nt_routed, int nt_shared) {
   const int64_t slots = static_cast<int64_t>(a.T) * a.K;
@@ -768,7 +835,8 @@ hipError_t launch_stream(const ExpertArgs& a, hipStream_t stream) {
   const int bn_cols = (MODE == SMode::GateUp) ? BN / 2 : BN;
   const int nt_r = (MODE == SMode::GateUp) ? a.I / bn_cols : a.H / bn_cols;
   const int nt_s = (MODE == SMode::GateUp) ? a.S / bn_cols : a.H / bn_cols;
-  const int grid = stream_grid(stream_tiles(a, BM, nt_r, nt_s));
+  const int parts = (MODE == SMode::GateUp) ? std::max(1, a.kparts) : 1;
+  const int grid = stream_grid(stream_tiles(a, BM, nt_r, nt_s) * parts);
   stream_expert_kernel<MODE, BM, BN, WM, FMT, NS><<<grid, kStreamThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
@@ -791,8 +859,42 @@ constexpr int fit_fmt() {
   return FMT == kMxWide && BM + BN > 192 ? kDtypeMxfp4 : (FMT == kFp8Quad && BM + BN > 144) ? kFp8Wide : FMT;
 }
 
+// Contraction split of the gate/up projection for calls too small to give every
+// CU a tile: one or a few tokens touch few experts, and with 64 intermediate
+// columns per tile the launch has fewer tiles than CUs (the one-token drafter step:
+// 64).  Each tile is cut into P parts of the contraction (P divides H/128, or
+// H/512 with fp8 weights, so that the parts end on stage boundaries of every
+// stage form), so that ~P times more CUs stream the weights; the parts write raw
+// gate and up sums and gate_up_finish_kernel adds them in fixed order and applies
+// SwiGLU.  P minimises an estimate of the stages the busiest CU runs.  Measured
+// (drafter gate/up): T = 1 40.9 -> 25.5 us, T = 2 43.6 -> 33.5, T = 4 43.6 ->
+// 33.2, fp8 T = 1 34.0 -> 30.2, narrow layer T = 1 51.4 -> 42.0; calls with at
+// least as many tiles as CUs are not split (at T = 224 a split ran slower: the
+// partial sums and the second launch cost more than the balance gains).
+int split_tile_rows(int64_t rho) { return rho <= 12 ? 16 : rho <= 24 ? 32 : 64; }
+
+template <int FMT>
+hipError_t launch_gate_up_split(const ExpertArgs& a, int64_t rho, hipStream_t stream) {
+  constexpr SMode M = SMode::GateUp;
+  hipError_t e;
+  switch (split_tile_rows(rho)) {
+    case 16: e = launch_stream<M, 16, 128, 1, fit_fmt<FMT, 16, 128>()>(a, stream); break;
+    case 32: e = launch_stream<M, 32, 128, 1, fit_fmt<FMT, 32, 128>()>(a, stream); break;
+    default: e = launch_stream<M, 64, 128, 1, fit_fmt<FMT, 64, 128>()>(a, stream); break;
+  }
+  if (e != hipSuccess) return e;
+  const int64_t items = static_cast<int64_t>(a.T) * a.K * (a.I / 4) + static_cast<int64_t>(a.T) * (a.S / 4);
+  const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(ceil_div(items, 256), 4096)));
+  if (FMT == kDtypeBf16) gate_up_finish_kernel<false><<<grid, 256, 0, stream>>>(a);
+  else gate_up_finish_kernel<true><<<grid, 256, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
 template <SMode MODE, int FMT>
 hipError_t launch_stream_rho(const ExpertArgs& a, int64_t rho, hipStream_t stream) {
+  if constexpr (MODE == SMode::GateUp) {
+    if (a.kparts > 1) return launch_gate_up_split<FMT>(a, rho, stream);
+  }
   const int64_t slots = static_cast<int64_t>(a.T) * a.K;
   const int64_t touched = std::min<int64_t>(a.E, slots);
   const int64_t n_out = (MODE == SMode::GateUp) ? a.I : a.H;
@@ -822,6 +924,28 @@ hipError_t launch_stream_rho(const ExpertArgs& a, int64_t rho, hipStream_t strea
 }
 
 }  // namespace
+
+int gate_up_kparts(int64_t T, int K, int E, int H, int I, int S, int weight_dtype) {
+  // bf16 and fp8 weights (MXFP4's one-token gate/up, at 0.25 of the bf16 bytes,
+  // measured no faster split).
+  if (weight_dtype != kDtypeBf16 && weight_dtype != kDtypeFp8) return 1;
+  const int unit = weight_dtype == kDtypeBf16 ? 128 : 512;   // contraction elements per part step
+  if (T <= 0 || E <= 0 || H % unit != 0 || I % 64 != 0 || S % 64 != 0) return 1;
+  const int64_t rho = T * K / E;
+  if (rho >= kStreamTallRows) return 1;
+  const int64_t touched = std::min<int64_t>(E, T * K);
+  const int64_t tiles = touched * (I / 64) + (S > 0 ? ceil_div(T, split_tile_rows(rho)) * (S / 64) : 0);
+  if (tiles >= 256) return 1;
+  // Estimated time in 256-byte row steps: rounds of work items over the 256 CUs,
+  // each item its share of a weight row's bytes plus ~2 steps of pipeline fill.
+  const int q = H / unit;
+  const int64_t nk = weight_dtype == kDtypeBf16 ? H / 128 : H / 256;
+  auto cost = [&](int p) { return ceil_div(tiles * p, 256) * (nk / p + 2); };
+  int best = 1;
+  for (int p = 2; p <= 16; ++p)
+    if (q % p == 0 && cost(p) < cost(best)) best = p;
+  return best;
+}
 
 hipError_t launch_router_stream(const ExpertArgs& a, hipStream_t stream) {
   const int grid = stream_grid(ceil_div(a.T, 64) * ceil_div(a.ncols, 128));

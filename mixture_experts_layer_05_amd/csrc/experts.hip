@@ -322,8 +322,25 @@ bool split_call(const ExpertArgs& a, int weight_dtype, int64_t rho) {
 // per expert it is given: from 192 rows per expert on average that share is mostly
 // short tails and cold groups, which 64-row tiles serve better (5 % faster at
 // T = 8192, alpha = 0, measured); below, it holds groups just short of 128 rows,
-// which 128-row tiles serve better (12 % at T = 4096, alpha = 0).
+// which 128-row tiles serve better (12 % at T = 4096, alpha = 0).  From 192 rows
+// the share is divided once more by group (schedule.h, splits 3 and 4): groups
+// left with more than 64 rows take 128-row tiles, the rest 64-row ones.
 int64_t rest_rows(int64_t rho) { return rho >= 192 ? 47 : rho; }
+constexpr int64_t kMidTileRho = 48;   // selects 128-row streaming tiles
+
+template <typename F>
+hipError_t launch_rest(const ExpertArgs& a, int weight_dtype, int64_t rho, F&& launch) {
+  ExpertArgs rest = a;
+  if (rest_rows(rho) == rho) {
+    rest.split = 2;
+    return launch(rest, weight_dtype, rho);
+  }
+  rest.split = 3;
+  const hipError_t e = launch(rest, weight_dtype, kMidTileRho);
+  if (e != hipSuccess) return e;
+  rest.split = 4;
+  return launch(rest, weight_dtype, rest_rows(rho));
+}
 
 int64_t rows_per_expert(const ExpertArgs& a) { return static_cast<int64_t>(a.T) * a.K / a.E; }
 
@@ -355,12 +372,13 @@ hipError_t launch_gate_up(const ExpertArgs& a, int weight_dtype, hipStream_t str
   if (a.force_tile > 0) return launch_gate_up_stream(a, weight_dtype, forced_rho(a.force_tile), stream);
   // MXFP4 weights run on the streaming kernel at every size (no LDS-tiled form).
   if (a.force_tile == kForceSplit || split_call(a, weight_dtype, rho)) {
-    ExpertArgs tall = a, rest = a;
+    ExpertArgs tall = a;
     tall.split = 1;
-    rest.split = 2;
     const hipError_t e = launch_gate_up_tall(tall, weight_dtype == kDtypeFp8, stream);
     if (e != hipSuccess) return e;
-    return launch_gate_up_stream(rest, weight_dtype, rest_rows(rho), stream);
+    return launch_rest(a, weight_dtype, rho, [&](const ExpertArgs& r, int dt, int64_t rr) {
+      return launch_gate_up_stream(r, dt, rr, stream);
+    });
   }
   ExpertArgs s = a;
   s.kparts = gate_up_kparts(a.T, a.K, a.E, a.H, a.I, a.S, weight_dtype);
@@ -376,12 +394,13 @@ hipError_t launch_down(const ExpertArgs& a, int weight_dtype, hipStream_t stream
   const int64_t rho = rows_per_expert(a);
   if (a.force_tile > 0) return launch_down_stream(a, weight_dtype, forced_rho(a.force_tile), stream);
   if ((a.force_tile == kForceSplit || split_call(a, weight_dtype, rho)) && a.H % 256 == 0) {
-    ExpertArgs tall = a, rest = a;
+    ExpertArgs tall = a;
     tall.split = 1;
-    rest.split = 2;
     const hipError_t e = launch_down_tall(tall, weight_dtype == kDtypeFp8, stream);
     if (e != hipSuccess) return e;
-    return launch_down_stream(rest, weight_dtype, rest_rows(rho), stream);
+    return launch_rest(a, weight_dtype, rho, [&](const ExpertArgs& r, int dt, int64_t rr) {
+      return launch_down_stream(r, dt, rr, stream);
+    });
   }
   return launch_down_stream(a, weight_dtype, rho, stream);
 }

@@ -23,22 +23,51 @@ constexpr int kDtypeF32 = 0, kDtypeBf16 = 1, kDtypeFp8 = 2, kDtypeMxfp4 = 3;
 // r_t = r rows, or r - r % kTallTile when that tail is shorter than kSplitRows,
 // go to the 256-row kernel (split 1; every one of its tiles is then at least half
 // full), and the other rows (short groups whole, tall groups' short tails from row
-// r_t on) to the streaming kernel (split 2).  The shared expert is never cut: its
-// rows are token indices.
+// r_t on) to the streaming kernel (split 2).  Splits 3 and 4 divide split 2's rows
+// once more, by group: the groups left with more than kMidRows of them (split 3,
+// for 128-row streaming tiles, which read a weight slab once where 64-row tiles
+// read it twice) and the others (split 4), provided those groups give at least
+// kMidMinTiles tiles of mid_nt n-tiles each; fewer would run as a launch that
+// leaves most CUs idle, so then split 4 takes all of split 2's rows and split 3
+// none.  Both launches must pass the same mid_nt (the 128-row launch's n-tiles per
+// group), whatever their own tile width, so that they divide the rows alike.  The
+// shared expert is never cut: its rows are token indices.
 constexpr int kSchedStride = kMaxExperts + 2;
 constexpr int kSchedInts = 3 * kSchedStride;
 
 constexpr int kSplitRows = 128;
 constexpr int kTallTile = 256;
+constexpr int kMidRows = 64;
+constexpr int kMidMinTiles = 256;
 
 __device__ int build_tile_prefix(int* sched, const int32_t* counts, const int32_t* offsets, int E, int T,
-                                 bool has_shared, int BM, int nt_routed, int nt_shared, int split = 0) {
+                                 bool has_shared, int BM, int nt_routed, int nt_shared, int split = 0,
+                                 int mid_nt = 0) {
   const int G = E + (has_shared ? 1 : 0);
   int* prefix = sched;
   int* rows_of = sched + kSchedStride;
   int* base_of = sched + 2 * kSchedStride;
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
+    // Rows of group g left to the streaming kernel in a row-divided call.
+    auto rest_of = [&](int g, int& first) {
+      const int r = (g < E) ? counts[g] : T;
+      const int tail = r % kTallTile;
+      const int rt = r < kSplitRows ? 0 : ((g < E && r >= kTallTile && tail < kSplitRows) ? r - tail : r);
+      first = rt;
+      return r - rt;
+    };
+    bool by_size = false;
+    if (split >= 3) {
+      int mid_tiles = 0;
+      for (int base = 0; base < G; base += kWave) {
+        const int g = base + lane;
+        int first;
+        const bool mid = g < G && rest_of(g, first) > kMidRows;
+        mid_tiles += __popcll(__ballot(mid));
+      }
+      by_size = mid_tiles * mid_nt >= kMidMinTiles;
+    }
     int carry = 0;
     for (int base = 0; base < G; base += kWave) {
       const int g = base + lane;
@@ -47,10 +76,15 @@ __device__ int build_tile_prefix(int* sched, const int32_t* counts, const int32_
         const int r = (g < E) ? counts[g] : T;
         int rows = r, first = 0;
         if (split != 0) {
-          const int tail = r % kTallTile;
-          const int rt = r < kSplitRows ? 0 : ((g < E && r >= kTallTile && tail < kSplitRows) ? r - tail : r);
-          if (split == 1) rows = rt;
-          else { rows = r - rt; first = rt; }
+          const int rest = rest_of(g, first);
+          if (split == 1) {
+            rows = r - rest;
+            first = 0;
+          } else {
+            rows = rest;
+            if (split == 3 && (!by_size || rows <= kMidRows)) rows = 0;
+            if (split == 4 && by_size && rows > kMidRows) rows = 0;
+          }
         }
         rows_of[g] = rows;
         base_of[g] = (g < E) ? offsets[g] + first : 0;

@@ -257,7 +257,10 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
   } else {
     const int nt_r = ((MODE == SMode::GateUp) ? a.I / bn_cols : H / bn_cols) * P;
     const int nt_s = has_shared ? ((MODE == SMode::GateUp) ? a.S / bn_cols : H / bn_cols) * P : 0;
-    build_tile_prefix(sched, a.counts, a.offsets, a.E, a.T, has_shared, BM, nt_r, nt_s, a.split);
+    // n-tiles per group of the 128 x 128 launch that serves split 3 (same value in
+    // the split-4 launch, whatever its own tile width).
+    const int mid_nt = (MODE == SMode::GateUp) ? a.I / 64 : H / 128;
+    build_tile_prefix(sched, a.counts, a.offsets, a.E, a.T, has_shared, BM, nt_r, nt_s, a.split, mid_nt);
     const int nk_r = ((MODE == SMode::GateUp) ? H : a.I) / C::kElems / P;
     const int nk_s = ((MODE == SMode::GateUp) ? H : a.S) / C::kElems / P;
     walk = balanced_walk<CostT>(sched, cpre, G, a.E, nk_r, nk_s);

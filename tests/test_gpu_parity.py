@@ -585,6 +585,22 @@ def test_seeded_large_shape_sweep(shape, T, seed, alpha):
     _run(shape, T, seed, alpha, tokens=48)
 
 
+# Row-divided calls from 192 rows per expert give the streaming kernel's share to
+# two launches by group: groups left with more than 64 rows (128-row tiles) and the
+# rest (64-row tiles, 64 columns wide in narrow gate/up calls), when the former fill
+# the GPU.  Both launches must divide alike: 9 such groups in a narrow call (too few
+# to divide, although the narrow launch's own tile count would say enough), and 27
+# groups' long tails (gate/up divided, down not), bf16 and fp8.
+@pytest.mark.parametrize("name,H,E,I,K,S,dt,T,alpha", [
+    ("restdiv_narrow_bf16", 1024, 31, 1024, 7, 512, W.DT_BF16, 3072, 1.5),
+    ("restdiv_tails_bf16", 1024, 32, 1024, 8, 0, W.DT_BF16, 1360, 0.0),
+    ("restdiv_tails_fp8", 1024, 32, 1024, 8, 256, W.DT_FP8, 1360, 0.0),
+])
+def test_rest_rows_divided_by_group_size(name, H, E, I, K, S, dt, T, alpha):
+    shape = W.LayerShape(name, H, E, I, K, S, dt, W.DT_BF16)
+    _run(shape, T, 950 + E, alpha, tokens=128)
+
+
 def test_graph_capture_replays_match_eager():
     """route -> dispatch -> forward captured once into a HIP graph: the library
     launches on the caller's stream with no host synchronisation, copy back or

@@ -42,13 +42,10 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
 
 // float -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
-__device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + __expf(-a)); }
+__device__ __forceinline__ float silu_f32(float a) { return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
 __device__ __forceinline__ float sigmoid_f32(float a) { return 1.0f / (1.0f + __expf(-a)); }
 
 // ---------------------------------------------------------------- MFMA wrappers

@@ -333,20 +333,18 @@ __global__ void __launch_bounds__(kPPThreads) tiledpp_expert_kernel(ExpertArgs a
     // 4 (l / 32) + v % 4, column l % 32.
     if constexpr (MODE == Mode::GateUp) {
       // The whole 256 x 128 bf16 h tile, rows padded to 136 elements (272 bytes:
-      // the two row halves a 32x32 store touches fall on disjoint banks).
+      // the two row halves a 32x32 store touches fall on disjoint banks).  Each
+      // lane writes its own 2-byte element (a pairing of neighbouring columns
+      // through a lane exchange made every write wait for that exchange).
       constexpr int kHs = 136;
-      uint32_t* stg = reinterpret_cast<uint32_t*>(smem);
+      uint16_t* stg = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
       for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const float hv = silu_f32(acc[i][0][v]) * acc[i][1][v];
-          const uint32_t b = f32_to_bf16_bits(hv);
-          const uint32_t nb = __shfl_xor(b, 1, kWave);   // the neighbouring column
-          if ((r32 & 1) == 0) {
-            const int row = arow0 + 32 * i + 8 * (v >> 2) + 4 * hi + (v & 3);
-            stg[(row * kHs + wn * 32 + r32) / 2] = b | (nb << 16);
-          }
+          const int row = arow0 + 32 * i + 8 * (v >> 2) + 4 * hi + (v & 3);
+          stg[row * kHs + wn * 32 + r32] = f32_to_bf16_bits(hv);
         }
       __syncthreads();
       const int width = t.shared ? a.S : a.I;

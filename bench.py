@@ -146,7 +146,12 @@ def gate_up_kernel(shape, T: int) -> str:
     # Rows divided between the 256-row LDS-tiled kernel and the streaming kernel.
     if dt != "mxfp4" and rho >= 16 and T * K * I >= 256 * 256 * 128:
         tall = "tiled8pp_expert_kernel<GateUp> (fp8, 256x128)" if fp8 else "tiledpp_expert_kernel<GateUp> (bf16, 256x256)"
-        return f"{tall} for groups of >= 128 rows + {stream(47 if rho >= 192 else rho)} for the rest"
+        if rho >= 192:
+            # The streaming share divided by group: more than 64 rows left (if such
+            # groups fill the GPU), and the rest.
+            return (f"{tall} for groups of >= 128 rows + {stream(48)} for groups left with > 64 rows"
+                    f" + {stream(47)} for the rest")
+        return f"{tall} for groups of >= 128 rows + {stream(rho)} for the rest"
     return stream(rho)
 
 

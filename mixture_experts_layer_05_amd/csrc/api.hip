@@ -21,6 +21,9 @@ constexpr int32_t kRouterTiledTokens = 4096;
 // Router contraction split for decode-sized batches (see moe_route).
 constexpr int32_t kRouterPlaneTokens = 1024;
 constexpr int kRouterParts = 8;
+// Contraction parts of the LDS-staged router (T >= kRouterTiledTokens) when its
+// columns fill whole 128-column tiles.
+constexpr int kRouterStreamParts = 2;
 // Upper bound (exclusive) on the byte size of x and of h; see check_forward.
 constexpr int64_t kMaxActivationBytes = 3LL << 30;
 
@@ -103,9 +106,13 @@ Layout layout(const moe_config& c, int64_t T) {
   L.ldz = static_cast<int>(align_up(E + 1, 16));
   // Logit planes: decode-sized batches (T <= kRouterPlaneTokens) split the router's
   // contraction over up to kRouterParts workgroups, each writing a partial plane.
-  // max(T, kRouterParts * min(T, kRouterPlaneTokens)) rows keeps the size
-  // monotone in T, so a workspace sized for max_tokens fits every smaller call.
-  L.zrows = std::max<int64_t>(T, static_cast<int64_t>(kRouterParts) * std::min<int64_t>(T, kRouterPlaneTokens));
+  // From kRouterTiledTokens the LDS-staged router may write kRouterStreamParts
+  // planes.  max(T or 2 T, kRouterParts * min(T, kRouterPlaneTokens)) rows keeps
+  // the size monotone in T, so a workspace sized for max_tokens fits every
+  // smaller call.
+  const int64_t tplanes = T >= kRouterTiledTokens ? kRouterStreamParts : 1;
+  L.zrows = std::max<int64_t>(tplanes * T,
+                              static_cast<int64_t>(kRouterParts) * std::min<int64_t>(T, kRouterPlaneTokens));
   L.z = take(static_cast<size_t>(L.zrows) * L.ldz * sizeof(float));
   L.chunks = take(static_cast<size_t>(ceil_div(T, 1024)) * E * sizeof(int32_t));
   L.ranks = take(static_cast<size_t>(T) * c.num_experts_per_tok * sizeof(int32_t));
@@ -353,6 +360,11 @@ int moe_route(const moe_config* cfg, int32_t T, const void* x, const void* w_rou
     r.T = T;
     r.H = H;
     r.E = E;
+    // Split in two when the columns fill whole 128-column tiles and each part
+    // keeps whole 128-element stages.
+    if (ncols % 128 == 0 && H % (128 * kRouterStreamParts) == 0) parts = kRouterStreamParts;
+    r.kparts = parts;
+    r.zplane = plane;
     if ((st = launched(launch_router_stream(r, s)))) return st;
   } else if (cfg->act_dtype == MOE_DTYPE_BF16) {
     // Enough workgroups for ~256 CUs: split the hidden dimension into parts when

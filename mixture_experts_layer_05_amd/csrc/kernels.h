@@ -63,6 +63,7 @@ struct ExpertArgs {
   const void* w_gcol;            // [H] or null
   float* z;                      // [T, ldz]
   int ldz, ncols;
+  size_t zplane;                 // floats between the logit planes of a split router launch
   int T, H, I, S, E, K;
 };
 

@@ -241,16 +241,16 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
   const int G = a.E + (has_shared ? 1 : 0);
   const int H = a.H;
   const int bn_cols = (MODE == SMode::GateUp) ? BN / 2 : BN;
-  // Contraction parts per (group, m-tile, n-tile) of a gate/up launch: tile index
-  // n' = P n + p covers n-tile n over the p-th 1/P of the contraction.
-  const int P = (MODE == SMode::GateUp) ? max(1, a.kparts) : 1;
+  // Contraction parts per (group, m-tile, n-tile) of a gate/up or router launch:
+  // tile index n' = P n + p covers n-tile n over the p-th 1/P of the contraction.
+  const int P = (MODE != SMode::Down) ? max(1, a.kparts) : 1;
   const size_t esz = FP8 ? 1 : 2;   // bytes per A (activation) element
   // Bytes of one weight row of `k` elements.
   auto b_row_bytes = [&](int k) -> size_t { return MX ? static_cast<size_t>(k) / 2 : static_cast<size_t>(k) * esz; };
   Walk walk;
   if constexpr (MODE == SMode::Router) {
     // Equal tiles: an equal run per XCD, strided by its workgroups.
-    const int total = static_cast<int>(ceil_div(a.T, BM) * ceil_div(a.ncols, BN));
+    const int total = static_cast<int>(ceil_div(a.T, BM) * ceil_div(a.ncols, BN)) * P;
     const int xcd = blockIdx.x % 8;
     walk = Walk{total * xcd / 8 + static_cast<int>(blockIdx.x / 8), total * (xcd + 1) / 8,
                 static_cast<int>(gridDim.x / 8)};
@@ -309,7 +309,7 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
   // that tail.
   const int last = walk.tile + (walk.end - 1 - walk.tile) / walk.step * walk.step;
   const int ntiles = (last - walk.tile) / walk.step + 1;
-  int nstages = ntiles * (H / C::kElems);
+  int nstages = ntiles * (H / C::kElems / P);
   if constexpr (MODE != SMode::Router) {
     const int nk_r = ((MODE == SMode::GateUp) ? H : a.I) / C::kElems / P;
     const int nk_s = ((MODE == SMode::GateUp) ? H : a.S) / C::kElems / P;
@@ -694,7 +694,8 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int m = t.m0 + wrow0 + 16 * i + 4 * g + e;
-              if (m < t.rows && col < a.ncols) a.z[static_cast<size_t>(m) * a.ldz + col] = acc[i][j][e];
+              if (m < t.rows && col < a.ncols)
+                a.z[static_cast<size_t>(d.part) * a.zplane + static_cast<size_t>(m) * a.ldz + col] = acc[i][j][e];
             }
           }
       } else if constexpr (MODE == SMode::GateUp) {
@@ -951,6 +952,16 @@ int gate_up_kparts(int64_t T, int K, int E, int H, int I, int S, int weight_dtyp
 }
 
 hipError_t launch_router_stream(const ExpertArgs& a, hipStream_t stream) {
+  if (a.kparts > 1) {
+    // 128 x 128 tiles over 1/kparts of H each (partial logit planes, added in
+    // order by the top-k pass): a third fewer bytes through the CUs than 64-row
+    // tiles over all of H, with as many work items.
+    const int grid = stream_grid(ceil_div(a.T, 128) * ceil_div(a.ncols, 128) * a.kparts);
+    using C = StreamCfg<SMode::Router, 128, 128, 2, kDtypeBf16>;
+    constexpr int NS = stream_stages(C::kAPasses + C::kBPasses);
+    stream_expert_kernel<SMode::Router, 128, 128, 2, kDtypeBf16, NS><<<grid, kStreamThreads, 0, stream>>>(a);
+    return hipGetLastError();
+  }
   const int grid = stream_grid(ceil_div(a.T, 64) * ceil_div(a.ncols, 128));
   using C = StreamCfg<SMode::Router, 64, 128, 1, kDtypeBf16>;
   constexpr int NS = stream_stages(C::kAPasses + C::kBPasses);

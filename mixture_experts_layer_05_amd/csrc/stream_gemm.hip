@@ -119,7 +119,10 @@ struct StreamCfg {
   static_assert(BN % kRowsPerPassB == 0, "BN must be a multiple of the rows per pass");
   static_assert(MODE == SMode::Down || kCB % 2 == 0, "gate/up needs gate and up blocks");
   static_assert(kRM >= 1 && BM % (16 * WM) == 0, "rows per wave must be a multiple of 16");
-  static_assert(!kQ || BM + BN <= kLoadThreads, "one scale per loader thread");
+  // Scale words a loader thread stages per stage: rows tid and tid + 256 (the
+  // activation rows first, then the weight rows).
+  static constexpr int kScaleWords = (BM + BN + kLoadThreads - 1) / kLoadThreads;
+  static_assert(!kQ || (BM <= kLoadThreads && kScaleWords <= 2), "at most two scale rows per loader thread");
 };
 
 // Register stages a loader keeps in flight: as many as fit ~160 VGPRs (more make
@@ -364,7 +367,7 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
     // scale word is at sizeof(SW) * stage).
     struct Src {
       uint32_t a[C::kAPasses];
-      const uint8_t* s;
+      const uint8_t* s[C::kScaleWords];
     };
     auto resolve = [&](const Tile& d, const Pend& p) {
       Src S;
@@ -383,7 +386,8 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
         }
         S.a[q] = (row < BM && m < t.rows) ? off : kDeadRow;
       }
-      S.s = nullptr;
+#pragma unroll
+      for (int w = 0; w < C::kScaleWords; ++w) S.s[w] = nullptr;
       if constexpr (FP8) {
         // Thread tid < BM stages the scale word of tile row tid, BM <= tid < BM+BN
         // that of B row tid-BM; the other threads re-read B row 0's (never stored).
@@ -404,22 +408,29 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
           sw0 = t.shared ? wscale(a.ss_down, a.e8s_down)
                          : wscale(a.s_down, a.e8_down) + static_cast<size_t>(t.group) * H * srow;
         }
-        if (tid < BM) {
-          const int mc = min(t.m0 + tid, t.rows - 1);
-          if constexpr (MODE == SMode::GateUp) {
-            const int tok = t.shared ? mc : p.ps / a.K;
-            S.s = (MX ? a.xe8 : reinterpret_cast<const uint8_t*>(a.xs)) + static_cast<size_t>(tok) * srow;
+        // Scale row tid + 256 w: activation rows [0, BM) (only in word 0, BM <= 256),
+        // then weight rows; rows past BM + BN re-read weight row 0 (never stored).
+#pragma unroll
+        for (int w = 0; w < C::kScaleWords; ++w) {
+          const int r = tid + kLoadThreads * w;
+          if (w == 0 && tid < BM) {
+            const int mc = min(t.m0 + tid, t.rows - 1);
+            if constexpr (MODE == SMode::GateUp) {
+              const int tok = t.shared ? mc : p.ps / a.K;
+              S.s[w] = (MX ? a.xe8 : reinterpret_cast<const uint8_t*>(a.xs)) + static_cast<size_t>(tok) * srow;
+            } else {
+              // Element offset of the row in h, in scale units (one per 32 or per 128).
+              S.s[w] = MX ? a.he8 + hrow(d, mc) / kMxBlock
+                          : reinterpret_cast<const uint8_t*>(a.hs + hrow(d, mc) / kGroup);
+            }
           } else {
-            // Element offset of the row in h, in scale units (one per 32 or per 128).
-            S.s = MX ? a.he8 + hrow(d, mc) / kMxBlock : reinterpret_cast<const uint8_t*>(a.hs + hrow(d, mc) / kGroup);
+            const int br = (r < BM + BN) ? r - BM : 0;
+            if constexpr (MODE == SMode::GateUp)
+              S.s[w] = (br < BN / 2) ? sw0 + static_cast<size_t>(d.n0 + br) * srow
+                                     : sw1 + static_cast<size_t>(d.n0 + br - BN / 2) * srow;
+            else
+              S.s[w] = sw0 + static_cast<size_t>(d.n0 + br) * srow;
           }
-        } else {
-          const int br = (tid < BM + BN) ? tid - BM : 0;
-          if constexpr (MODE == SMode::GateUp)
-            S.s = (br < BN / 2) ? sw0 + static_cast<size_t>(d.n0 + br) * srow
-                                : sw1 + static_cast<size_t>(d.n0 + br - BN / 2) * srow;
-          else
-            S.s = sw0 + static_cast<size_t>(d.n0 + br) * srow;
         }
       }
       return S;
@@ -467,7 +478,7 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
 
     struct Regs {
       uint4 a[C::kAPasses], b[C::kBPasses];
-      SW s;
+      SW s[C::kScaleWords];
     };
     auto gload = [&](Regs& R, const BPtr& P, const Src& S, int ks) {
       const uint32_t off = static_cast<uint32_t>(ks) * C::kRowDataA + lcol;
@@ -476,7 +487,10 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
       for (int q = 0; q < C::kBPasses; ++q) R.b[q] = ld16_stream(P.b[q] + offb);
 #pragma unroll
       for (int q = 0; q < C::kAPasses; ++q) R.a[q] = buf_ld16(arsrc, S.a[q] + off, 0);
-      if constexpr (FP8) R.s = *reinterpret_cast<const SW*>(S.s + sizeof(SW) * ks);
+      if constexpr (FP8) {
+#pragma unroll
+        for (int w = 0; w < C::kScaleWords; ++w) R.s[w] = *reinterpret_cast<const SW*>(S.s[w] + sizeof(SW) * ks);
+      }
     };
     auto lstore = [&](const Regs& R, int slot) {
       uint8_t* base = smem + slot * C::kSlot;
@@ -489,7 +503,9 @@ __global__ void __launch_bounds__(kStreamThreads, 1) stream_expert_kernel(Expert
         *reinterpret_cast<uint4*>(base + C::kBOff + lds_at<C::kRowStrideB>(lrowb + q * C::kRowsPerPassB, lcolb / 16)) =
             R.b[q];
       if constexpr (FP8) {
-        if (tid < C::kScales) sscale[slot * C::kScales + tid] = R.s;
+#pragma unroll
+        for (int w = 0; w < C::kScaleWords; ++w)
+          if (tid + kLoadThreads * w < C::kScales) sscale[slot * C::kScales + tid + kLoadThreads * w] = R.s[w];
       }
     };
 
@@ -915,8 +931,15 @@ hipError_t launch_stream_rho(const ExpertArgs& a, int64_t rho, hipStream_t strea
   // give 33 % more flops per loaded byte than 64 x 128 in 512-element stages and
   // ran the large layer 16 % faster at T = 8192; for bf16 and fp8 they ran 3-7 %
   // faster than 128-row LDS-tiled kernels between 48 and 160 rows per expert.
-  if (rho >= kStreamTallRows)
+  if (rho >= kStreamTallRows) {
+    if constexpr (FMT == kDtypeMxfp4 || FMT == kMxWide) {
+      // MXFP4: 128 x 256 tiles (256 weight rows) where the output widths allow:
+      // 1.5x the flops per loaded byte of 128 x 128.
+      const bool wide = (MODE == SMode::GateUp) ? (a.I % 128 == 0 && a.S % 128 == 0) : a.H % 256 == 0;
+      if (wide) return launch_stream<MODE, 128, 256, 2, kDtypeMxfp4>(a, stream);
+    }
     return launch_stream<MODE, 128, 128, 2, fit_fmt<FMT, 128, 128>()>(a, stream);
+  }
   if constexpr (MODE == SMode::Down) {
     if (rho <= 12 && narrow_down) return launch_stream<MODE, 16, 64, 1, fit_fmt<FMT, 16, 64>()>(a, stream);
   }

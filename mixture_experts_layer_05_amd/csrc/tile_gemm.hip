@@ -13,7 +13,7 @@
 //
 //   * tiledpp_expert_kernel (bf16): 256 x 256 tiles, 8 waves of 128 x 64 with
 //     32x32x16 MFMAs; see its own description below.
-//   * tiled8pp_expert_kernel (fp8): 256 x 128 tiles, 8 waves of 64 x 64 with
+//   * tiled8pp_expert_kernel (fp8): 256 x 256 tiles, 8 waves of 128 x 64 with
 //     16x16x128 fp8 MFMAs and all operands loaded by LDS DMA; see below.
 //
 // The expert launchers (experts.hip) give these kernels the rows that fill a
@@ -395,46 +395,47 @@ __global__ void __launch_bounds__(kPPThreads) tiledpp_expert_kernel(ExpertArgs a
   }
 }
 
-// ---------------------------------------------------------------- 256 x 128 (fp8): shared pieces
+// ---------------------------------------------------------------- 256 x 256 (fp8): shared pieces
 //
-// The fp8 prefill tile: 256 x 128 outputs per workgroup, from 16x16x128 fp8
+// The fp8 prefill tile: 256 x 256 outputs per workgroup, from 16x16x128 fp8
 // MFMAs.  A stage is one 128-element scale group (128 bytes per row).  Every
 // product is rescaled by its row and column group scales on the VALU, which
 // cannot reach the accumulation registers; the accumulators therefore live in
 // ordinary registers.
 //
 // Everything a stage needs goes memory -> LDS by DMA: the 256 activation rows,
-// the 128 weight rows and both sets of group scales (48 KiB + 1.5 KiB).  Three
-// stage buffers keep two stages in flight while one is multiplied out; the
-// waits are explicit (every wave issues the same instructions per stage and they
-// complete in order), so nothing else shortens the prefetch distance.  Same
-// unpadded, piece-permuted row layout as the bf16 tile.
-constexpr int kF8Bufs = 3;
-constexpr int kF8Stage = (256 + 128) * kT4RowBytes;   // 48 KiB
+// the 256 weight rows and both sets of group scales (64 KiB + 2 KiB).  Two stage
+// buffers: the next stage is in flight while one is multiplied out.  The waits
+// are explicit (every wave issues the same instructions per stage and they
+// complete in order).  Same unpadded, piece-permuted row layout as the bf16 tile.
+// Every kernel here receives its operands at a similar rate per CU, whatever
+// their source (L2 or HBM), so the tile is as large as the registers allow: a
+// 256 x 128 tile with two stages in flight (48 KiB per 8.4 MFLOP stage) ran the
+// large fp8 layer slower than this one (66 KiB per 16.8 MFLOP stage).
+constexpr int kF8Bufs = 2;
+constexpr int kF8Stage = (256 + 256) * kT4RowBytes;   // 64 KiB
 
-// ---------------------------------------------------------------- 256 x 128, 8 waves (fp8)
+// ---------------------------------------------------------------- 256 x 256, 8 waves (fp8)
 //
-// 8 waves, two per SIMD: wave w computes rows [64 (w / 2), +64) x the column
-// half w % 2 as 4 x 4 blocks of 16x16 (64 accumulator registers), so that one
-// wave's VALU rescale, fragment reads and waits overlap the other's MFMAs (4
-// waves of 128 x 64, one per SIMD, ran the fp8 layer 9 % slower, measured).
-// Per stage every wave issues the same 7 DMA instructions: 4 of activation rows
-// (32 rows), 2 of weight rows (16 rows of its half), and 1 of scales (waves 0-3:
-// 64 activation rows each; waves 4-7: one weight half each, issued twice with
-// identical values).
+// 8 waves, two per SIMD: wave w computes rows [128 (w / 4), +128) x the column
+// quarter w % 4 (gate/up: 32 gate and the 32 up rows of the same h columns;
+// down: 64 output columns) as 8 x 4 blocks of 16x16 (128 accumulator registers),
+// so that one wave's VALU rescale, fragment reads and waits overlap the other's
+// MFMAs.  Per stage every wave issues the same 9 DMA instructions: 4 of
+// activation rows (32 rows), 4 of weight rows (32 rows), and 1 of scales (waves
+// 0-3: 64 activation rows each; waves 4-7: 64 weight rows each).
 constexpr int kF8PPThreads = 512;
-constexpr int kF8PPDmaPerStage = 4 + 2 + 1;
 
 template <Mode MODE>
 __global__ void __launch_bounds__(kF8PPThreads) tiled8pp_expert_kernel(ExpertArgs a) {
-  constexpr int BM = 256, BN = 128;
+  constexpr int BM = 256, BN = 256;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kF8Bufs * kF8Stage];
   __shared__ __attribute__((aligned(16))) float sscale[kF8Bufs][BM + BN];
   __shared__ int prefix[kSchedInts];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
 
   const bool has_shared = a.S > 0;
   const int G = a.E + (has_shared ? 1 : 0);
@@ -492,68 +493,76 @@ __global__ void __launch_bounds__(kF8PPThreads) tiled8pp_expert_kernel(ExpertArg
       ra = dma_rsrc(a.hq + hrow0, static_cast<uint32_t>(t.rows) * krow);
       rsa = dma_rsrc(a.hs + hrow0 / kGroup, static_cast<uint32_t>(t.rows) * ng * 4);
     }
-    // B rows: the 64-row half (wave & 1) of the tile, gate / up rows (gate/up) or
-    // output rows n0 + 64 (wave & 1) ... (down); wave loads rows 16 (wave >> 1) + ...
-    const int half = wave & 1;
-    i32x4_t rb, rsb;
-    uint32_t boff[2];
+    // B rows of this wave: tile rows [32 wave, +32).  Gate/up: waves 0-3 the gate
+    // rows n0 + 32 wave ..., waves 4-7 the up rows of the same h columns; down:
+    // output rows n0 + 32 wave ...
+    i32x4_t rb;
+    uint32_t boff[4];
     {
-      const uint8_t* wb;
-      const float* sbp;
+      const uint8_t* wsrc;
+      size_t erow;
       if constexpr (MODE == Mode::GateUp) {
-        const uint8_t* wsrc = static_cast<const uint8_t*>(t.shared ? (half ? a.ws_up : a.ws_gate) : (half ? a.w_up : a.w_gate));
-        const float* ssrc = t.shared ? (half ? a.ss_up : a.ss_gate) : (half ? a.s_up : a.s_gate);
-        const size_t erow = (t.shared ? 0 : static_cast<size_t>(t.group) * a.I) + n0;
-        wb = wsrc + erow * krow;
-        sbp = ssrc + erow * ng;
+        const bool up = wave >= 4;
+        wsrc = static_cast<const uint8_t*>(t.shared ? (up ? a.ws_up : a.ws_gate) : (up ? a.w_up : a.w_gate));
+        erow = (t.shared ? 0 : static_cast<size_t>(t.group) * a.I) + n0 + 32 * (wave & 3);
       } else {
-        const uint8_t* wsrc = static_cast<const uint8_t*>(t.shared ? a.ws_down : a.w_down);
-        const float* ssrc = t.shared ? a.ss_down : a.s_down;
-        const size_t erow = (t.shared ? 0 : static_cast<size_t>(t.group) * H) + n0 + 64 * half;
-        wb = wsrc + erow * krow;
-        sbp = ssrc + erow * ng;
+        wsrc = static_cast<const uint8_t*>(t.shared ? a.ws_down : a.w_down);
+        erow = (t.shared ? 0 : static_cast<size_t>(t.group) * H) + n0 + 32 * wave;
       }
-      rb = dma_rsrc(wb, 64 * krow);
-      rsb = dma_rsrc(sbp, 64 * ng * 4);
+      rb = dma_rsrc(wsrc + erow * krow, 32 * krow);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) boff[h] = static_cast<uint32_t>(drow) * krow + dpiece[h];
+      for (int q = 0; q < 4; ++q) boff[q] = static_cast<uint32_t>(8 * q + drow) * krow + dpiece[q & 1];
     }
-    // Down: the destinations of the wave's 64 output rows (lane l: row 64 wm + l),
-    // loaded here and not touched before the epilogue (a load issued between the
-    // epilogue's stores would make the wave wait for them).
-    int pre_slot = 0;
-    float pre_w = 1.0f;
+    // Down: the destinations of the wave's 128 output rows (lane l: rows
+    // 128 wm + l and 128 wm + 64 + l), loaded here and not touched before the
+    // epilogue (a load issued between the epilogue's stores would make the wave
+    // wait for them).
+    int pre_slot[2] = {0, 0};
+    float pre_w[2] = {1.0f, 1.0f};
     if constexpr (MODE == Mode::Down) {
-      const int m = min(t.m0 + wm * 64 + lane, t.rows - 1);
-      pre_slot = a.perm[t.rowbase + m];
-      if (t.shared) pre_w = a.shared_gate[m];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int m = min(t.m0 + wm * 128 + 64 * h + lane, t.rows - 1);
+        pre_slot[h] = a.perm[t.rowbase + m];
+        if (t.shared) pre_w[h] = a.shared_gate[m];
+      }
     }
 
     // The scale vector this wave stages: waves 0-3 the activation rows
-    // [64 wave, +64); waves 4-7 the weight half (wave & 1).
-    const bool a_scales = wave < 4;
+    // [64 wave, +64); waves 4-7 the weight rows [64 (wave - 4), +64) (gate/up:
+    // waves 4-5 gate rows, 6-7 up rows).
     i32x4_t rss;
     uint32_t ssoff, ssdst;
-    if (a_scales) {
+    if (wave < 4) {
       const int ms = min(t.m0 + 64 * wave + lane, t.rows - 1);
       rss = rsa;
       if constexpr (MODE == Mode::GateUp) ssoff = static_cast<uint32_t>(row_token(a, t, ms)) * ng * 4;
       else ssoff = static_cast<uint32_t>(ms) * ng * 4;
       ssdst = 64 * wave * 4;
     } else {
-      rss = rsb;
+      const int bw = wave - 4;
+      const float* ssrc;
+      size_t erow;
+      if constexpr (MODE == Mode::GateUp) {
+        const bool up = bw >= 2;
+        ssrc = t.shared ? (up ? a.ss_up : a.ss_gate) : (up ? a.s_up : a.s_gate);
+        erow = (t.shared ? 0 : static_cast<size_t>(t.group) * a.I) + n0 + 64 * (bw & 1);
+      } else {
+        ssrc = t.shared ? a.ss_down : a.s_down;
+        erow = (t.shared ? 0 : static_cast<size_t>(t.group) * H) + n0 + 64 * bw;
+      }
+      rss = dma_rsrc(ssrc + erow * ng, 64 * ng * 4);
       ssoff = static_cast<uint32_t>(lane) * ng * 4;
-      ssdst = (BM + 64 * half) * 4;
+      ssdst = (BM + 64 * bw) * 4;
     }
 
-    // Stage ks -> buffer ks % 3: A rows at [0, 32 KiB), B rows after; scales in sscale.
+    // Stage ks -> buffer ks % 2: A rows at [0, 32 KiB), B rows after; scales in sscale.
     auto issue = [&](int ks) {
-      const int b = ks % kF8Bufs;
+      const int b = ks & 1;
       const uint32_t buf = lds0 + static_cast<uint32_t>(b) * kF8Stage;
       const uint32_t kb = static_cast<uint32_t>(ks) * kT4RowBytes;
       dma4_rows(ra, aoff, kb, buf + 4 * wave * 1024);
-      dma2_step(rb, boff, kb + 16 * (wave >> 1) * krow, 8 * krow,
-                buf + BM * kT4RowBytes + (64 * half + 16 * (wave >> 1)) * kT4RowBytes);
+      dma4_rows(rb, boff, kb, buf + BM * kT4RowBytes + 4 * wave * 1024);
       const uint32_t sbuf = sc0 + static_cast<uint32_t>(b) * (BM + BN) * 4;
       dma1_dword(rss, ssoff, static_cast<uint32_t>(ks) * 4, sbuf + ssdst);
     };
@@ -567,18 +576,18 @@ __global__ void __launch_bounds__(kF8PPThreads) tiled8pp_expert_kernel(ExpertArg
       const uint4 hi = *reinterpret_cast<const uint4*>(row + pc1);
       return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     };
-    constexpr int NI = 4;
+    constexpr int NI = 8;
     f32x4 acc[NI][4];
 #pragma unroll
     for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto compute = [&](int ks) {
-      const int b = ks % kF8Bufs;
+      const int b = ks & 1;
       const uint8_t* base = smem + b * kF8Stage;
-      const uint8_t* As = base + (wm * 64 + r16) * kT4RowBytes;
+      const uint8_t* As = base + (wm * 128 + r16) * kT4RowBytes;
       const uint8_t* Bs = base + BM * kT4RowBytes;
-      const float* sA = &sscale[b][wm * 64 + 4 * g];
+      const float* sA = &sscale[b][wm * 128 + 4 * g];
       const float* sB = &sscale[b][BM];
       const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
       i32x8 bf[4];
@@ -613,17 +622,15 @@ __global__ void __launch_bounds__(kF8PPThreads) tiled8pp_expert_kernel(ExpertArg
       }
     };
 
-    // Stage ks: wait for this wave's part of it (only stage ks + 1's 7
-    // instructions may still be pending); barrier; start stage ks + 2 into the
+    // Stage ks: wait for this wave's part of it; barrier (every wave's part has
+    // landed and every wave is done with stage ks - 1); start stage ks + 1 into the
     // buffer stage ks - 1 used; multiply stage ks.
-    __syncthreads();                   // the previous tile is done with every buffer
+    __syncthreads();                   // the previous tile is done with both buffers
     issue(0);
-    if (nk > 1) issue(1);
     for (int ks = 0; ks < nk; ++ks) {
-      if (ks + 1 < nk) wait_vm<kF8PPDmaPerStage>();
-      else wait_vm<0>();
+      wait_vm<0>();
       __syncthreads();
-      if (ks + 2 < nk) issue(ks + 2);
+      if (ks + 1 < nk) issue(ks + 1);
       compute(ks);
     }
 
@@ -637,7 +644,7 @@ __global__ void __launch_bounds__(kF8PPThreads) tiled8pp_expert_kernel(ExpertArg
       for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int m = t.m0 + wm * 64 + 16 * i + 4 * g + e;
+          const int m = t.m0 + wm * 128 + 16 * i + 4 * g + e;
           if (m < t.rows) {
             float* hr = hbase + static_cast<size_t>(m) * width + col0;
 #pragma unroll
@@ -650,9 +657,10 @@ __global__ void __launch_bounds__(kF8PPThreads) tiled8pp_expert_kernel(ExpertArg
       for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int m = t.m0 + wm * 64 + 16 * i + 4 * g + e;
-          const int slot = __shfl(pre_slot, 16 * i + 4 * g + e, kWave);
-          const float w = __shfl(pre_w, 16 * i + 4 * g + e, kWave);
+          const int r = 16 * i + 4 * g + e;           // wave row; half i / 4 of pre_slot
+          const int m = t.m0 + wm * 128 + r;
+          const int slot = __shfl(pre_slot[i >> 2], r & 63, kWave);
+          const float w = __shfl(pre_w[i >> 2], r & 63, kWave);
           if (m < t.rows) {
             float* yr = (t.shared ? a.y + static_cast<size_t>(m) * a.H
                                   : a.o + static_cast<size_t>(slot_clamp(slot, a)) * a.H) + col0;
@@ -685,7 +693,7 @@ bool dma_offsets_fit(const ExpertArgs& a) {
 bool tall_tiles_fit(const ExpertArgs& a) { return dma_offsets_fit(a); }
 
 hipError_t launch_gate_up_tall(const ExpertArgs& a, bool fp8, hipStream_t stream) {
-  const int hcols = fp8 ? 64 : 128;   // h columns per tile
+  const int hcols = 128;              // h columns per tile (bf16 and fp8)
   const int grid = tiled_grid(a, 256, a.I / hcols, a.S / hcols);
   if (fp8) tiled8pp_expert_kernel<Mode::GateUp><<<grid, kF8PPThreads, 0, stream>>>(a);
   else tiledpp_expert_kernel<Mode::GateUp><<<grid, kPPThreads, 0, stream>>>(a);
@@ -693,7 +701,7 @@ hipError_t launch_gate_up_tall(const ExpertArgs& a, bool fp8, hipStream_t stream
 }
 
 hipError_t launch_down_tall(const ExpertArgs& a, bool fp8, hipStream_t stream) {
-  const int ycols = fp8 ? 128 : 256;  // output columns per tile
+  const int ycols = 256;              // output columns per tile (bf16 and fp8)
   const int grid = tiled_grid(a, 256, a.H / ycols, a.H / ycols);
   if (fp8) tiled8pp_expert_kernel<Mode::Down><<<grid, kF8PPThreads, 0, stream>>>(a);
   else tiledpp_expert_kernel<Mode::Down><<<grid, kPPThreads, 0, stream>>>(a);

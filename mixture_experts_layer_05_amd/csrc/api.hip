@@ -67,7 +67,7 @@ int check_tokens(const moe_config* c, int32_t T) {
 }
 
 struct Layout {
-  size_t z, h, o, xq, xs, hq, hs, chunks, ranks, bpart, bcount, gpart, total;
+  size_t z, h, o, xq, xs, hq, hs, chunks, ranks, bpart, bcount, gpart, gpart_bytes, total;
   int ldz;
   int64_t zrows;   // rows of z: T per logit plane
   size_t h_shared;  // element offset of the shared expert's rows in h
@@ -125,7 +125,8 @@ Layout layout(const moe_config& c, int64_t T) {
   const size_t hsize = (c.weight_dtype == MOE_DTYPE_BF16) ? 2 : 4;
   L.h = take(elems * hsize);
   L.o = take(static_cast<size_t>(T) * c.num_experts_per_tok * c.hidden_size * sizeof(float));
-  L.gpart = take(gate_up_part_bytes(c, T));   // decode-sized calls' contraction split
+  L.gpart_bytes = gate_up_part_bytes(c, T);
+  L.gpart = take(L.gpart_bytes);               // decode-sized calls' contraction split
   if (c.weight_dtype == MOE_DTYPE_FP8_E4M3_G128) {
     L.xq = take(static_cast<size_t>(T) * c.hidden_size);
     L.xs = take(static_cast<size_t>(T) * (c.hidden_size / kGroup) * sizeof(float));
@@ -255,6 +256,7 @@ ExpertArgs expert_args(const moe_config& c, int32_t T, const void* x, const floa
   a.split = 0;
   a.kparts = 1;   // the gate/up launcher sets the contraction split
   a.gpart = at<float>(ws, L.gpart);
+  a.gpart_floats = L.gpart_bytes / sizeof(float);
   tile_override(c, &a.force_tile);   // validated by check_forward
   a.y = y;
   a.T = T;

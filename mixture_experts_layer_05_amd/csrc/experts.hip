@@ -382,6 +382,10 @@ hipError_t launch_gate_up(const ExpertArgs& a, int weight_dtype, hipStream_t str
   }
   ExpertArgs s = a;
   s.kparts = gate_up_kparts(a.T, a.K, a.E, a.H, a.I, a.S, weight_dtype);
+  // The partial sums must fit the workspace's region for them (sized by the same
+  // estimate); a call it was not sized for runs unsplit rather than past its end.
+  if (s.kparts > 1 && static_cast<size_t>(s.kparts) * gate_up_part_floats(a.T, a.K, a.I, a.S) > a.gpart_floats)
+    s.kparts = 1;
   return launch_gate_up_stream(s, weight_dtype, rho, stream);
 }
 

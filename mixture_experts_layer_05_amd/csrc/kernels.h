@@ -55,6 +55,7 @@ struct ExpertArgs {
   // adds the parts in order p = 0, 1, ... and applies SwiGLU.
   int kparts;
   float* gpart;
+  size_t gpart_floats;           // capacity of gpart: the launcher never splits beyond it
   void* y_act;                   // [T, H] act dtype or null: the cast of y
   int act_bf16;                  // y_act is bf16 (else float32)
   // Router logits (router mode of the streaming kernel): z[t, c] = x_t . col_c with

@@ -134,7 +134,7 @@ def gate_up_kernel(shape, T: int) -> str:
     def stream(r):
         narrow = min(E, T * K) * (I // 64) < 3 * 256
         if r >= 48:
-            cfg = "128, 128, 2"
+            cfg = "128, 256, 2" if dt == "mxfp4" and I % 128 == 0 and S % 128 == 0 else "128, 128, 2"
         elif r <= 12:
             cfg = "16, 128, 1"
         elif r <= 24:
@@ -145,7 +145,7 @@ def gate_up_kernel(shape, T: int) -> str:
 
     # Rows divided between the 256-row LDS-tiled kernel and the streaming kernel.
     if dt != "mxfp4" and rho >= 16 and T * K * I >= 256 * 256 * 128:
-        tall = "tiled8pp_expert_kernel<GateUp> (fp8, 256x128)" if fp8 else "tiledpp_expert_kernel<GateUp> (bf16, 256x256)"
+        tall = "tiled8pp_expert_kernel<GateUp> (fp8, 256x256)" if fp8 else "tiledpp_expert_kernel<GateUp> (bf16, 256x256)"
         if rho >= 192:
             # The streaming share divided by group: more than 64 rows left (if such
             # groups fill the GPU), and the rest.

@@ -556,7 +556,7 @@ def test_seeded_shape_sweep(shape, T, seed):
 def _large_sweep_shapes(n=9, seed=11):
     """Larger random layers whose calls divide their rows between the 256-row and the
     streaming kernels (bf16, fp8: at least 16 rows per expert and T*K*I of at least
-    twice 256 x 256 x 128) or run the 128-row streaming tiles (MXFP4), with Zipf
+    twice 256 x 256 x 128) or run the 128-row streaming tiles (MXFP4: 128 x 256), with Zipf
     router skew, shared expert, budget and top-p drawn at random.  H is a multiple
     of 512, so the fp8 and MXFP4 decode stages take their widest forms."""
     rng = np.random.default_rng(seed)

@@ -144,8 +144,10 @@ def gate_up_kernel(shape, T: int) -> str:
         return f"stream_expert_kernel<GateUp, {cfg}, {dt}>"
 
     # Rows divided between the 256-row LDS-tiled kernel and the streaming kernel.
-    if dt != "mxfp4" and rho >= 16 and T * K * I >= 256 * 256 * 128:
-        tall = "tiled8pp_expert_kernel<GateUp> (fp8, 256x256)" if fp8 else "tiledpp_expert_kernel<GateUp> (bf16, 256x256)"
+    if rho >= 16 and T * K * I >= 256 * 256 * 128:
+        tall = {"bf16": "tiledpp_expert_kernel<GateUp> (bf16, 256x256)",
+                "fp8": "tiled8pp_expert_kernel<GateUp> (fp8, 256x256)",
+                "mxfp4": "tiledmx_expert_kernel<GateUp> (mxfp4, 256x256)"}[dt]
         if rho >= 192:
             # The streaming share divided by group: more than 64 rows left (if such
             # groups fill the GPU), and the rest.

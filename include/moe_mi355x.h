@@ -41,9 +41,9 @@
  *     family selection"]).  "stream16", "stream32", "stream64", "stream128": the
  *     weight-streaming kernel alone with tiles of that many token rows.  "split":
  *     the rows divided by the realised counts between the 256-row LDS-tiled kernel
- *     and the streaming kernel (BF16 and FP8 weights only).  Any other value, or a
- *     value the configuration cannot use (F32 weights; "split" with MXFP4
- *     weights), returns MOE_ERR_BAD_SHAPE before anything is launched, as invalid
+ *     and the streaming kernel.  Any other value, or a value the configuration
+ *     cannot use (F32 weights), returns MOE_ERR_BAD_SHAPE before anything is
+ *     launched, as invalid
  *     overrides fail loudly in [DeepGEMM PR #381, "Forced-wave calibration"].
  *     Every setting computes the same y up to float32 summation order.
  *   - Supported dtype combinations (weight_dtype / act_dtype):

@@ -178,8 +178,7 @@ int tile_override(const moe_config& c, int* force) {
       *force = s.rows;
       return MOE_OK;
     }
-  if (std::strcmp(v, "split") == 0 &&
-      (c.weight_dtype == MOE_DTYPE_BF16 || c.weight_dtype == MOE_DTYPE_FP8_E4M3_G128)) {
+  if (std::strcmp(v, "split") == 0) {   // bf16, fp8 and MXFP4 (f32 returned above)
     *force = kForceSplit;
     return MOE_OK;
   }

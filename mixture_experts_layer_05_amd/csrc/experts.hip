@@ -304,7 +304,7 @@ int tile_bound(const ExpertArgs& a, int BM, int nt_routed, int nt_shared) {
 // rows could fill the GPU with 256-row tiles (T*K*I >= 256 CUs x 256 rows x 128
 // columns) and whose experts see at least kMixRows rows on average is instead
 // divided by its realised counts, read on the device (schedule.h,
-// build_tile_prefix), when its weights are bf16 or fp8: rows that fill a 256-row
+// build_tile_prefix), whatever its weight format: rows that fill a 256-row
 // tile at least half go to the LDS-tiled MFMA kernels (tile_gemm.hip), short
 // groups and the short tails of long ones to the streaming kernel.  Two launches,
 // disjoint rows.  Measured: the large layer at T = 512-1024 with Zipf skew
@@ -314,7 +314,7 @@ int tile_bound(const ExpertArgs& a, int BM, int nt_routed, int nt_shared) {
 constexpr int64_t kMixRows = 16;
 
 bool split_call(const ExpertArgs& a, int weight_dtype, int64_t rho) {
-  return weight_dtype != kDtypeMxfp4 && rho >= kMixRows &&
+  return rho >= kMixRows &&
          static_cast<int64_t>(a.T) * a.K * a.I >= int64_t{256} * 256 * 128 && tall_tiles_fit(a);
 }
 
@@ -359,7 +359,7 @@ int64_t forced_rho(int force_tile) {
 }  // namespace
 
 bool split_allowed(const ExpertArgs& a, int weight_dtype) {
-  return (weight_dtype == kDtypeBf16 || weight_dtype == kDtypeFp8) && tall_tiles_fit(a);
+  return (weight_dtype == kDtypeBf16 || weight_dtype == kDtypeFp8 || weight_dtype == kDtypeMxfp4) && tall_tiles_fit(a);
 }
 
 hipError_t launch_gate_up(const ExpertArgs& a, int weight_dtype, hipStream_t stream) {
@@ -370,11 +370,10 @@ hipError_t launch_gate_up(const ExpertArgs& a, int weight_dtype, hipStream_t str
   }
   const int64_t rho = rows_per_expert(a);
   if (a.force_tile > 0) return launch_gate_up_stream(a, weight_dtype, forced_rho(a.force_tile), stream);
-  // MXFP4 weights run on the streaming kernel at every size (no LDS-tiled form).
   if (a.force_tile == kForceSplit || split_call(a, weight_dtype, rho)) {
     ExpertArgs tall = a;
     tall.split = 1;
-    const hipError_t e = launch_gate_up_tall(tall, weight_dtype == kDtypeFp8, stream);
+    const hipError_t e = launch_gate_up_tall(tall, weight_dtype, stream);
     if (e != hipSuccess) return e;
     return launch_rest(a, weight_dtype, rho, [&](const ExpertArgs& r, int dt, int64_t rr) {
       return launch_gate_up_stream(r, dt, rr, stream);
@@ -400,7 +399,7 @@ hipError_t launch_down(const ExpertArgs& a, int weight_dtype, hipStream_t stream
   if ((a.force_tile == kForceSplit || split_call(a, weight_dtype, rho)) && a.H % 256 == 0) {
     ExpertArgs tall = a;
     tall.split = 1;
-    const hipError_t e = launch_down_tall(tall, weight_dtype == kDtypeFp8, stream);
+    const hipError_t e = launch_down_tall(tall, weight_dtype, stream);
     if (e != hipSuccess) return e;
     return launch_rest(a, weight_dtype, rho, [&](const ExpertArgs& r, int dt, int64_t rr) {
       return launch_down_stream(r, dt, rr, stream);

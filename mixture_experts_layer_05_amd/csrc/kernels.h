@@ -100,8 +100,8 @@ hipError_t launch_down(const ExpertArgs& a, int weight_dtype, hipStream_t stream
 // 256-row LDS-tiled kernels (tile_gemm.hip); tall_tiles_fit: their 32-bit
 // operand offsets cover the call's activation matrices.
 bool tall_tiles_fit(const ExpertArgs& a);
-hipError_t launch_gate_up_tall(const ExpertArgs& a, bool fp8, hipStream_t stream);
-hipError_t launch_down_tall(const ExpertArgs& a, bool fp8, hipStream_t stream);
+hipError_t launch_gate_up_tall(const ExpertArgs& a, int weight_dtype, hipStream_t stream);
+hipError_t launch_down_tall(const ExpertArgs& a, int weight_dtype, hipStream_t stream);
 hipError_t launch_gate_up_stream(const ExpertArgs& a, int weight_dtype, int64_t rho, hipStream_t stream);
 // Contraction parts of a call's gate/up streaming launch (1: unsplit; see
 // stream_gemm.hip).

@@ -15,6 +15,8 @@
 //     32x32x16 MFMAs; see its own description below.
 //   * tiled8pp_expert_kernel (fp8): 256 x 256 tiles, 8 waves of 128 x 64 with
 //     16x16x128 fp8 MFMAs and all operands loaded by LDS DMA; see below.
+//   * tiledmx_expert_kernel (MXFP4 weights x MXFP8 activations): the same tile on
+//     the block-scaled fp8 x fp4 MFMA; see below.
 //
 // The expert launchers (experts.hip) give these kernels the rows that fill a
 // 256-row tile at least half, in calls large enough to fill the GPU with such
@@ -672,6 +674,256 @@ __global__ void __launch_bounds__(kF8PPThreads) tiled8pp_expert_kernel(ExpertArg
   }
 }
 
+// ---------------------------------------------------------------- 256 x 256 (MXFP4)
+//
+// The MXFP4 prefill tile: MXFP8 activation rows x MXFP4 weight rows, 256 x 256
+// outputs per workgroup, on the block-scaled 16x16x128 fp8 x fp4 MFMA, which
+// applies both operands' E8M0 scales itself (no VALU rescale, so the
+// accumulators could stay in the MFMA chain).  A stage is 128 contraction
+// elements: 128 bytes of each activation row, 64 bytes of each weight row and one
+// 4-byte scale word per row (the E8M0 bytes of its four 32-element blocks), 50 KiB
+// per stage, all by LDS DMA into three stage buffers (two stages in flight).  Same
+// wave layout as the fp8 tile: wave w computes rows [128 (w / 4), +128) x the
+// column quarter w % 4 as 8 x 4 blocks of 16x16.
+//
+// Weight rows of 64 bytes (four 16-byte pieces) keep piece p at slot
+// p ^ ((row / 4) mod 4): a fragment read (16 consecutive rows x one piece) then
+// touches 16 distinct 16-byte bank groups.  A DMA instruction writes 16 such rows
+// (1 KiB): lane l fills row l / 4, slot l % 4, so it loads global piece
+// (l % 4) ^ ((l / 16) mod 4) of its row.
+constexpr int kMxBufs = 3;
+constexpr int kMxRowB = 64;                                  // weight bytes per row per stage
+constexpr int kMxStage = 256 * kT4RowBytes + 256 * kMxRowB;   // 48 KiB of codes
+
+template <Mode MODE>
+__global__ void __launch_bounds__(kF8PPThreads) tiledmx_expert_kernel(ExpertArgs a) {
+  constexpr int BM = 256, BN = 256;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kMxBufs * kMxStage];
+  __shared__ __attribute__((aligned(16))) uint32_t sscale[kMxBufs][BM + BN];
+  __shared__ int prefix[kSchedInts];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+  const int wm = wave >> 2, wn = wave & 3;
+
+  const bool has_shared = a.S > 0;
+  const int G = a.E + (has_shared ? 1 : 0);
+  const int H = a.H;
+  const int bn_cols = (MODE == Mode::GateUp) ? BN / 2 : BN;
+  const int nt_r = (MODE == Mode::GateUp) ? a.I / bn_cols : H / bn_cols;
+  const int nt_s = has_shared ? ((MODE == Mode::GateUp) ? a.S / bn_cols : H / bn_cols) : 0;
+  const int total = build_tile_prefix(prefix, a.counts, a.offsets, a.E, a.T, has_shared, BM, nt_r, nt_s,
+                                      a.split);
+
+  // Activation rows: as in the fp8 tile (instruction q covers 8 rows of 128 bytes).
+  const int drow = lane >> 3;
+  uint32_t dpiece[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) dpiece[h] = static_cast<uint32_t>(((lane & 7) ^ ((4 * h + (drow >> 1)) & 7)) * 16);
+  // Weight rows: instruction q covers 16 rows of 64 bytes.
+  const uint32_t wpiece = static_cast<uint32_t>(((lane & 3) ^ ((lane >> 4) & 3)) * 16);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(smem));
+  const uint32_t sc0 = __builtin_amdgcn_readfirstlane(lds_address(&sscale[0][0]));
+  const int r16 = lane & 15, g = lane >> 4;
+  const uint32_t fsw = static_cast<uint32_t>((r16 >> 1) & 7);
+  const uint32_t pc0 = (static_cast<uint32_t>(g) ^ fsw) * 16, pc1 = (static_cast<uint32_t>(4 + g) ^ fsw) * 16;
+  const uint32_t pb = (static_cast<uint32_t>(g) ^ ((r16 >> 2) & 3)) * 16;
+
+  const XcdWalk walk(total);
+  for (int tile = walk.tile; tile < walk.end; tile += walk.step) {
+    TileInfo t = find_tile(prefix, G, tile, a, BM, kBand);
+    t.group = __builtin_amdgcn_readfirstlane(t.group);
+    t.shared = __builtin_amdgcn_readfirstlane(static_cast<int>(t.shared)) != 0;
+    t.rows = __builtin_amdgcn_readfirstlane(t.rows);
+    t.rowbase = __builtin_amdgcn_readfirstlane(t.rowbase);
+    t.m0 = __builtin_amdgcn_readfirstlane(t.m0);
+    t.nt = __builtin_amdgcn_readfirstlane(t.nt);
+    const int kdim = (MODE == Mode::GateUp) ? H : (t.shared ? a.S : a.I);
+    const int nk = kdim / kGroup;               // 128 elements per stage
+    const int n0 = t.nt * bn_cols;
+    const uint32_t krow = static_cast<uint32_t>(kdim);          // bytes per MXFP8 row
+    const uint32_t wrow = static_cast<uint32_t>(kdim / 2);      // bytes per MXFP4 row
+    const uint32_t srow = static_cast<uint32_t>(kdim / kMxBlock);   // E8M0 bytes per row
+    const size_t hrow0 = t.shared ? static_cast<size_t>(a.h_shared) : static_cast<size_t>(t.rowbase) * kdim;
+
+    // A rows of this wave: 32 wave + 8 q + lane / 8 (q < 4).
+    i32x4_t ra, rsa;
+    uint32_t aoff[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int m = min(t.m0 + 32 * wave + 8 * q + drow, t.rows - 1);
+      if constexpr (MODE == Mode::GateUp)
+        aoff[q] = static_cast<uint32_t>(row_token(a, t, m)) * krow + dpiece[q & 1];
+      else
+        aoff[q] = static_cast<uint32_t>(m) * krow + dpiece[q & 1];
+    }
+    if constexpr (MODE == Mode::GateUp) {
+      ra = dma_rsrc(a.xq, static_cast<uint32_t>(a.T) * krow);
+      rsa = dma_rsrc(a.xe8, static_cast<uint32_t>(a.T) * srow);
+    } else {
+      ra = dma_rsrc(a.hq + hrow0, static_cast<uint32_t>(t.rows) * krow);
+      rsa = dma_rsrc(a.he8 + hrow0 / kMxBlock, static_cast<uint32_t>(t.rows) * srow);
+    }
+    // B rows of this wave: tile rows [32 wave, +32) (gate/up: waves 0-3 gate rows,
+    // 4-7 the up rows of the same h columns; down: output rows n0 + 32 wave ...).
+    i32x4_t rb;
+    uint32_t boff[2];
+    {
+      const uint8_t* wsrc;
+      size_t erow;
+      if constexpr (MODE == Mode::GateUp) {
+        const bool up = wave >= 4;
+        wsrc = static_cast<const uint8_t*>(t.shared ? (up ? a.ws_up : a.ws_gate) : (up ? a.w_up : a.w_gate));
+        erow = (t.shared ? 0 : static_cast<size_t>(t.group) * a.I) + n0 + 32 * (wave & 3);
+      } else {
+        wsrc = static_cast<const uint8_t*>(t.shared ? a.ws_down : a.w_down);
+        erow = (t.shared ? 0 : static_cast<size_t>(t.group) * H) + n0 + 32 * wave;
+      }
+      rb = dma_rsrc(wsrc + erow * wrow, 32 * wrow);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) boff[q] = static_cast<uint32_t>(16 * q + (lane >> 2)) * wrow + wpiece;
+    }
+    // Down: the destinations of the wave's 128 output rows (see the fp8 tile).
+    int pre_slot[2] = {0, 0};
+    float pre_w[2] = {1.0f, 1.0f};
+    if constexpr (MODE == Mode::Down) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int m = min(t.m0 + wm * 128 + 64 * h + lane, t.rows - 1);
+        pre_slot[h] = a.perm[t.rowbase + m];
+        if (t.shared) pre_w[h] = a.shared_gate[m];
+      }
+    }
+
+    // Scale words this wave stages: waves 0-3 the activation rows [64 wave, +64);
+    // waves 4-7 the weight rows [64 (wave - 4), +64) (gate/up: 4-5 gate, 6-7 up).
+    i32x4_t rss;
+    uint32_t ssoff, ssdst;
+    if (wave < 4) {
+      const int ms = min(t.m0 + 64 * wave + lane, t.rows - 1);
+      rss = rsa;
+      if constexpr (MODE == Mode::GateUp) ssoff = static_cast<uint32_t>(row_token(a, t, ms)) * srow;
+      else ssoff = static_cast<uint32_t>(ms) * srow;
+      ssdst = 64 * wave * 4;
+    } else {
+      const int bw = wave - 4;
+      const uint8_t* ssrc;
+      size_t erow;
+      if constexpr (MODE == Mode::GateUp) {
+        const bool up = bw >= 2;
+        ssrc = t.shared ? (up ? a.e8s_up : a.e8s_gate) : (up ? a.e8_up : a.e8_gate);
+        erow = (t.shared ? 0 : static_cast<size_t>(t.group) * a.I) + n0 + 64 * (bw & 1);
+      } else {
+        ssrc = t.shared ? a.e8s_down : a.e8_down;
+        erow = (t.shared ? 0 : static_cast<size_t>(t.group) * H) + n0 + 64 * bw;
+      }
+      rss = dma_rsrc(ssrc + erow * srow, 64 * srow);
+      ssoff = static_cast<uint32_t>(lane) * srow;
+      ssdst = (BM + 64 * bw) * 4;
+    }
+
+    // Stage ks -> buffer ks % 3: A rows at [0, 32 KiB), B rows after; scales in sscale.
+    auto issue = [&](int ks) {
+      const int b = ks % kMxBufs;
+      const uint32_t buf = lds0 + static_cast<uint32_t>(b) * kMxStage;
+      dma4_rows(ra, aoff, static_cast<uint32_t>(ks) * kT4RowBytes, buf + 4 * wave * 1024);
+      const uint32_t bbuf = buf + BM * kT4RowBytes + 32 * wave * kMxRowB;
+      dma2_step(rb, boff, static_cast<uint32_t>(ks) * kMxRowB, 0, bbuf);   // rows 16 q + lane / 4
+      const uint32_t sbuf = sc0 + static_cast<uint32_t>(b) * (BM + BN) * 4;
+      dma1_dword(rss, ssoff, static_cast<uint32_t>(ks) * 4, sbuf + ssdst);
+    };
+
+    auto brow = [&](int j) -> int {
+      if constexpr (MODE == Mode::GateUp) return ((j < 2) ? 0 : BN / 2) + wn * 32 + 16 * (j & 1) + r16;
+      else return wn * 64 + 16 * j + r16;
+    };
+    constexpr int NI = 8;
+    f32x4 acc[NI][4];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int ks) {
+      const int b = ks % kMxBufs;
+      const uint8_t* base = smem + b * kMxStage;
+      const uint8_t* As = base + (wm * 128 + r16) * kT4RowBytes;
+      const uint8_t* Bs = base + BM * kT4RowBytes;
+      const uint32_t* sA = &sscale[b][wm * 128 + r16];
+      const uint32_t* sB = &sscale[b][BM];
+      i32x8 bf[4];
+      int sb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint4 v = *reinterpret_cast<const uint4*>(Bs + brow(j) * kMxRowB + pb);
+        bf[j] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        sb[j] = static_cast<int>((sB[brow(j)] >> (8 * g)) & 0xffu);
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const uint8_t* row = As + i * 16 * kT4RowBytes;
+        const uint4 lo = *reinterpret_cast<const uint4*>(row + pc0);
+        const uint4 hi = *reinterpret_cast<const uint4*>(row + pc1);
+        const i32x8 af = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        const int sa = static_cast<int>((sA[16 * i] >> (8 * g)) & 0xffu);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_mxfp8_mxfp4_16x16x128(af, bf[j], acc[i][j], sa, sb[j]);
+      }
+    };
+
+    // Stage ks: wait for this wave's part of it (stage ks + 1's instructions may
+    // still be pending); barrier (every wave's part has landed and every wave is
+    // done with stage ks - 1); start stage ks + 2 into the buffer stage ks - 1 used;
+    // multiply stage ks.
+    constexpr int kDmaPerStage = 4 + 2 + 1;
+    __syncthreads();                   // the previous tile is done with every buffer
+    issue(0);
+    if (nk > 1) issue(1);
+    for (int ks = 0; ks < nk; ++ks) {
+      if (ks + 1 < nk) wait_vm<kDmaPerStage>();
+      else wait_vm<0>();
+      __syncthreads();
+      if (ks + 2 < nk) issue(ks + 2);
+      compute(ks);
+    }
+
+    // 16x16 output placement: lane l, element e -> row 4 (l / 16) + e, column l % 16.
+    if constexpr (MODE == Mode::GateUp) {
+      const int width = t.shared ? a.S : a.I;
+      float* hbase = static_cast<float*>(a.h) +
+                     (t.shared ? static_cast<size_t>(a.h_shared) : static_cast<size_t>(t.rowbase) * width);
+      const int col0 = n0 + wn * 32 + r16;
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = t.m0 + wm * 128 + 16 * i + 4 * g + e;
+          if (m < t.rows) {
+            float* hr = hbase + static_cast<size_t>(m) * width + col0;
+#pragma unroll
+            for (int jh = 0; jh < 2; ++jh) hr[16 * jh] = silu_f32(acc[i][jh][e]) * acc[i][jh + 2][e];
+          }
+        }
+    } else {
+      const int col0 = n0 + wn * 64 + r16;
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * i + 4 * g + e;
+          const int m = t.m0 + wm * 128 + r;
+          const int slot = __shfl(pre_slot[i >> 2], r & 63, kWave);
+          const float w = __shfl(pre_w[i >> 2], r & 63, kWave);
+          if (m < t.rows) {
+            float* yr = (t.shared ? a.y + static_cast<size_t>(m) * a.H
+                                  : a.o + static_cast<size_t>(slot_clamp(slot, a)) * a.H) + col0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) yr[16 * j] = w * acc[i][j][e];
+          }
+        }
+    }
+  }
+}
+
 int tiled_grid(const ExpertArgs& a, int BM, int nt_routed, int nt_shared) {
   const int64_t slots = static_cast<int64_t>(a.T) * a.K;
   int64_t b = (slots / BM + std::min<int64_t>(a.E, slots)) * nt_routed;
@@ -692,18 +944,20 @@ bool dma_offsets_fit(const ExpertArgs& a) {
 
 bool tall_tiles_fit(const ExpertArgs& a) { return dma_offsets_fit(a); }
 
-hipError_t launch_gate_up_tall(const ExpertArgs& a, bool fp8, hipStream_t stream) {
-  const int hcols = 128;              // h columns per tile (bf16 and fp8)
+hipError_t launch_gate_up_tall(const ExpertArgs& a, int weight_dtype, hipStream_t stream) {
+  const int hcols = 128;              // h columns per tile (every weight format)
   const int grid = tiled_grid(a, 256, a.I / hcols, a.S / hcols);
-  if (fp8) tiled8pp_expert_kernel<Mode::GateUp><<<grid, kF8PPThreads, 0, stream>>>(a);
+  if (weight_dtype == kDtypeFp8) tiled8pp_expert_kernel<Mode::GateUp><<<grid, kF8PPThreads, 0, stream>>>(a);
+  else if (weight_dtype == kDtypeMxfp4) tiledmx_expert_kernel<Mode::GateUp><<<grid, kF8PPThreads, 0, stream>>>(a);
   else tiledpp_expert_kernel<Mode::GateUp><<<grid, kPPThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
-hipError_t launch_down_tall(const ExpertArgs& a, bool fp8, hipStream_t stream) {
-  const int ycols = 256;              // output columns per tile (bf16 and fp8)
+hipError_t launch_down_tall(const ExpertArgs& a, int weight_dtype, hipStream_t stream) {
+  const int ycols = 256;              // output columns per tile (every weight format)
   const int grid = tiled_grid(a, 256, a.H / ycols, a.H / ycols);
-  if (fp8) tiled8pp_expert_kernel<Mode::Down><<<grid, kF8PPThreads, 0, stream>>>(a);
+  if (weight_dtype == kDtypeFp8) tiled8pp_expert_kernel<Mode::Down><<<grid, kF8PPThreads, 0, stream>>>(a);
+  else if (weight_dtype == kDtypeMxfp4) tiledmx_expert_kernel<Mode::Down><<<grid, kF8PPThreads, 0, stream>>>(a);
   else tiledpp_expert_kernel<Mode::Down><<<grid, kPPThreads, 0, stream>>>(a);
   return hipGetLastError();
 }

@@ -195,7 +195,6 @@ def test_workspace_size_is_monotone_in_tokens(kw):
     ("bogus", {}, BAD_SHAPE),
     ("stream48", {}, BAD_SHAPE),
     ("Split", {}, BAD_SHAPE),
-    ("split", dict(weight_dtype="mxfp4"), BAD_SHAPE),
     ("stream16", dict(weight_dtype="f32", act_dtype="f32"), BAD_SHAPE),
     ("split", dict(weight_dtype="f32", act_dtype="f32"), BAD_SHAPE),
 ])
@@ -212,10 +211,14 @@ def test_tile_override_rejects_bad_values_before_launching(monkeypatch, value, k
 
 
 @pytest.mark.parametrize("value", ["", "auto", "stream16", "stream32", "stream64", "stream128", "split"])
-def test_tile_override_accepts_documented_values(monkeypatch, value):
+@pytest.mark.parametrize("wdt", ["bf16", "fp8_e4m3_g128", "mxfp4"])
+def test_tile_override_accepts_documented_values(monkeypatch, value, wdt):
     monkeypatch.setenv("MOE_FORCE_TILE", value)
+    cfg = _cfg(weight_dtype=wdt)
+    extra = {} if wdt == "bf16" else dict(s_gate=FAKE, s_up=FAKE, s_down=FAKE,
+                                          ss_gate=FAKE, ss_up=FAKE, ss_down=FAKE)
     for name in ("moe_forward", "moe_forward_gate_up", "moe_forward_down"):
-        assert _forward(_cfg(), T=0, name=name) == OK
+        assert _forward(cfg, T=0, name=name, **extra) == OK
 
 
 def test_noalloc_forward_checks_before_launching():

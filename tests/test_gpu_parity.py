@@ -276,9 +276,7 @@ def test_tile_override_config_invariance(dt, monkeypatch):
     T = 512
     case = Hn.make_case(shape, T, W.base_seed(6, T), 1.0)
     ora = Hn.run_oracle(case)
-    settings = ["auto", "stream16", "stream32", "stream64", "stream128"]
-    if dt != W.DT_MXFP4:
-        settings.append("split")
+    settings = ["auto", "stream16", "stream32", "stream64", "stream128", "split"]
     base = None
     for st in settings:
         print(f"\n[case] {shape.name} T={T} MOE_FORCE_TILE={st}", flush=True)
@@ -292,11 +290,6 @@ def test_tile_override_config_invariance(dt, monkeypatch):
         d = Hn.rel_l2(gpu["y"], base["y"])
         assert np.array_equal(gpu["y"], base["y"]), (st, d)
         print(f"[case] ok {st}: {errs} vs default {d:.2e}", flush=True)
-    if dt == W.DT_MXFP4:
-        monkeypatch.setenv("MOE_FORCE_TILE", "split")
-        with pytest.raises(moe.MoEError) as ei:
-            Hn.run_gpu(case)
-        assert ei.value.status == -2
 
 
 def test_invalid_tile_override_launches_nothing(monkeypatch):
@@ -348,29 +341,30 @@ def test_masked_experts_fewer_finite_than_k(poison):
 EDGE = W.LayerShape("edge_k_eq_e", 256, 4, 256, 4, 128, W.DT_BF16, W.DT_BF16)
 
 
-# Few experts, many rows each: the LDS-tiled kernels with partial 128- and 256-row tiles.
+# Few experts, many rows each: the LDS-tiled kernels with partial 128- and 256-row
+# tiles.  These calls are smaller than the size from which the launcher divides
+# rows by itself (T*K*I >= 256 x 256 x 128), so the tile override forces the
+# division and the 256-row kernels run at sizes the oracle checks on every token.
 TILED = W.LayerShape("tiled_rows", 512, 4, 256, 2, 256, W.DT_BF16, W.DT_BF16)
 
 
+@pytest.mark.parametrize("dt", [W.DT_BF16, W.DT_FP8, W.DT_MXFP4])
 @pytest.mark.parametrize("T", [300, 700])
-def test_tiled_kernels_with_partial_tiles(T):
-    _run(TILED, T, 20 + T)
-
-
-@pytest.mark.parametrize("T", [300, 700])
-def test_tiled_fp8_kernels_with_partial_tiles(T):
-    _run(TILED.with_(name="tiled_rows_fp8", weight_dtype=W.DT_FP8), T, 30 + T)
+def test_tiled_kernels_with_partial_tiles(T, dt, monkeypatch):
+    monkeypatch.setenv("MOE_FORCE_TILE", "split")
+    _run(TILED.with_(name=f"tiled_rows_{dt}", weight_dtype=dt), T, 20 + T + (10 if dt != W.DT_BF16 else 0))
 
 
 # Rows on both sides of the split between the 256-row LDS-tiled kernel and the
 # streaming kernel's 128-row tiles (Zipf-skewed counts: short groups, and long
 # groups whose short tails go to the streaming kernel), checked on every token;
-# the shared expert (600 rows) runs whole on the tiled kernel.
+# the shared expert (600 rows) runs whole on the tiled kernel.  Forced as above.
 MIXED = W.LayerShape("mixed_groups", 512, 8, 256, 2, 256, W.DT_BF16, W.DT_BF16)
 
 
-@pytest.mark.parametrize("dt", [W.DT_BF16, W.DT_FP8])
-def test_groups_split_between_kernels_by_rows(dt):
+@pytest.mark.parametrize("dt", [W.DT_BF16, W.DT_FP8, W.DT_MXFP4])
+def test_groups_split_between_kernels_by_rows(dt, monkeypatch):
+    monkeypatch.setenv("MOE_FORCE_TILE", "split")
     shape = MIXED.with_(name=f"mixed_groups_{dt}", weight_dtype=dt)
     case, gpu, ora, _ = _run(shape, 600, 61, 1.5)
     counts = gpu["counts"]
@@ -379,18 +373,26 @@ def test_groups_split_between_kernels_by_rows(dt):
     assert ((counts > 0) & (counts < 128)).any(), counts                  # a short group
 
 
-# 256-row tiles with the shortest contractions the kernels accept (128 elements)
-# and a single n-tile per group.
+# 256-row tiles with the shortest contractions the kernels accept (128 elements;
+# 256 with MXFP4) and a single n-tile per group.  Forced as above.
 SHORT_K = W.LayerShape("tiled_short_k", 256, 2, 128, 1, 128, W.DT_BF16, W.DT_BF16)
 
 
-def test_tall_tiles_with_short_contractions():
+def test_tall_tiles_with_short_contractions(monkeypatch):
+    monkeypatch.setenv("MOE_FORCE_TILE", "split")
     _run(SHORT_K, 600, 41)
 
 
-def test_tall_fp8_tiles_with_short_contractions():
+def test_tall_fp8_tiles_with_short_contractions(monkeypatch):
     # fp8 256-row tiles: gate/up over 2 scale groups, down over 1 (a one-stage pipeline).
+    monkeypatch.setenv("MOE_FORCE_TILE", "split")
     _run(SHORT_K.with_(name="tiled_short_k_fp8", weight_dtype=W.DT_FP8), 600, 42)
+
+
+def test_tall_mxfp4_tiles_with_short_contractions(monkeypatch):
+    # MXFP4 256-row tiles over two 128-element stages (gate/up and down).
+    monkeypatch.setenv("MOE_FORCE_TILE", "split")
+    _run(W.LayerShape("tiled_short_k_mxfp4", 256, 2, 256, 1, 256, W.DT_MXFP4, W.DT_BF16), 600, 43)
 
 
 def test_k_equals_e_with_ragged_tokens():

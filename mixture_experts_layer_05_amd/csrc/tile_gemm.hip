@@ -858,15 +858,26 @@ __global__ void __launch_bounds__(kF8PPThreads) tiledmx_expert_kernel(ExpertArgs
         bf[j] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
         sb[j] = static_cast<int>((sB[brow(j)] >> (8 * g)) & 0xffu);
       }
+      // Every scale word of the stage first (a word read just before its MFMAs
+      // would stall them for the LDS latency), then the A fragments one row block
+      // ahead of their MFMAs.
+      uint32_t saw[NI];
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
+      for (int i = 0; i < NI; ++i) saw[i] = sA[16 * i];
+      auto afrag = [&](int i) {
         const uint8_t* row = As + i * 16 * kT4RowBytes;
         const uint4 lo = *reinterpret_cast<const uint4*>(row + pc0);
         const uint4 hi = *reinterpret_cast<const uint4*>(row + pc1);
-        const i32x8 af = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        const int sa = static_cast<int>((sA[16 * i] >> (8 * g)) & 0xffu);
+        return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      };
+      i32x8 af[2];
+      af[0] = afrag(0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_mxfp8_mxfp4_16x16x128(af, bf[j], acc[i][j], sa, sb[j]);
+      for (int i = 0; i < NI; ++i) {
+        if (i + 1 < NI) af[(i + 1) & 1] = afrag(i + 1);
+        const int sa = static_cast<int>((saw[i] >> (8 * g)) & 0xffu);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_mxfp8_mxfp4_16x16x128(af[i & 1], bf[j], acc[i][j], sa, sb[j]);
       }
     };
 

@@ -5,18 +5,18 @@
 // instead of weight streaming.  A workgroup owns a 256-row output tile of one
 // group (routed expert or the shared expert); for gate/up, the tile's B rows are
 // gate rows and the up rows of the same intermediate columns, so SwiGLU is fused
-// in registers.  The contraction runs in stages of 128 bytes per row (64 bf16 or
-// one 128-element fp8 scale group).  Tiles are walked persistently; consecutive
+// in registers.  The contraction runs in stages of 128 bytes per activation row
+// (64 bf16, one 128-element fp8 scale group, or 128 MXFP8 codes).  Tiles are walked persistently; consecutive
 // tiles share a weight slab or a row block and are given to workgroups on the
 // same XCD, so those operands are fetched from HBM once per XCD and hit that
-// XCD's L2 afterwards.  Two kernels, each with two waves per SIMD:
+// XCD's L2 afterwards.  Three kernels, each with two waves per SIMD:
 //
 //   * tiledpp_expert_kernel (bf16): 256 x 256 tiles, 8 waves of 128 x 64 with
 //     32x32x16 MFMAs; see its own description below.
 //   * tiled8pp_expert_kernel (fp8): 256 x 256 tiles, 8 waves of 128 x 64 with
 //     16x16x128 fp8 MFMAs and all operands loaded by LDS DMA; see below.
-//   * tiledmx_expert_kernel (MXFP4 weights x MXFP8 activations): the same tile on
-//     the block-scaled fp8 x fp4 MFMA; see below.
+//   * tiledmx_expert_kernel (MXFP4 weights x MXFP8 activations): 256 x 256 tiles,
+//     8 waves of 64 x 128 on the block-scaled fp8 x fp4 MFMA; see below.
 //
 // The expert launchers (experts.hip) give these kernels the rows that fill a
 // 256-row tile at least half, in calls large enough to fill the GPU with such
@@ -678,8 +678,8 @@ __global__ void __launch_bounds__(kF8PPThreads) tiled8pp_expert_kernel(ExpertArg
 //
 // The MXFP4 prefill tile: MXFP8 activation rows x MXFP4 weight rows, 256 x 256
 // outputs per workgroup, on the block-scaled 16x16x128 fp8 x fp4 MFMA, which
-// applies both operands' E8M0 scales itself (no VALU rescale, so the
-// accumulators could stay in the MFMA chain).  A stage is 128 contraction
+// applies both operands' E8M0 scales itself (no VALU rescale: the accumulators
+// stay in the MFMA chain).  A stage is 128 contraction
 // elements: 128 bytes of each activation row, 64 bytes of each weight row and one
 // 4-byte scale word per row (the E8M0 bytes of its four 32-element blocks), 50 KiB
 // per stage, all by LDS DMA into three stage buffers (two stages in flight).  Wave
